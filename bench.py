@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark: AWQ scale search + pack of one linear layer on one MI355X.
+
+A step is one pass of the whole per-layer path on one synthetic layer: activation
+statistics, scale family + fake quantisation + output-error loss for all 20 alphas,
+argmin, final quantise-and-pack.  Inputs are resident in HBM before timing starts.
+The default workload is the 4096 x 4096 layer with 4096 calibration tokens (4-bit,
+zero-point, group 128, 20 alphas).
+
+Prints one JSON line.  The loss product's live duration comes from HIP events that the
+library records on its own stream around that launch (one launch per step, the whole
+alpha grid in one pass).  The CPU baseline is the oracle, timed on a bounded row subset
+of the same layer (the loss is a sum over rows) and scaled to the full layer.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="c2", help="workload name (c1 .. c5)")
+    p.add_argument("--layer", type=int, default=0, help="layer index within the workload")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=256,
+                   help="rows of W in the oracle's timed sample")
+    p.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "profiles", "loss_gemm_c2_traffic.json"),
+                   help="HBM bytes per loss-product launch measured with rocprofv3 counters")
+    return p.parse_args()
+
+
+def cpu_baseline(layer, alphas, cfg, rows):
+    """Time the oracle (as it stands) on rows [0, rows) of W with the full X."""
+    import numpy as np
+    from oracle import awq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    ocfg = O.QConfig(cfg.w_bit, cfg.group_size, cfg.zero_point)
+    W, X = layer.W, layer.X
+    M = W.shape[0]
+    rows = min(rows, M)
+    t0 = time.perf_counter()
+    a = O.act_stats(X)
+    t1 = time.perf_counter()
+    res = O.search_scales(W[:rows], X, a, alphas, ocfg)
+    O.quantize_pack(W[:rows], res["s_star"], ocfg)
+    t2 = time.perf_counter()
+    layer_s = (t1 - t0) + (t2 - t1) * (M / rows)
+    return {"value": 1.0 / layer_s, "unit": "layers/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"statistics over all {X.shape[0]} tokens, then the 20-alpha search and the "
+                       f"pack on rows 0..{rows - 1} of {M}; search+pack time scaled by {M / rows:g} "
+                       f"(the loss and the pack are sums/maps over rows); measured "
+                       f"{t2 - t0:.1f} s")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build measures "
+              "one GPU's share of the layer and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import weight_only_quantization_act_amd as awq
+    from synth import CONFIGS, alpha_grid, make_layer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP GPU", file=sys.stderr)
+        sys.exit(3)
+    torch.cuda.set_device(0)
+    spec = CONFIGS[args.config][args.layer]
+    layer = make_layer(spec)
+    M, K, N = spec.out_features, spec.in_features, spec.n_tokens
+    cfg = awq.qconfig(spec.w_bit, spec.group_size, spec.zero_point)
+    alphas = alpha_grid(spec.n_alpha)
+    nA = len(alphas)
+
+    Wd = torch.from_numpy(layer.W).cuda()
+    Xd = torch.from_numpy(layer.X).cuda()
+    ws_search = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, nA, 0), dtype=torch.uint8,
+                            device="cuda")
+    ws_stats = torch.empty(awq.awq_act_stats_workspace_bytes(N, K), dtype=torch.uint8,
+                           device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev["st0"].record(stream)
+        a = awq.awq_act_stats(Xd, workspace=ws_stats)
+        if ev is not None:
+            ev["st1"].record(stream)
+            awq.awq_set_profile_events(ev["g0"], ev["g1"], ev["f0"], ev["f1"])
+        res = awq.awq_search_scales(Wd, Xd, a, alphas, cfg, workspace=ws_search)
+        if ev is not None:
+            ev["p0"].record(stream)
+        out = awq.awq_quantize_pack(Wd, res["s"], cfg)
+        if ev is not None:
+            ev["p1"].record(stream)
+        return res, out
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    names = ("st0", "st1", "g0", "g1", "f0", "f1", "p0", "p1")
+    evs = [{n: torch.cuda.Event(enable_timing=True) for n in names} for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        res, out = step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    def avg(a, b):
+        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+
+    gemm_ms, fq_ms = avg("g0", "g1"), avg("f0", "f1")
+    stats_ms, pack_ms = avg("st0", "st1"), avg("p0", "p1")
+
+    status = int(res["status"].cpu()[0])
+    gemm_flops = 2.0 * M * N * K * nA                       # one launch = all alphas
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    g = spec.group_size
+    stats_bytes = 2.0 * N * K + 4.0 * K
+    fq_bytes = 2.0 * M * K + 4.0 * K * nA + 2.0 * M * K * nA
+    pack_bytes = 2.0 * M * K + 4.0 * K + M * K / 2 + 4.0 * M * K / g
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                tj = json.load(f)
+            if tj.get("workload") == spec.name and tj.get("kernel_source_sha") == _kernel_sha():
+                traffic = tj.get("hbm_bytes_per_launch")
+        except Exception:  # noqa: BLE001
+            traffic = None
+
+    line = {
+        "metric": "AWQ layers/s at 4096x4096; loss-GEMM TFLOP/s & MFMA util; pack GB/s",
+        "value": 1000.0 / ms_per_step,
+        "unit": "layers/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded fp16 weights and calibration activations with outlier channels)",
+        "config": {"workload": (f"{spec.name}: W {M}x{K} fp16, X {N} tokens x {K}, "
+                                f"{spec.w_bit}-bit {'zero-point' if spec.zero_point else 'symmetric'}, "
+                                f"group {g}, {nA} alphas"),
+                   "out_features": M, "in_features": K, "n_tokens": N, "w_bit": spec.w_bit,
+                   "group_size": g, "zero_point": spec.zero_point, "n_alpha": nA,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": gemm_tflops / MFMA_F16_PEAK_TFLOPS,
+                     "traffic": traffic,
+                     "kernel": "k_loss_gemm", "flops_per_launch": gemm_flops,
+                     "avg_launch_ms": gemm_ms},
+        "kernels": {
+            "act_stats": {"ms": stats_ms, "GB/s": stats_bytes / (stats_ms * 1e-3) / 1e9,
+                          "frac_hbm": stats_bytes / (stats_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "fake_quant": {"ms": fq_ms, "GB/s": fq_bytes / (fq_ms * 1e-3) / 1e9,
+                           "frac_hbm": fq_bytes / (fq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "loss_gemm": {"ms": gemm_ms, "TFLOP/s": gemm_tflops,
+                          "frac_mfma": gemm_tflops / MFMA_F16_PEAK_TFLOPS},
+            "quant_pack": {"ms": pack_ms, "GB/s": pack_bytes / (pack_ms * 1e-3) / 1e9,
+                           "frac_hbm": pack_bytes / (pack_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        },
+        "search_status": status,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(layer, alphas, cfg, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+def _kernel_sha():
+    import hashlib
+    p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "weight_only_quantization_act_amd",
+                     "csrc", "loss_gemm.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * awq_act.h -- C ABI of the MI355X (gfx950) library for AWQ's per-layer
+ * activation-aware scale search and 4-bit packing.
+ *
+ * Pages this interface follows (title, site):
+ *   [AWQ-notes]   "AWQ" -- lizn-zn.github.io scholia-log, inference-quantization notes
+ *   [AWQ-tut]     "AWQ量化" tutorial -- aiqz.cc
+ *   [AWQ-blog]    "AWQ量化技术解析：激活感知的权重量化革命" -- kwkr.cn
+ *   [GPTQ-AWQ]    "大模型的开发应用（十八）：大模型量化：GPTQ与AWQ" -- ewbang.com
+ *   [AutoAWQ-70B] "AWQ 量化全流程拆解：将 70B 大模型塞进单张消费级 GPU" -- lnrq.cn
+ *
+ * Layouts (all row-major, fp16 = IEEE binary16 stored as uint16):
+ *   W   fp16 [out_features][in_features]      weight of one linear layer, M x K
+ *   X   fp16 [n_tokens][in_features]          calibration activations, N x K (the
+ *                                             pages' X, K x N, stored transposed)
+ *   a   fp32 [in_features]                    per-channel mean |x|
+ *   s   fp32 [in_features]                    per-channel scale
+ *
+ * Conventions shared by every entry point:
+ *   - Array arguments are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or keeps them.  Scratch memory comes from a caller-provided
+ *     workspace whose size the matching *_workspace_bytes query returns.
+ *   - W, X, packed codes and dW pointers must be 16-byte aligned; other arrays 4-byte
+ *     (8-byte for fp64).  in_features must be a multiple of group_size.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ *     asynchronous: outputs are valid once the caller synchronises that stream.  No
+ *     call synchronises the host.
+ *   - Errors are return codes (awq_status); nothing throws across the ABI.  All
+ *     argument checks run on the host before any launch; a failed check enqueues
+ *     nothing.  AWQ_E_HIP reports a failed launch or HIP runtime call.
+ *   - Calls are thread-safe given distinct workspaces (no global mutable state other
+ *     than the per-thread profiling hook below).
+ *   - Sizes: M*K and N*K must stay below 2^31 elements.
+ */
+#ifndef AWQ_ACT_H
+#define AWQ_ACT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Quantiser settings: AutoAWQ's quant_config keys w_bit, q_group_size, zero_point
+ * [AutoAWQ-70B §三; GPTQ-AWQ §3 (key parameters)]. */
+typedef struct awq_qconfig {
+  int32_t w_bit;      /* 2, 3 or 4; codes always occupy a 4-bit slot              */
+  int32_t group_size; /* 32, 64 or 128 consecutive input channels of one row      */
+  int32_t zero_point; /* 0 = symmetric (offset-binary codes), 1 = zero-point      */
+} awq_qconfig;
+
+typedef enum awq_status {
+  AWQ_OK = 0,
+  AWQ_E_NULL = 1,       /* a required pointer is NULL                                */
+  AWQ_E_SHAPE = 2,      /* negative/zero size where one is needed, K % g != 0, too big */
+  AWQ_E_CONFIG = 3,     /* w_bit or group_size or zero_point out of range             */
+  AWQ_E_ALPHA = 4,      /* n_alpha outside [1, AWQ_MAX_ALPHA] or an alpha outside [0,1] */
+  AWQ_E_WORKSPACE = 5,  /* workspace NULL or smaller than required                    */
+  AWQ_E_DEVICE = 6,     /* a pointer that must be device memory is not                */
+  AWQ_E_ALIGN = 7,      /* a pointer is not aligned as required                       */
+  AWQ_E_HIP = 8,        /* a HIP runtime call or kernel launch failed                 */
+  AWQ_W_NONFINITE = 9   /* device status word only: no alpha gave a finite loss      */
+} awq_status;
+
+#define AWQ_MAX_ALPHA 64
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* awq_status_str(int status);
+
+/* ------------------------------------------------------------------------------------
+ * A1  activation statistics: a_i = (1/N) * sum_t |X[t][i]|
+ *     [AWQ-notes §1.2 (a_i = E|x_i|); AWQ-tut 激活感知 (mean absolute activation over
+ *     the N calibration samples)].
+ *   X          fp16 [n_tokens][in_features], device
+ *   a_out      fp32 [in_features], device (written)
+ *   workspace  device scratch of at least awq_act_stats_workspace_bytes(N, K) bytes
+ * Sums are taken in fp64 in a fixed order (deterministic; exact for fp16 inputs while
+ * partial sums stay below 2^29), divided by N in fp64, rounded to fp32.
+ * n_tokens >= 1, in_features >= 0.
+ * ---------------------------------------------------------------------------------- */
+size_t awq_act_stats_workspace_bytes(int64_t n_tokens, int64_t in_features);
+int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* a_out,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * A2-A5  scale search over an alpha grid
+ *   For every alpha_k:  s_k = a^alpha_k (a_i == 0 -> 1)            [AWQ-notes §4.1]
+ *                       dW_k = W - Q(W diag(s_k)) diag(s_k)^-1      [AWQ-tut 缩放保护]
+ *                       losses[k] = || dW_k X^T ||_F^2               [AWQ-notes §1.1, §4.1]
+ *   best = argmin over finite losses (first index on ties), s_out = s_best
+ *   [AWQ-notes §4.1; GPTQ-AWQ §3 二 (objective and grid search of alpha in [0,1])].
+ *   Q: per (row, group of group_size input channels), fp32 with one rounding per
+ *   operation, round-half-to-even; symmetric step = max|v|/(2^(b-1)-1), zero-point
+ *   step = (max(v,0) - min(v,0))/(2^b-1), z = rint(-min/step); a zero step becomes 1.
+ *
+ *   W           fp16 [out][in], device           X  fp16 [n_tokens][in], device
+ *   a           fp32 [in], device (from awq_act_stats or the caller)
+ *   alphas_host fp32 [n_alpha], HOST memory, each in [0,1]; copied during the call
+ *   s_out       fp32 [in], device (written: s of the chosen alpha; all 1 if none)
+ *   losses_out  fp64 [n_alpha], device (written)
+ *   best_out    int32 [1], device (written: chosen index, or -1 if no finite loss)
+ *   status_out  int32 [1], device (written: AWQ_OK or AWQ_W_NONFINITE); may be NULL
+ *   workspace   device scratch; see awq_workspace_bytes.
+ * Losses are computed with dW rounded to fp16 and an fp16 MFMA product with fp32
+ * accumulation, reduced in fp64 in a fixed order (bitwise repeatable run to run).
+ * out_features >= 0, in_features >= 0 (multiple of group_size), n_tokens >= 1.
+ * ---------------------------------------------------------------------------------- */
+
+/* Workspace bytes for a search that processes `alpha_batch` grid points per pass
+ * (alpha_batch <= 0 or > n_alpha means all n_alpha at once, the fastest).  Any
+ * workspace of at least awq_workspace_bytes(..., 1) bytes is accepted; the search then
+ * runs as many grid points per pass as fit.  Returns 0 for invalid arguments. */
+size_t awq_workspace_bytes(int64_t out_features, int64_t in_features, int64_t n_tokens,
+                           const awq_qconfig* cfg, int32_t n_alpha, int32_t alpha_batch);
+
+int awq_search_scales(const void* W, const void* X, const float* a,
+                      int64_t out_features, int64_t in_features, int64_t n_tokens,
+                      const awq_qconfig* cfg, const float* alphas_host, int32_t n_alpha,
+                      float* s_out, double* losses_out, int32_t* best_out,
+                      int32_t* status_out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * A3 alone: dW = W - Q(W diag(s)) diag(s)^-1 rounded to fp16, the operand the search's
+ * loss product consumes [AWQ-tut 缩放保护 (W_hat = Q(s W)/s)].
+ *   W fp16 [out][in], s fp32 [in], dW_out fp16 [out][in]; all device.
+ * ---------------------------------------------------------------------------------- */
+int awq_fake_quant_delta(const void* W, const float* s, int64_t out_features,
+                         int64_t in_features, const awq_qconfig* cfg, void* dW_out,
+                         void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * A6  quantise W diag(s) and pack
+ *   codes_out   uint8 [out][in/2]: two codes per byte, input channel 2j in the low
+ *               nibble [AWQ-blog §4.2]; codes in [0, 2^w_bit - 1] (symmetric codes are
+ *               offset by 2^(w_bit-1))
+ *   scales_out  fp16 [out][in/group_size]: the fp32 step rounded to nearest-even fp16
+ *               [AWQ-blog §1.2, §2.1 (int4 codes with an fp16 scale)]
+ *   zeros_out   fp16 [out][in/group_size]: the integer zero point z (2^(w_bit-1) when
+ *               symmetric) [AutoAWQ-70B §三 zero_point, §四 per-group metadata]
+ * Dequantisation of the scaled weight is (code - z) * scale; the unscaled weight is
+ * that divided by s, which the caller folds into the preceding operation
+ * [AWQ-notes §4.3].  Codes are bit-identical to the oracle's for the same s.
+ * ---------------------------------------------------------------------------------- */
+int awq_quantize_pack(const void* W, const float* s, int64_t out_features,
+                      int64_t in_features, const awq_qconfig* cfg, uint8_t* codes_out,
+                      void* scales_out, void* zeros_out, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Profiling hook (per calling thread, one-shot): the next awq_search_scales call on
+ * this thread records `gemm_start`/`gemm_stop` (hipEvent_t) on its stream immediately
+ * before its first and after its last loss-product launch, and `fq_start`/`fq_stop`
+ * around its first fake-quantisation launch.  Any of them may be NULL.  With the whole
+ * alpha grid in one pass (a workspace of awq_workspace_bytes(..., n_alpha, 0)), each
+ * pair brackets exactly one kernel launch.  Returns AWQ_OK.
+ * ---------------------------------------------------------------------------------- */
+int awq_set_profile_events(void* gemm_start, void* gemm_stop, void* fq_start,
+                           void* fq_stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_ACT_H */

@@ -1,0 +1,144 @@
+"""C ABI on the host: the library loads, exports every declared entry point, and rejects
+bad arguments with the documented status codes before touching the GPU.
+
+Every call below fails a host-side check that runs before any HIP call, so these tests
+run without a GPU.  Pointer values are fake (never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_only_quantization_act_amd as awq
+from weight_only_quantization_act_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq_act.h")
+
+E = {"OK": 0, "NULL": 1, "SHAPE": 2, "CONFIG": 3, "ALPHA": 4, "WORKSPACE": 5, "DEVICE": 6,
+     "ALIGN": 7, "HIP": 8, "NONFINITE": 9}
+
+P = ctypes.c_void_p(0x10000)     # aligned fake device pointer (never dereferenced)
+P_ODD = ctypes.c_void_p(0x10002)  # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    return awq.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int|size_t)\s+(awq_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in awq_act.h but not exported"
+    assert set(names) == set(_lib._SIGNATURES)
+
+
+def test_status_strings_and_enum(L):
+    text = open(HEADER).read()
+    for name, val in E.items():
+        key = "AWQ_OK" if name == "OK" else ("AWQ_W_NONFINITE" if name == "NONFINITE" else f"AWQ_E_{name}")
+        assert re.search(rf"\b{key}\s*=\s*{val}\b", text), key
+        s = awq.status_str(val)
+        assert s.startswith(key)
+    assert "unknown" in awq.status_str(12345)
+
+
+def _cfg(b=4, g=128, zp=1):
+    return ctypes.byref(awq.qconfig(b, g, zp))
+
+
+def _search(L, W=P, X=P, a=P, M=256, K=256, N=64, cfg=None, alphas=(0.0, 0.5, 1.0),
+            n_alpha=None, s=P, losses=P, best=P, status=P, ws=P, ws_bytes=1 << 40):
+    al = (ctypes.c_float * max(1, len(alphas)))(*alphas)
+    n = len(alphas) if n_alpha is None else n_alpha
+    return L.awq_search_scales(W, X, a, M, K, N, cfg if cfg is not None else _cfg(), al, n, s,
+                               losses, best, status, ws, ws_bytes, None)
+
+
+def test_search_validation(L):
+    assert _search(L, W=None) == E["NULL"]
+    assert _search(L, X=None) == E["NULL"]
+    assert _search(L, s=None) == E["NULL"]
+    assert _search(L, ws=None) == E["WORKSPACE"]
+    assert _search(L, cfg=_cfg(5)) == E["CONFIG"]
+    assert _search(L, cfg=_cfg(1)) == E["CONFIG"]
+    assert _search(L, cfg=_cfg(4, 96)) == E["CONFIG"]
+    assert _search(L, cfg=_cfg(4, 128, 2)) == E["CONFIG"]
+    assert _search(L, K=200) == E["SHAPE"]           # not a multiple of 128
+    assert _search(L, M=-1) == E["SHAPE"]
+    assert _search(L, N=0) == E["SHAPE"]
+    assert _search(L, M=1 << 20, K=1 << 12) == E["SHAPE"]  # M*K >= 2^31
+    assert _search(L, N=1 << 20, K=1 << 12) == E["SHAPE"]
+    assert _search(L, alphas=(), n_alpha=0) == E["ALPHA"]
+    assert _search(L, alphas=tuple([0.5] * 65)) == E["ALPHA"]
+    assert _search(L, alphas=(0.0, 1.5)) == E["ALPHA"]
+    assert _search(L, alphas=(-0.1,)) == E["ALPHA"]
+    assert _search(L, alphas=(float("nan"),)) == E["ALPHA"]
+    need1 = awq.awq_workspace_bytes(256, 256, 64, awq.qconfig(), 3, 1)
+    assert _search(L, ws_bytes=need1 - 1) == E["WORKSPACE"]
+    assert _search(L, W=P_ODD) == E["ALIGN"]
+    assert _search(L, X=P_ODD) == E["ALIGN"]
+    assert _search(L, losses=ctypes.c_void_p(0x10004)) == E["ALIGN"]
+    assert _search(L, ws=ctypes.c_void_p(0x10010)) == E["ALIGN"]
+
+
+def test_workspace_query(L):
+    cfg = awq.qconfig(4, 128, 1)
+    M = K = N = 4096
+    full = awq.awq_workspace_bytes(M, K, N, cfg, 20, 0)
+    one = awq.awq_workspace_bytes(M, K, N, cfg, 20, 1)
+    tiles = (M // 256) * (N // 256)
+    fixed = 20 * K * 4 + 20 * tiles * 8          # both already multiples of 256
+    assert one == fixed + M * K * 2
+    assert full == fixed + 20 * M * K * 2
+    assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 7) == fixed + 7 * M * K * 2
+    assert awq.awq_workspace_bytes(M, K, N, cfg, 0, 0) == 0
+    assert awq.awq_workspace_bytes(M, 100, N, cfg, 20, 0) == 0
+    assert awq.awq_workspace_bytes(0, K, N, cfg, 3, 0) == ((3 * K * 4 + 255) // 256) * 256
+    s = awq.awq_act_stats_workspace_bytes(4096, 4096)
+    assert s > 0 and s % 256 == 0
+    assert awq.awq_act_stats_workspace_bytes(0, 16) == 0
+
+
+def test_stats_validation(L):
+    ws = awq.awq_act_stats_workspace_bytes(64, 256)
+    f = L.awq_act_stats
+    assert f(None, 64, 256, P, P, ws, None) == E["NULL"]
+    assert f(P, 64, 256, None, P, ws, None) == E["NULL"]
+    assert f(P, 64, 256, P, None, ws, None) == E["WORKSPACE"]
+    assert f(P, 0, 256, P, P, ws, None) == E["SHAPE"]
+    assert f(P, 64, -3, P, P, ws, None) == E["SHAPE"]
+    assert f(P, 64, 256, P, P, ws - 1, None) == E["WORKSPACE"]
+    assert f(P_ODD, 64, 256, P, P, ws, None) == E["ALIGN"]
+    assert f(P, 64, 256, ctypes.c_void_p(0x10001), P, ws, None) == E["ALIGN"]
+
+
+def test_pack_and_fake_quant_validation(L):
+    f = L.awq_quantize_pack
+    assert f(None, P, 8, 128, _cfg(), P, P, P, None) == E["NULL"]
+    assert f(P, P, 8, 128, _cfg(), P, P, None, None) == E["NULL"]
+    assert f(P, P, 8, 128, _cfg(4, 48), P, P, P, None) == E["CONFIG"]
+    assert f(P, P, 8, 96, _cfg(4, 64), P, P, P, None) == E["SHAPE"]
+    assert f(P, P_ODD, 8, 128, _cfg(), P, P, P, None) == E["ALIGN"]
+    assert f(P, P, 8, 128, _cfg(), ctypes.c_void_p(0x10002), P, P, None) == E["ALIGN"]
+    g = L.awq_fake_quant_delta
+    assert g(None, P, 8, 128, _cfg(), P, None) == E["NULL"]
+    assert g(P, P, 8, 100, _cfg(4, 32), P, None) == E["SHAPE"]
+    assert g(P, P, 8, 128, _cfg(3, 128, 3), P, None) == E["CONFIG"]
+    assert g(P, P, 8, 128, _cfg(), P_ODD, None) == E["ALIGN"]
+    # empty weights are a no-op that succeeds without touching memory
+    assert f(P, P, 0, 128, _cfg(), P, P, P, None) == E["OK"]
+    assert g(P, P, 8, 0, _cfg(), P, None) == E["OK"]
+
+
+def test_profile_hook_set_and_clear(L):
+    assert L.awq_set_profile_events(None, None, None, None) == E["OK"]

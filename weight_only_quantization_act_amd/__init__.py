@@ -1,0 +1,23 @@
+"""MI355X-native AWQ activation-aware scale search and 4-bit packing.
+
+The work runs in libawq_act.so (hand-written HIP for gfx950, C ABI in include/awq_act.h);
+this package is a thin ctypes binding with the same entry-point names.
+"""
+from ._lib import (  # noqa: F401
+    AWQ_MAX_ALPHA,
+    AWQ_OK,
+    AWQ_W_NONFINITE,
+    AwqError,
+    LIB_PATH,
+    awq_act_stats,
+    awq_act_stats_workspace_bytes,
+    awq_fake_quant_delta,
+    awq_quantize_pack,
+    awq_search_scales,
+    awq_set_profile_events,
+    awq_workspace_bytes,
+    lib,
+    qconfig,
+    quantize_layer,
+    status_str,
+)

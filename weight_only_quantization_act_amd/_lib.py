@@ -1,0 +1,223 @@
+"""ctypes binding of libawq_act.so: argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; this module checks tensor
+dtypes, devices and contiguity, hands raw device pointers and the current HIP stream to
+the C ABI, and turns non-zero status codes into exceptions.  There is no fallback: if
+the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch  # imported first so that the library binds to torch's HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libawq_act.so")
+
+AWQ_OK = 0
+AWQ_W_NONFINITE = 9
+AWQ_MAX_ALPHA = 64
+
+
+class AwqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)}")
+
+
+class awq_qconfig(ctypes.Structure):
+    _fields_ = [("w_bit", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("zero_point", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+_cfgp = ctypes.POINTER(awq_qconfig)
+
+_SIGNATURES = {
+    "awq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "awq_act_stats_workspace_bytes": (_sz, [_i64, _i64]),
+    "awq_act_stats": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "awq_workspace_bytes": (_sz, [_i64, _i64, _i64, _cfgp, _i32, _i32]),
+    "awq_search_scales": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _cfgp, _vp, _i32,
+                                         _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "awq_fake_quant_delta": (ctypes.c_int, [_vp, _vp, _i64, _i64, _cfgp, _vp, _vp]),
+    "awq_quantize_pack": (ctypes.c_int, [_vp, _vp, _i64, _i64, _cfgp, _vp, _vp, _vp, _vp]),
+    "awq_set_profile_events": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
+}
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libawq_act.so (built in-tree by weight_only_quantization_act_amd.build)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m weight_only_quantization_act_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def status_str(status: int) -> str:
+    return lib().awq_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != AWQ_OK:
+        raise AwqError(status, where)
+
+
+def qconfig(w_bit: int = 4, group_size: int = 128, zero_point: int = 1) -> awq_qconfig:
+    return awq_qconfig(int(w_bit), int(group_size), int(zero_point))
+
+
+def _stream_ptr(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return int(t.data_ptr())
+
+
+def _buf(nbytes: int, device) -> torch.Tensor:
+    # at least 256 bytes so that a zero-size request still yields a valid device pointer
+    return torch.empty(max(256, int(nbytes)), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------------------
+def awq_act_stats_workspace_bytes(n_tokens: int, in_features: int) -> int:
+    return int(lib().awq_act_stats_workspace_bytes(n_tokens, in_features))
+
+
+def awq_act_stats(X: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """a_i = mean over tokens of |X[t, i]| for X fp16 [N, K]  ->  fp32 [K] (device)."""
+    _dev(X, torch.float16, "X")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [n_tokens, in_features]")
+    N, K = X.shape
+    a = out if out is not None else torch.empty(max(K, 1), dtype=torch.float32, device=X.device)[:K]
+    need = awq_act_stats_workspace_bytes(N, K)
+    ws = workspace if workspace is not None else _buf(need, X.device)
+    st = lib().awq_act_stats(_ptr(X), N, K, _ptr(a) if K else _ptr(ws), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream_ptr(stream))
+    _check(st, "awq_act_stats")
+    return a
+
+
+def awq_workspace_bytes(out_features: int, in_features: int, n_tokens: int, cfg: awq_qconfig,
+                        n_alpha: int, alpha_batch: int = 0) -> int:
+    return int(lib().awq_workspace_bytes(out_features, in_features, n_tokens,
+                                         ctypes.byref(cfg), n_alpha, alpha_batch))
+
+
+def awq_search_scales(W: torch.Tensor, X: torch.Tensor, a: torch.Tensor,
+                      alphas: Sequence[float], cfg: awq_qconfig,
+                      workspace: Optional[torch.Tensor] = None, alpha_batch: int = 0,
+                      stream=None):
+    """Grid search over alpha.  Returns device tensors (s [K] fp32, losses [n_alpha] fp64,
+    best [1] int32, status [1] int32); nothing is synchronised."""
+    _dev(W, torch.float16, "W")
+    _dev(X, torch.float16, "X")
+    M, K = W.shape
+    N = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be [n_tokens, in_features] with W's in_features")
+    _dev(a, torch.float32, "a", (K,))
+    al = (ctypes.c_float * max(1, len(alphas)))(*[float(v) for v in alphas])
+    n_alpha = len(alphas)
+    dev = W.device
+    s = torch.empty(max(K, 1), dtype=torch.float32, device=dev)
+    losses = torch.empty(max(n_alpha, 1), dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = _buf(awq_workspace_bytes(M, K, N, cfg, n_alpha, alpha_batch), dev)
+    a_ptr = _ptr(a) if K else _ptr(s)
+    st = lib().awq_search_scales(_ptr(W) if W.numel() else _ptr(workspace),
+                                 _ptr(X) if X.numel() else _ptr(workspace), a_ptr, M, K, N,
+                                 ctypes.byref(cfg), al, n_alpha, _ptr(s), _ptr(losses),
+                                 _ptr(best), _ptr(status), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream_ptr(stream))
+    _check(st, "awq_search_scales")
+    return {"s": s[:K], "losses": losses[:n_alpha], "best": best, "status": status}
+
+
+def awq_fake_quant_delta(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig,
+                         stream=None) -> torch.Tensor:
+    """fp16 W - Q(W diag(s)) diag(s)^-1 for one scale vector."""
+    _dev(W, torch.float16, "W")
+    M, K = W.shape
+    _dev(s, torch.float32, "s", (K,))
+    dW = torch.empty_like(W)
+    if W.numel() == 0:
+        return dW
+    st = lib().awq_fake_quant_delta(_ptr(W), _ptr(s), M, K, ctypes.byref(cfg), _ptr(dW),
+                                    _stream_ptr(stream))
+    _check(st, "awq_fake_quant_delta")
+    return dW
+
+
+def awq_quantize_pack(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig, stream=None):
+    """Packed codes uint8 [M, K/2], fp16 scales [M, K/g], fp16 zeros [M, K/g]."""
+    _dev(W, torch.float16, "W")
+    M, K = W.shape
+    _dev(s, torch.float32, "s", (K,))
+    g = cfg.group_size
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=W.device)
+    scales = torch.empty((M, K // g if g else 0), dtype=torch.float16, device=W.device)
+    zeros = torch.empty_like(scales)
+    if W.numel() == 0:
+        return codes, scales, zeros
+    st = lib().awq_quantize_pack(_ptr(W), _ptr(s), M, K, ctypes.byref(cfg), _ptr(codes),
+                                 _ptr(scales), _ptr(zeros), _stream_ptr(stream))
+    _check(st, "awq_quantize_pack")
+    return codes, scales, zeros
+
+
+def awq_set_profile_events(gemm_start=None, gemm_stop=None, fq_start=None, fq_stop=None):
+    """Arm the one-shot per-thread event hook of the next awq_search_scales call.
+    Arguments are torch.cuda.Event objects (recorded by the library on its stream)."""
+    def h(e):
+        return None if e is None else int(e.cuda_event)
+    _check(lib().awq_set_profile_events(h(gemm_start), h(gemm_stop), h(fq_start), h(fq_stop)),
+           "awq_set_profile_events")
+
+
+def quantize_layer(W: torch.Tensor, X: torch.Tensor, alphas: Sequence[float],
+                   cfg: awq_qconfig, search_workspace: Optional[torch.Tensor] = None,
+                   stats_workspace: Optional[torch.Tensor] = None, stream=None):
+    """The whole per-layer path: statistics -> alpha search -> pack (all on device)."""
+    a = awq_act_stats(X, workspace=stats_workspace, stream=stream)
+    res = awq_search_scales(W, X, a, alphas, cfg, workspace=search_workspace, stream=stream)
+    codes, scales, zeros = awq_quantize_pack(W, res["s"], cfg, stream=stream)
+    res.update({"a": a, "codes": codes, "scales": scales, "zeros": zeros})
+    return res

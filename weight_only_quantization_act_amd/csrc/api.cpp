@@ -1,0 +1,253 @@
+// C ABI of the AWQ scale-search library: argument checks, workspace carving, launches.
+// Every check that can fail runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "awq_act.h"
+#include "awq_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxElems = (int64_t)1 << 31;  // M*K and N*K stay below 2^31
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool cfg_valid(const awq_qconfig* c) {
+  if (!c) return false;
+  if (c->w_bit < 2 || c->w_bit > 4) return false;
+  if (c->group_size != 32 && c->group_size != 64 && c->group_size != 128) return false;
+  if (c->zero_point != 0 && c->zero_point != 1) return false;
+  return true;
+}
+
+// Shape check common to the weight-side calls.
+int weight_shape(int64_t M, int64_t K, const awq_qconfig* cfg) {
+  if (M < 0 || K < 0) return AWQ_E_SHAPE;
+  if (K % cfg->group_size != 0) return AWQ_E_SHAPE;
+  if (M >= kMaxElems || K >= kMaxElems || (K > 0 && M >= kMaxElems / K)) return AWQ_E_SHAPE;
+  return AWQ_OK;
+}
+
+int token_shape(int64_t N, int64_t K) {
+  if (N < 1 || K < 0) return AWQ_E_SHAPE;
+  if (N >= kMaxElems || (K > 0 && N >= kMaxElems / K)) return AWQ_E_SHAPE;
+  return AWQ_OK;
+}
+
+// A pointer the kernels dereference must be device (or managed) memory of HIP.
+int device_ptr(const void* p) {
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return AWQ_E_DEVICE;
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) return AWQ_OK;
+  return AWQ_E_DEVICE;
+}
+
+struct SearchLayout {
+  size_t s_off, p_off, dw_off;
+  size_t dw_bytes_per_alpha;
+  int64_t tiles;
+};
+
+SearchLayout search_layout(int64_t M, int64_t K, int64_t N, int32_t n_alpha) {
+  SearchLayout L;
+  const bool work = (M > 0 && K > 0);
+  L.tiles = work ? awq::loss_tiles_m(M) * awq::loss_tiles_n(N) : 0;
+  L.s_off = 0;
+  L.p_off = round_up((size_t)n_alpha * (size_t)K * sizeof(float), kAlign);
+  L.dw_off = L.p_off + round_up((size_t)n_alpha * (size_t)L.tiles * sizeof(double), kAlign);
+  L.dw_bytes_per_alpha = work ? (size_t)M * (size_t)K * 2 : 0;
+  return L;
+}
+
+struct ProfileHook {
+  void* gemm_start = nullptr;
+  void* gemm_stop = nullptr;
+  void* fq_start = nullptr;
+  void* fq_stop = nullptr;
+};
+thread_local ProfileHook g_hook;
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_E_HIP; }
+
+inline int record(void* ev, hipStream_t st) {
+  if (!ev) return AWQ_OK;
+  return hip_status(hipEventRecord((hipEvent_t)ev, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* awq_status_str(int status) {
+  switch (status) {
+    case AWQ_OK: return "AWQ_OK";
+    case AWQ_E_NULL: return "AWQ_E_NULL: a required pointer is NULL";
+    case AWQ_E_SHAPE: return "AWQ_E_SHAPE: invalid or unsupported sizes";
+    case AWQ_E_CONFIG: return "AWQ_E_CONFIG: w_bit, group_size or zero_point out of range";
+    case AWQ_E_ALPHA: return "AWQ_E_ALPHA: n_alpha or an alpha value out of range";
+    case AWQ_E_WORKSPACE: return "AWQ_E_WORKSPACE: workspace missing or too small";
+    case AWQ_E_DEVICE: return "AWQ_E_DEVICE: pointer is not HIP device memory";
+    case AWQ_E_ALIGN: return "AWQ_E_ALIGN: pointer not aligned as required";
+    case AWQ_E_HIP: return "AWQ_E_HIP: HIP runtime call or kernel launch failed";
+    case AWQ_W_NONFINITE: return "AWQ_W_NONFINITE: no grid point gave a finite loss";
+    default: return "AWQ: unknown status";
+  }
+}
+
+size_t awq_act_stats_workspace_bytes(int64_t n_tokens, int64_t in_features) {
+  if (token_shape(n_tokens, in_features) != AWQ_OK) return 0;
+  const int splits = awq::stats_splits(n_tokens, in_features);
+  return round_up((size_t)splits * (size_t)in_features * sizeof(double), kAlign) + kAlign;
+}
+
+int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* a_out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!X || !a_out) return AWQ_E_NULL;
+  if (!workspace) return AWQ_E_WORKSPACE;
+  int st = token_shape(n_tokens, in_features);
+  if (st != AWQ_OK) return st;
+  if (workspace_bytes < awq_act_stats_workspace_bytes(n_tokens, in_features)) return AWQ_E_WORKSPACE;
+  if (!aligned(X, in_features % 8 == 0 ? 16 : 2) || !aligned(a_out, 4) || !aligned(workspace, 8))
+    return AWQ_E_ALIGN;
+  if (in_features == 0) return AWQ_OK;
+  if ((st = device_ptr(X)) || (st = device_ptr(a_out)) || (st = device_ptr(workspace))) return st;
+  const int splits = awq::stats_splits(n_tokens, in_features);
+  return hip_status(awq::launch_act_stats((const uint16_t*)X, (int)n_tokens, (int)in_features,
+                                          a_out, (double*)workspace, splits,
+                                          (hipStream_t)stream));
+}
+
+size_t awq_workspace_bytes(int64_t out_features, int64_t in_features, int64_t n_tokens,
+                           const awq_qconfig* cfg, int32_t n_alpha, int32_t alpha_batch) {
+  if (!cfg_valid(cfg)) return 0;
+  if (weight_shape(out_features, in_features, cfg) != AWQ_OK) return 0;
+  if (token_shape(n_tokens, in_features) != AWQ_OK) return 0;
+  if (n_alpha < 1 || n_alpha > AWQ_MAX_ALPHA) return 0;
+  if (alpha_batch <= 0 || alpha_batch > n_alpha) alpha_batch = n_alpha;
+  SearchLayout L = search_layout(out_features, in_features, n_tokens, n_alpha);
+  return L.dw_off + (size_t)alpha_batch * L.dw_bytes_per_alpha;
+}
+
+int awq_search_scales(const void* W, const void* X, const float* a, int64_t out_features,
+                      int64_t in_features, int64_t n_tokens, const awq_qconfig* cfg,
+                      const float* alphas_host, int32_t n_alpha, float* s_out,
+                      double* losses_out, int32_t* best_out, int32_t* status_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const int64_t M = out_features, K = in_features, N = n_tokens;
+  if (!W || !X || !a || !cfg || !alphas_host || !s_out || !losses_out || !best_out)
+    return AWQ_E_NULL;
+  if (!workspace) return AWQ_E_WORKSPACE;
+  if (!cfg_valid(cfg)) return AWQ_E_CONFIG;
+  int st = weight_shape(M, K, cfg);
+  if (st != AWQ_OK) return st;
+  if ((st = token_shape(N, K)) != AWQ_OK) return st;
+  if (n_alpha < 1 || n_alpha > AWQ_MAX_ALPHA) return AWQ_E_ALPHA;
+  awq::AlphaList al;
+  memset(&al, 0, sizeof(al));
+  for (int k = 0; k < n_alpha; ++k) {
+    const float v = alphas_host[k];
+    if (!(v >= 0.0f && v <= 1.0f)) return AWQ_E_ALPHA;  // also rejects NaN
+    al.v[k] = v;
+  }
+  const size_t need_min = awq_workspace_bytes(M, K, N, cfg, n_alpha, 1);
+  if (workspace_bytes < need_min) return AWQ_E_WORKSPACE;
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(a, 4) || !aligned(s_out, 4) ||
+      !aligned(losses_out, 8) || !aligned(best_out, 4) || !aligned(status_out, 4) ||
+      !aligned(workspace, kAlign))
+    return AWQ_E_ALIGN;
+  if ((st = device_ptr(W)) || (st = device_ptr(X)) || (st = device_ptr(a)) ||
+      (st = device_ptr(s_out)) || (st = device_ptr(losses_out)) || (st = device_ptr(best_out)) ||
+      (st = device_ptr(workspace)))
+    return st;
+  if (status_out && (st = device_ptr(status_out))) return st;
+
+  ProfileHook hook = g_hook;
+  g_hook = ProfileHook();
+  hipStream_t sm = (hipStream_t)stream;
+  SearchLayout L = search_layout(M, K, N, n_alpha);
+  char* ws = (char*)workspace;
+  float* s_table = (float*)(ws + L.s_off);
+  double* partials = (double*)(ws + L.p_off);
+  uint16_t* dW = (uint16_t*)(ws + L.dw_off);
+  int batch = n_alpha;
+  if (L.dw_bytes_per_alpha > 0) {
+    const size_t fit = (workspace_bytes - L.dw_off) / L.dw_bytes_per_alpha;
+    if (fit < (size_t)batch) batch = (int)fit;
+  }
+
+  if ((st = hip_status(awq::launch_make_scales(a, (int)K, al, n_alpha, s_table, sm)))) return st;
+  if (L.tiles > 0) {
+    for (int k0 = 0; k0 < n_alpha; k0 += batch) {
+      const int nb = n_alpha - k0 < batch ? n_alpha - k0 : batch;
+      const bool first = (k0 == 0);
+      if (first && (st = record(hook.fq_start, sm))) return st;
+      st = hip_status(awq::launch_fake_quant_delta((const uint16_t*)W, s_table + (size_t)k0 * K,
+                                                   (int)M, (int)K, nb, cfg->w_bit,
+                                                   cfg->group_size, cfg->zero_point, dW, sm));
+      if (st) return st;
+      if (first && (st = record(hook.fq_stop, sm))) return st;
+      if (first && (st = record(hook.gemm_start, sm))) return st;
+      st = hip_status(awq::launch_loss_gemm(dW, (const uint16_t*)X, (int)M, (int)N, (int)K, nb,
+                                            partials + (size_t)k0 * L.tiles, sm));
+      if (st) return st;
+    }
+    if ((st = record(hook.gemm_stop, sm))) return st;
+  }
+  return hip_status(awq::launch_reduce_select(partials, n_alpha, (int)L.tiles, s_table, (int)K,
+                                              losses_out, best_out, status_out, s_out, sm));
+}
+
+int awq_fake_quant_delta(const void* W, const float* s, int64_t out_features,
+                         int64_t in_features, const awq_qconfig* cfg, void* dW_out,
+                         void* stream) {
+  if (!W || !s || !cfg || !dW_out) return AWQ_E_NULL;
+  if (!cfg_valid(cfg)) return AWQ_E_CONFIG;
+  int st = weight_shape(out_features, in_features, cfg);
+  if (st != AWQ_OK) return st;
+  if (!aligned(W, 16) || !aligned(s, 16) || !aligned(dW_out, 16)) return AWQ_E_ALIGN;
+  if (out_features == 0 || in_features == 0) return AWQ_OK;
+  if ((st = device_ptr(W)) || (st = device_ptr(s)) || (st = device_ptr(dW_out))) return st;
+  return hip_status(awq::launch_fake_quant_delta(
+      (const uint16_t*)W, s, (int)out_features, (int)in_features, 1, cfg->w_bit,
+      cfg->group_size, cfg->zero_point, (uint16_t*)dW_out, (hipStream_t)stream));
+}
+
+int awq_quantize_pack(const void* W, const float* s, int64_t out_features, int64_t in_features,
+                      const awq_qconfig* cfg, uint8_t* codes_out, void* scales_out,
+                      void* zeros_out, void* stream) {
+  if (!W || !s || !cfg || !codes_out || !scales_out || !zeros_out) return AWQ_E_NULL;
+  if (!cfg_valid(cfg)) return AWQ_E_CONFIG;
+  int st = weight_shape(out_features, in_features, cfg);
+  if (st != AWQ_OK) return st;
+  if (!aligned(W, 16) || !aligned(s, 16) || !aligned(codes_out, 4) || !aligned(scales_out, 2) ||
+      !aligned(zeros_out, 2))
+    return AWQ_E_ALIGN;
+  if (out_features == 0 || in_features == 0) return AWQ_OK;
+  if ((st = device_ptr(W)) || (st = device_ptr(s)) || (st = device_ptr(codes_out)) ||
+      (st = device_ptr(scales_out)) || (st = device_ptr(zeros_out)))
+    return st;
+  return hip_status(awq::launch_quant_pack((const uint16_t*)W, s, (int)out_features,
+                                           (int)in_features, cfg->w_bit, cfg->group_size,
+                                           cfg->zero_point, codes_out, (uint16_t*)scales_out,
+                                           (uint16_t*)zeros_out, (hipStream_t)stream));
+}
+
+int awq_set_profile_events(void* gemm_start, void* gemm_stop, void* fq_start, void* fq_stop) {
+  g_hook.gemm_start = gemm_start;
+  g_hook.gemm_stop = gemm_stop;
+  g_hook.fq_start = fq_start;
+  g_hook.fq_stop = fq_stop;
+  return AWQ_OK;
+}
+
+}  // extern "C"

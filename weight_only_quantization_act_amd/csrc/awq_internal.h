@@ -1,0 +1,48 @@
+// Internal launchers shared between the HIP kernel files and the C-ABI layer.
+// Every launcher enqueues on `stream` and returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace awq {
+
+// ---- loss product tiling (also used by the host to size workspaces) ----------------
+constexpr int kLossBM = 256;  // rows of dW per tile
+constexpr int kLossBN = 256;  // tokens per tile
+constexpr int kLossBK = 64;   // input channels per pipeline stage
+
+inline int64_t loss_tiles_m(int64_t M) { return (M + kLossBM - 1) / kLossBM; }
+inline int64_t loss_tiles_n(int64_t N) { return (N + kLossBN - 1) / kLossBN; }
+
+// ---- statistics ----------------------------------------------------------------------
+// Number of token splits the two-pass statistics reduction uses for an N x K input.
+int stats_splits(int64_t N, int64_t K);
+hipError_t launch_act_stats(const uint16_t* X, int N, int K, float* a_out, double* partials,
+                            int splits, hipStream_t stream);
+
+// ---- scales, fake quantisation, packing ------------------------------------------------
+constexpr int kMaxAlpha = 64;
+struct AlphaList {
+  float v[kMaxAlpha];
+};
+hipError_t launch_make_scales(const float* a, int K, const AlphaList& alphas, int n_alpha,
+                              float* s_table, hipStream_t stream);
+// dW[k] = fp16(W - Q(W s_k) / s_k) for k in [0, nb); dW stride M*K per k.
+hipError_t launch_fake_quant_delta(const uint16_t* W, const float* s_table, int M, int K,
+                                   int nb, int w_bit, int group_size, int zero_point,
+                                   uint16_t* dW, hipStream_t stream);
+hipError_t launch_quant_pack(const uint16_t* W, const float* s, int M, int K, int w_bit,
+                             int group_size, int zero_point, uint8_t* codes,
+                             uint16_t* scales, uint16_t* zeros, hipStream_t stream);
+
+// ---- loss product and selection ------------------------------------------------------
+// partials[k * tiles + tm * tiles_n + tn] = sum over the tile of (dW_k X^T)^2.
+hipError_t launch_loss_gemm(const uint16_t* dW, const uint16_t* X, int M, int N, int K,
+                            int nb, double* partials, hipStream_t stream);
+hipError_t launch_reduce_select(const double* partials, int n_alpha, int tiles,
+                                const float* s_table, int K, double* losses, int32_t* best,
+                                int32_t* status, float* s_out, hipStream_t stream);
+
+}  // namespace awq
