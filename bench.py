@@ -35,10 +35,50 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=256,
                    help="rows of W in the oracle's timed sample")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="after timing, run one device-to-device copy of this many MiB (a kernel of "
+                        "known traffic, used to scale the HBM byte counters)")
     p.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                           "profiles", "loss_gemm_c2_traffic.json"),
                    help="HBM bytes per loss-product launch measured with rocprofv3 counters")
     return p.parse_args()
+
+
+class HipEvent:
+    """A raw hipEvent_t from the HIP runtime torch already loaded (same SONAME), so that
+    the library can record it on its own launches and we can read the elapsed time."""
+
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")
+            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._hip = hip
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreate(ctypes.byref(self.h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+
+    @property
+    def handle(self) -> int:
+        return int(self.h.value)
+
+    def record(self, stream_ptr: int):
+        if HipEvent._hip.hipEventRecord(self.h, self._ct.c_void_p(stream_ptr)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        f = self._ct.c_float()
+        rc = HipEvent._hip.hipEventElapsedTime(self._ct.byref(f), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(f.value)
 
 
 def cpu_baseline(layer, alphas, cfg, rows):
@@ -99,20 +139,21 @@ def main():
     ws_stats = torch.empty(awq.awq_act_stats_workspace_bytes(N, K), dtype=torch.uint8,
                            device="cuda")
     stream = torch.cuda.current_stream()
+    sptr = int(stream.cuda_stream)
 
     def step(ev=None):
         if ev is not None:
-            ev["st0"].record(stream)
+            ev["st0"].record(sptr)
         a = awq.awq_act_stats(Xd, workspace=ws_stats)
         if ev is not None:
-            ev["st1"].record(stream)
+            ev["st1"].record(sptr)
             awq.awq_set_profile_events(ev["g0"], ev["g1"], ev["f0"], ev["f1"])
         res = awq.awq_search_scales(Wd, Xd, a, alphas, cfg, workspace=ws_search)
         if ev is not None:
-            ev["p0"].record(stream)
+            ev["p0"].record(sptr)
         out = awq.awq_quantize_pack(Wd, res["s"], cfg)
         if ev is not None:
-            ev["p1"].record(stream)
+            ev["p1"].record(sptr)
         return res, out
 
     for _ in range(args.warmup):
@@ -120,20 +161,19 @@ def main():
     torch.cuda.synchronize()
 
     names = ("st0", "st1", "g0", "g1", "f0", "f1", "p0", "p1")
-    evs = [{n: torch.cuda.Event(enable_timing=True) for n in names} for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    evs = [{n: HipEvent() for n in names} for _ in range(args.steps)]
+    t_start, t_end = HipEvent(), HipEvent()
     torch.cuda.synchronize()
-    t_start.record(stream)
+    t_start.record(sptr)
     for i in range(args.steps):
         res, out = step(evs[i])
-    t_end.record(stream)
+    t_end.record(sptr)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    total_ms = t_start.elapsed_ms(t_end)
     ms_per_step = total_ms / args.steps
 
     def avg(a, b):
-        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+        return float(np.mean([e[a].elapsed_ms(e[b]) for e in evs]))
 
     gemm_ms, fq_ms = avg("g0", "g1"), avg("f0", "f1")
     stats_ms, pack_ms = avg("st0", "st1"), avg("p0", "p1")
@@ -192,6 +232,13 @@ def main():
         },
         "search_status": status,
     }
+    if args.calib_copy_mib > 0:
+        src = torch.ones(args.calib_copy_mib * (1 << 20) // 2, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calib_copy_bytes"] = {"read": src.numel() * 2, "write": dst.numel() * 2}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layer, alphas, cfg, args.cpu_rows)
     print(json.dumps(line), flush=True)

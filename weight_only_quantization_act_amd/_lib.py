@@ -205,9 +205,11 @@ def awq_quantize_pack(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig, stream
 
 def awq_set_profile_events(gemm_start=None, gemm_stop=None, fq_start=None, fq_stop=None):
     """Arm the one-shot per-thread event hook of the next awq_search_scales call.
-    Arguments are torch.cuda.Event objects (recorded by the library on its stream)."""
+    Arguments are hipEvent_t handles (int), or objects exposing one as `.handle`."""
     def h(e):
-        return None if e is None else int(e.cuda_event)
+        if e is None:
+            return None
+        return int(e) if isinstance(e, int) else int(e.handle)
     _check(lib().awq_set_profile_events(h(gemm_start), h(gemm_stop), h(fq_start), h(fq_stop)),
            "awq_set_profile_events")
 

@@ -11,7 +11,6 @@ namespace awq {
 // ---- loss product tiling (also used by the host to size workspaces) ----------------
 constexpr int kLossBM = 256;  // rows of dW per tile
 constexpr int kLossBN = 256;  // tokens per tile
-constexpr int kLossBK = 64;   // input channels per pipeline stage
 
 inline int64_t loss_tiles_m(int64_t M) { return (M + kLossBM - 1) / kLossBM; }
 inline int64_t loss_tiles_n(int64_t N) { return (N + kLossBN - 1) / kLossBN; }

@@ -9,13 +9,20 @@
 // is a "TN" product whose tiles stream straight from HBM.  The product itself is never
 // stored: each 256 x 256 tile is squared and summed in registers.
 //
-// Tiling for CDNA4 (gfx950, wave64, 160 KiB LDS per CU):
-//   block 256 threads = 4 waves in a 2 x 2 arrangement, tile 256 (dW rows) x 256 (tokens)
-//   wave sub-tile 128 x 128 = 4 x 4 MFMA 32x32x16 f16 blocks, 256 fp32 accumulators/lane
-//   K staged 64 at a time through a double-buffered LDS ring (2 x 64 KiB); global loads of
-//   stage k+1 are issued before the MFMAs of stage k.  Rows of a stage are 128 bytes; the
-//   16-byte chunk index is XOR-swizzled with (row & 7) so that the 8 lanes served per LDS
-//   cycle read 8 distinct bank groups.
+// Design for CDNA4 (gfx950, wave64, 160 KiB LDS per CU, 64-bank LDS):
+//   block = 8 waves (2 x 4), tile 256 dW rows x 256 tokens, wave sub-tile 128 x 64 =
+//   4 x 2 MFMA 32x32x16 f16 blocks (128 fp32 accumulators per lane, two waves per SIMD).
+//   K streams through LDS 64 channels per stage in a ring of NS stages.  Operands move
+//   global -> LDS with the gfx950 buffer_load ... lds DMA (no register staging): lane l
+//   of a wave-DMA lands at LDS byte 16 l of a 1 KiB block, and out-of-range offsets
+//   (rows past the matrix, channels past in_features) arrive as zeros.  A stage buffer
+//   is refilled right after the barrier that follows the last fragment read from it,
+//   with explicit s_waitcnt accounting (the number of DMAs in flight is constant).
+//   Rows of a stage are 128 bytes; the 16-byte chunk index is XOR-swizzled with
+//   (row & 7) ^ ((row >> 3) & 1), which keeps every 16 consecutive rows on 16 distinct
+//   16-byte bank groups modulo 256 bytes, so fragment reads are conflict-free.
+//   Fragments ping-pong between two register sets so the LDS reads of step k+1 overlap
+//   the MFMAs of step k.
 //   MFMA operand layout (32x32x16 f16): lane l supplies row (l mod 32) and channels
 //   8*(l div 32) .. +7 of the 16-channel slice for A, and the same for B with tokens
 //   in place of rows.  The loss only needs the sum of squares of the output tile, so the
@@ -25,35 +32,129 @@
 //   keeps the panels its 32 CUs share resident in that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "awq_act.h"
 #include "awq_internal.h"
+
+#ifndef LOSS_BK
+#define LOSS_BK 64
+#endif
+#ifndef LOSS_NS
+#define LOSS_NS 2
+#endif
+#ifndef LOSS_WM
+#define LOSS_WM 2
+#endif
+#ifndef LOSS_WN
+#define LOSS_WN 4
+#endif
 
 namespace awq {
 
 namespace {
 
-constexpr int BM = kLossBM, BN = kLossBN, BK = kLossBK;
+constexpr int BM = kLossBM, BN = kLossBN;
 constexpr int kThreads = 256;
-constexpr int kStageHalves = (BM + BN) * BK;          // 32768 halves = 64 KiB
-constexpr int kLoadsA = BM * BK / 8 / kThreads;       // 16-byte chunks per thread, A
-constexpr int kLoadsB = BN * BK / 8 / kThreads;       // same for B
-constexpr int kBandM = 4;                              // tile-rows per raster band
+constexpr int kBandM = 4;  // tile-rows per raster band
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-__global__ __launch_bounds__(kThreads, 1) void k_loss_gemm(
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (gfx9 layout): 48-bit base, stride 0, byte range, 32-bit data
+// format.  Accesses at offsets >= num_bytes return zero.
+__device__ __forceinline__ int32x4 make_rsrc(const void* base, unsigned num_bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  int32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)(b & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)((b >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (int)(unsigned)(size_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// One wave-level 16-byte-per-lane DMA from global memory into LDS: lane l's 16 bytes at
+// buffer offset voff + soff land at LDS byte lds + 16 l.  Issued as inline assembly so
+// that the compiler's automatic waits do not drain the DMA queue before unrelated LDS
+// reads; every wait for these transfers is the explicit s_waitcnt at the barriers.
+// The instruction writes no VGPR (its data goes to LDS), so no register of the asm is
+// overwritten after the statement.
+__device__ __forceinline__ void dma16(const int32x4& rsrc, unsigned lds, unsigned voff,
+                                      unsigned soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
+}
+
+// s_waitcnt immediate for gfx9: vmcnt(vm) with expcnt/lgkmcnt: lgkmcnt(0), expcnt(7).
+template <int VM>
+struct WaitVmLgkm {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  static constexpr int value = (VM & 0xF) | ((VM >> 4) << 14) | (7 << 4);
+};
+
+// Tile geometry: a K slice of BK channels per stage, NS stages, WM x WN waves.
+template <int BK_, int NS_, int WM_, int WN_>
+struct Stage {
+  static constexpr int BK = BK_;
+  static constexpr int NS = NS_;
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int WAVES = WM * WN;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int MI = BM / WM / 32;                     // 32-row MFMA blocks per wave
+  static constexpr int NI = BN / WN / 32;                     // 32-token MFMA blocks per wave
+  static constexpr int CPR = BK / 8;                          // 16-byte chunks per row
+  static constexpr int ROWS_PER_DMA = 64 / CPR;               // rows one wave-DMA fills
+  static constexpr int DMA_A = BM * BK * 2 / 1024 / WAVES;    // DMAs per wave for A
+  static constexpr int DMA_B = BN * BK * 2 / 1024 / WAVES;
+  static constexpr int PER_STAGE = DMA_A + DMA_B;             // vmcnt units per stage
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int BYTES = (BM + BN) * BK * 2;
+  static constexpr int KSTEPS = BK / 16;
+  static_assert(DMA_A >= 1 && DMA_B >= 1, "each wave issues at least one DMA per operand");
+  // XOR swizzle of the 16-byte chunk index within a row.  A fragment read has the 32
+  // lanes of a half-wave on 32 consecutive rows at the same logical chunk; the swizzle
+  // spreads every 16 consecutive rows over 16 distinct 16-byte slots modulo 256 bytes
+  // (and every 8 over 8 slots modulo 128 bytes), so neither a 64-bank nor a 32-bank
+  // LDS sees a conflict.  128-byte rows: (row & 7) ^ ((row >> 3) & 1);
+  // 64-byte rows: ((row >> 1) & 3) ^ ((row >> 3) & 1).  Both depend on row & 15 only.
+  __device__ static int swz(int row) {
+    return CPR == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : (((row >> 1) & 3) ^ ((row >> 3) & 1));
+  }
+};
+
+template <class S>
+__global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     const uint16_t* __restrict__ dW, const uint16_t* __restrict__ X, int M, int N, int K,
     int tiles_m, int tiles_n, int nb, double* __restrict__ partials) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStageHalves];
-  __shared__ double red[kThreads / 64];
+  // One LDS array per pipeline stage: distinct objects let the compiler see that a DMA
+  // into one stage never aliases fragment reads from another, so it does not drain the
+  // DMA queue before every LDS read.
+  __shared__ __attribute__((aligned(1024))) uint8_t sm0[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm1[S::NS > 1 ? S::BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm2[S::NS > 2 ? S::BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm3[S::NS > 3 ? S::BYTES : 16];
+  __shared__ double red[S::WAVES];
+  static_assert(S::NS >= 2 && S::NS <= 4, "2..4 stages");
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index as a scalar (uniform) value, so LDS bases derived from it live in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / S::WN;
+  const int wn = wave % S::WN;
 
   // ---- block -> (grid point, tile row, tile column), XCD-contiguous ----------------
   const int per_alpha = tiles_m * tiles_n;
@@ -77,106 +178,173 @@ __global__ __launch_bounds__(kThreads, 1) void k_loss_gemm(
   const int rows_a = min(BM, M - tm * BM);
   const int rows_b = min(BN, N - tn * BN);
 
-  // ---- global -> register staging ----------------------------------------------------
-  const int ld_row = tid >> 3;  // 0..31
-  const int ld_kc = tid & 7;    // 16-byte chunk within a 64-channel stage row
-  u32x4 ra[kLoadsA], rb[kLoadsB];
+  // ---- DMA through buffer resources.  Lane l of a wave-level buffer_load ... lds fills
+  //      LDS bytes [16 l, 16 l + 16) of a 1 KiB block: row l / CPR of the block,
+  //      physical chunk l % CPR, which holds logical chunk (l % CPR) ^ swz(row) (swz
+  //      depends only on the lane for these blocks).  The per-lane byte offset is fixed;
+  //      the block index and the K position go into the scalar offset.  Rows past the
+  //      end of the tile and channels past in_features fall outside the resource's
+  //      range, and the hardware writes zeros for them.
+  // A wave-DMA block covers ROWS_PER_DMA (8 or 16) rows starting at a multiple of that
+  // count, so row & 15 is (block parity) * 8 + lane / CPR when blocks hold 8 rows.
+  const int dma_row_in = lane / S::CPR;
+  const int dma_lchunk_even = (lane % S::CPR) ^ S::swz(dma_row_in);
+  const int dma_lchunk_odd = (lane % S::CPR) ^ S::swz(dma_row_in + (S::ROWS_PER_DMA == 8 ? 8 : 0));
+  const int32x4 rsrc_a = make_rsrc(A, (unsigned)rows_a * (unsigned)K * 2u);
+  const int32x4 rsrc_b = make_rsrc(B, (unsigned)rows_b * (unsigned)K * 2u);
+  static_assert(S::DMA_A % 2 == 0 && S::DMA_B % 2 == 0, "block parity follows j");
+  const unsigned row_a = (unsigned)(wave * S::DMA_A * S::ROWS_PER_DMA + dma_row_in);
+  const unsigned row_b = (unsigned)(wave * S::DMA_B * S::ROWS_PER_DMA + dma_row_in);
+  const unsigned vo_a0 = (row_a * (unsigned)K + dma_lchunk_even * 8) * 2u;
+  const unsigned vo_a1 = (row_a * (unsigned)K + dma_lchunk_odd * 8) * 2u;
+  const unsigned vo_b0 = (row_b * (unsigned)K + dma_lchunk_even * 8) * 2u;
+  const unsigned vo_b1 = (row_b * (unsigned)K + dma_lchunk_odd * 8) * 2u;
+  const unsigned dma_row_stride = (unsigned)S::ROWS_PER_DMA * (unsigned)K * 2u;  // bytes per j
+  constexpr unsigned kOutOfRange = 0x80000000u;
 
-  auto gload = [&](int k0) {
-    const int kc = k0 + ld_kc * 8;
-    const bool k_ok = kc < K;
-#pragma unroll
-    for (int j = 0; j < kLoadsA; ++j) {
-      const int row = ld_row + 32 * j;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (k_ok && row < rows_a) v = *(const u32x4*)(A + (size_t)row * K + kc);
-      ra[j] = v;
-    }
-#pragma unroll
-    for (int j = 0; j < kLoadsB; ++j) {
-      const int row = ld_row + 32 * j;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (k_ok && row < rows_b) v = *(const u32x4*)(B + (size_t)row * K + kc);
-      rb[j] = v;
-    }
-  };
-  auto sstore = [&](int stage) {
-    uint16_t* sa = smem + stage * kStageHalves;
-    uint16_t* sb = sa + BM * BK;
-#pragma unroll
-    for (int j = 0; j < kLoadsA; ++j) {
-      const int row = ld_row + 32 * j;
-      *(u32x4*)(sa + row * BK + ((ld_kc ^ (row & 7)) << 3)) = ra[j];
-    }
-#pragma unroll
-    for (int j = 0; j < kLoadsB; ++j) {
-      const int row = ld_row + 32 * j;
-      *(u32x4*)(sb + row * BK + ((ld_kc ^ (row & 7)) << 3)) = rb[j];
-    }
+  auto stage_ptr = [&](auto st) -> uint8_t* {
+    constexpr int ST = decltype(st)::value;
+    if constexpr (ST == 0) return sm0;
+    else if constexpr (ST == 1) return sm1;
+    else if constexpr (ST == 2) return sm2;
+    else return sm3;
   };
 
-  floatx16 acc[4][4];
+  auto dma_stage = [&](auto st, int k0) {
+    uint8_t* sa = stage_ptr(st);
+    uint8_t* sb = sa + S::A_BYTES;
+    const bool k_ok0 = k0 + dma_lchunk_even * 8 < K;
+    const bool k_ok1 = k0 + dma_lchunk_odd * 8 < K;
+    const unsigned va0 = k_ok0 ? vo_a0 : kOutOfRange, va1 = k_ok1 ? vo_a1 : kOutOfRange;
+    const unsigned vb0 = k_ok0 ? vo_b0 : kOutOfRange, vb1 = k_ok1 ? vo_b1 : kOutOfRange;
+    const unsigned kbytes = (unsigned)k0 * 2u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < S::DMA_A; ++j)
+      dma16(rsrc_a, lds_addr(sa + (wave * S::DMA_A + j) * 1024), (j & 1) ? va1 : va0,
+            kbytes + j * dma_row_stride);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < S::DMA_B; ++j)
+      dma16(rsrc_b, lds_addr(sb + (wave * S::DMA_B + j) * 1024), (j & 1) ? vb1 : vb0,
+            kbytes + j * dma_row_stride);
+  };
+
+  // ---- fragment reads: MFMA 32x32x16 f16 operand = row (l mod 32), channels
+  //      8*(l div 32) .. +7 of the 16-channel step, for A (dW rows) and B (tokens).
+  const int frag_row = lane & 31;
+  const int frag_half = lane >> 5;
+  const int frag_swz = S::swz(frag_row);
+  const int a_off = (wm * S::MI * 32 + frag_row) * S::BK * 2;
+  const int b_off = S::A_BYTES + (wn * S::NI * 32 + frag_row) * S::BK * 2;
+
+  struct Frag {
+    half8 a[S::MI], b[S::NI];
+  };
+  auto load_frag = [&](auto st, int ks, Frag& f) {
+    const uint8_t* base = stage_ptr(st);
+    const int chunk = ((2 * ks + frag_half) ^ frag_swz) * 16;
+#pragma unroll
+    for (int mi = 0; mi < S::MI; ++mi)
+      f.a[mi] = *(const half8*)(base + a_off + mi * 32 * S::BK * 2 + chunk);
+#pragma unroll
+    for (int ni = 0; ni < S::NI; ++ni)
+      f.b[ni] = *(const half8*)(base + b_off + ni * 32 * S::BK * 2 + chunk);
+  };
+
+  floatx16 acc[S::MI][S::NI];
+#pragma unroll
+  for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int nk = (K + BK - 1) / BK;
-  const int frag_row = lane & 31;
-  const int frag_half = lane >> 5;
-  const int swz = frag_row & 7;  // (row & 7) for every fragment row of this lane
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int mi = 0; mi < S::MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < S::NI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+  };
 
-  if (nk > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
+  const int nk = (K + S::BK - 1) / S::BK;
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const uint16_t* sa = smem + cur * kStageHalves + (wm * 128 + frag_row) * BK;
-    const uint16_t* sb = smem + cur * kStageHalves + BM * BK + (wn * 128 + frag_row) * BK;
+  // ---- pipeline: NS stages in flight; a stage buffer is refilled right after the
+  //      barrier that follows the last fragment read from it.  DMAs are issued for
+  //      every stage slot (past the end of K they read zeros into a slot nobody reads),
+  //      so the number of DMAs in flight, hence the vmcnt to wait for, is constant.
+  //      The K loop is unrolled by NS so that every access names its stage array.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1 % S::NS>;
+  using I2 = std::integral_constant<int, 2 % S::NS>;
+  using I3 = std::integral_constant<int, 3 % S::NS>;
+  dma_stage(I0{}, 0);
+  if constexpr (S::NS > 1) dma_stage(I1{}, 1 * S::BK);
+  if constexpr (S::NS > 2) dma_stage(I2{}, 2 * S::BK);
+  if constexpr (S::NS > 3) dma_stage(I3{}, 3 * S::BK);
+  __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 1) * S::PER_STAGE>::value);
+  __builtin_amdgcn_s_barrier();
+
+  // Fragments ping-pong between two register sets; KSTEPS is even, so a stage always
+  // starts with its first k-step in f0 and ends having loaded the next stage's first
+  // k-step into f0 as well.
+  static_assert(S::KSTEPS % 2 == 0, "even number of 16-channel steps per stage");
+  Frag f0, f1;
+  if (nk > 0) load_frag(I0{}, 0, f0);
+
+  // one k-tile held in stage ST (k-tile index kt)
+  auto step = [&](auto st, int kt) {
+    constexpr int ST = decltype(st)::value;
+    using NEXT = std::integral_constant<int, (ST + 1) % S::NS>;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int chunk = ((2 * ks + frag_half) ^ swz) << 3;
-      half8 af[4], bf[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) af[mi] = *(const half8*)(sa + mi * 32 * BK + chunk);
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) bf[ni] = *(const half8*)(sb + ni * 32 * BK + chunk);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] =
-              __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+    for (int ks = 0; ks + 2 < S::KSTEPS; ks += 2) {
+      load_frag(st, ks + 1, f1);
+      mma(f0);
+      load_frag(st, ks + 2, f0);
+      mma(f1);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+    load_frag(st, S::KSTEPS - 1, f1);
+    mma(f0);
+    // stage kt+1 has landed (own DMAs) and this wave's reads of stage kt are done
+    __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 2) * S::PER_STAGE>::value);
+    __builtin_amdgcn_s_barrier();
+    dma_stage(st, (kt + S::NS) * S::BK);
+    if (kt + 1 < nk) load_frag(NEXT{}, 0, f0);
+    mma(f1);
+  };
+
+  for (int kt = 0; kt < nk; kt += S::NS) {
+    step(I0{}, kt);
+    if constexpr (S::NS > 1) { if (kt + 1 >= nk) break; step(I1{}, kt + 1); }
+    if constexpr (S::NS > 2) { if (kt + 2 >= nk) break; step(I2{}, kt + 2); }
+    if constexpr (S::NS > 3) { if (kt + 3 >= nk) break; step(I3{}, kt + 3); }
   }
+  __builtin_amdgcn_s_waitcnt(WaitVmLgkm<0>::value);  // no LDS write may outlive the block
 
   // ---- epilogue: sum of squares of the 256 x 256 output tile -------------------------
   double ssum = 0.0;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < S::MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
+    for (int ni = 0; ni < S::NI; ++ni) {
       float t = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) t += acc[mi][ni][e] * acc[mi][ni][e];
       ssum += (double)t;
+      __builtin_amdgcn_sched_barrier(0);  // one 32x32 block at a time: low VGPR pressure
     }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off);
   if (lane == 0) red[wave] = ssum;
   __syncthreads();
-  if (tid == 0)
-    partials[(size_t)kk_alpha * per_alpha + (size_t)tm * tiles_n + tn] =
-        (red[0] + red[1]) + (red[2] + red[3]);
+  if (tid == 0) {
+    double t = red[0];
+#pragma unroll
+    for (int w = 1; w < S::WAVES; ++w) t += red[w];
+    partials[(size_t)kk_alpha * per_alpha + (size_t)tm * tiles_n + tn] = t;
+  }
 }
+
+using LossStage = Stage<LOSS_BK, LOSS_NS, LOSS_WM, LOSS_WN>;
 
 __global__ __launch_bounds__(256) void k_reduce_select(const double* __restrict__ partials,
                                                        int n_alpha, int tiles,
@@ -231,8 +399,9 @@ hipError_t launch_loss_gemm(const uint16_t* dW, const uint16_t* X, int M, int N,
   const int tm = (int)loss_tiles_m(M), tn = (int)loss_tiles_n(N);
   const long long blocks = (long long)nb * tm * tn;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_loss_gemm, dim3((unsigned)blocks), dim3(kThreads), 0, stream, dW, X, M, N,
-                     K, tm, tn, nb, partials);
+  hipLaunchKernelGGL(k_loss_gemm<LossStage>, dim3((unsigned)blocks), dim3(LossStage::THREADS), 0,
+                     stream, dW,
+                     X, M, N, K, tm, tn, nb, partials);
   return hipGetLastError();
 }
 
