@@ -25,9 +25,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunkLanes = 64;                     // chunks (8 channels) per block
 constexpr int kTokenLanes = kThreads / kChunkLanes;  // token strides per block
-constexpr int kTargetBlocks = 2048;
-constexpr int kMinTokensPerSplit = 32;
-constexpr int kMaxSplits = 256;
+constexpr int kTargetBlocks = 1024;
+constexpr int kMinTokensPerSplit = 64;
+constexpr int kMaxSplits = 128;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -81,14 +81,29 @@ __global__ __launch_bounds__(kThreads) void k_act_stats_partial(const uint16_t* 
   }
 }
 
+// Pass 2: a block owns 64 channels; its 4 waves take interleaved slices of the splits
+// (wave u sums splits u, u+4, u+8, ... in order) and the 4 sums are added in a fixed
+// order.  Reads are 64 consecutive doubles per wave instruction.
 __global__ __launch_bounds__(kThreads) void k_act_stats_finalize(const double* __restrict__ part,
                                                                  int splits, int N, int K,
                                                                  float* __restrict__ a) {
-  const int i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= K) return;
+  __shared__ double red[kTokenLanes][kChunkLanes];
+  const int lc = threadIdx.x % kChunkLanes;
+  const int lt = threadIdx.x / kChunkLanes;
+  const int i = blockIdx.x * kChunkLanes + lc;
   double s = 0.0;
-  for (int p = 0; p < splits; ++p) s += part[(size_t)p * K + i];
-  a[i] = (float)(s / (double)N);
+  if (i < K) {
+#pragma unroll 4
+    for (int p = lt; p < splits; p += kTokenLanes) s += part[(size_t)p * K + i];
+  }
+  red[lt][lc] = s;
+  __syncthreads();
+  if (lt == 0 && i < K) {
+    double t = red[0][lc];
+#pragma unroll
+    for (int u = 1; u < kTokenLanes; ++u) t += red[u][lc];
+    a[i] = (float)(t / (double)N);
+  }
 }
 
 }  // namespace
@@ -118,8 +133,8 @@ hipError_t launch_act_stats(const uint16_t* X, int N, int K, float* a_out, doubl
                        tps, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_act_stats_finalize, dim3((K + kThreads - 1) / kThreads), dim3(kThreads),
-                     0, stream, partials, splits, N, K, a_out);
+  hipLaunchKernelGGL(k_act_stats_finalize, dim3((K + kChunkLanes - 1) / kChunkLanes),
+                     dim3(kThreads), 0, stream, partials, splits, N, K, a_out);
   return hipGetLastError();
 }
 

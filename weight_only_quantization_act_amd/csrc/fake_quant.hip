@@ -84,8 +84,10 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant_delta(
 #pragma unroll
       for (int i = 0; i < 8; ++i) s[i] = 1.0f;
     }
+    // 1/s only enters the weight error fed to the fp16 loss product (not the codes), so
+    // the hardware reciprocal (1 ulp) is accurate enough.
 #pragma unroll
-    for (int i = 0; i < 8; ++i) inv[i] = 1.0f / s[i];
+    for (int i = 0; i < 8; ++i) inv[i] = __builtin_amdgcn_rcpf(s[i]);
 
     uint16_t* out = dW + (size_t)k * M * K;
 #pragma unroll
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant_delta(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float d = (code[i] - z) * st;   // quantised scaled weight
-        e[i] = w[r][i] - d * inv[i];          // weight error of the de-scaled weight
+        e[i] = (v[i] - d) * inv[i];           // weight error, W - Q(W s)/s = (v - d)/s
       }
       if (col_ok) *(u32x4*)(out + (size_t)(row0 + r) * K + col0) = pack8(e);
     }

@@ -55,7 +55,6 @@ namespace awq {
 namespace {
 
 constexpr int BM = kLossBM, BN = kLossBN;
-constexpr int kThreads = 256;
 constexpr int kBandM = 4;  // tile-rows per raster band
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -346,32 +345,30 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
 
 using LossStage = Stage<LOSS_BK, LOSS_NS, LOSS_WM, LOSS_WN>;
 
-__global__ __launch_bounds__(256) void k_reduce_select(const double* __restrict__ partials,
-                                                       int n_alpha, int tiles,
-                                                       const float* __restrict__ s_table,
-                                                       int K, double* __restrict__ losses,
-                                                       int32_t* __restrict__ best_out,
-                                                       int32_t* __restrict__ status_out,
-                                                       float* __restrict__ s_out) {
-  __shared__ double red[256];
+// Per-alpha loss = fixed-order fp64 sum of its tile partials (wave w handles alphas
+// w, w + 16, ...: lane-strided sums, then a butterfly in a fixed order), then the argmin
+// over finite losses (first index on ties) and the chosen scale vector.
+constexpr int kSelectThreads = 1024;
+
+__global__ __launch_bounds__(kSelectThreads) void k_reduce_select(
+    const double* __restrict__ partials, int n_alpha, int tiles, const float* __restrict__ s_table,
+    int K, double* __restrict__ losses, int32_t* __restrict__ best_out,
+    int32_t* __restrict__ status_out, float* __restrict__ s_out) {
   __shared__ double lsh[kMaxAlpha];
   __shared__ int best_sh;
   const int tid = threadIdx.x;
-  for (int k = 0; k < n_alpha; ++k) {
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int k = wave; k < n_alpha; k += kSelectThreads / 64) {
     double acc = 0.0;
-    for (int i = tid; i < tiles; i += 256) acc += partials[(size_t)k * tiles + i];
-    red[tid] = acc;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-      if (tid < w) red[tid] += red[tid + w];
-      __syncthreads();
+    for (int i = lane; i < tiles; i += 64) acc += partials[(size_t)k * tiles + i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) {
+      lsh[k] = acc;
+      losses[k] = acc;
     }
-    if (tid == 0) {
-      lsh[k] = red[0];
-      losses[k] = red[0];
-    }
-    __syncthreads();
   }
+  __syncthreads();
   if (tid == 0) {
     int best = -1;
     double bl = 0.0;
@@ -388,7 +385,8 @@ __global__ __launch_bounds__(256) void k_reduce_select(const double* __restrict_
   }
   __syncthreads();
   const int best = best_sh;
-  for (int i = tid; i < K; i += 256) s_out[i] = best >= 0 ? s_table[(size_t)best * K + i] : 1.0f;
+  for (int i = tid; i < K; i += kSelectThreads)
+    s_out[i] = best >= 0 ? s_table[(size_t)best * K + i] : 1.0f;
 }
 
 }  // namespace
@@ -408,8 +406,8 @@ hipError_t launch_loss_gemm(const uint16_t* dW, const uint16_t* X, int M, int N,
 hipError_t launch_reduce_select(const double* partials, int n_alpha, int tiles,
                                 const float* s_table, int K, double* losses, int32_t* best,
                                 int32_t* status, float* s_out, hipStream_t stream) {
-  hipLaunchKernelGGL(k_reduce_select, dim3(1), dim3(256), 0, stream, partials, n_alpha, tiles,
-                     s_table, K, losses, best, status, s_out);
+  hipLaunchKernelGGL(k_reduce_select, dim3(1), dim3(kSelectThreads), 0, stream, partials, n_alpha,
+                     tiles, s_table, K, losses, best, status, s_out);
   return hipGetLastError();
 }
 

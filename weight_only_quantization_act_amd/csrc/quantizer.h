@@ -17,8 +17,10 @@
 //   dequantised scaled value d = (code - zero) * step        one fp32 rounding
 // Every operation is a single IEEE fp32 operation: no contraction into FMA (the build
 // uses -ffp-contract=off and this header turns it off again), divisions correctly
-// rounded, rint = round half to even (v_rndne_f32), fp32 denormals kept.  That makes
-// the codes bit-identical to any implementation that performs the same operations.
+// rounded, rint = round half to even (v_rndne_f32), fp32 denormals kept.  The quotient
+// v / step is evaluated through a reciprocal with an exact fallback near ties (see
+// round_quotient), which provably yields the same integer.  That makes the codes
+// bit-identical to any implementation that performs the same operations.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,18 +30,70 @@
 
 namespace awq {
 
+// Cross-lane max/min inside aligned groups of LANES lanes (4, 8 or 16) with DPP moves.
+// max and min are exact, so any pattern that lets every lane see every member of its
+// group gives the same result: row_mirror (lane i <-> 15-i within 16), row_half_mirror
+// (i <-> 7-i within 8), then quad swaps (i <-> i^1, i <-> i^2).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xf, 0xf, false));
+}
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+
 template <int LANES>
 __device__ __forceinline__ float group_max(float x) {
-#pragma unroll
-  for (int m = 1; m < LANES; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16, "group of 4, 8 or 16 lanes");
+  if constexpr (LANES == 16) x = fmaxf(x, dpp_mov<kDppRowMirror>(x));
+  if constexpr (LANES >= 8) x = fmaxf(x, dpp_mov<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_mov<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_mov<kDppQuadXor2>(x));
   return x;
 }
 
 template <int LANES>
 __device__ __forceinline__ float group_min(float x) {
-#pragma unroll
-  for (int m = 1; m < LANES; m <<= 1) x = fminf(x, __shfl_xor(x, m));
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16, "group of 4, 8 or 16 lanes");
+  if constexpr (LANES == 16) x = fminf(x, dpp_mov<kDppRowMirror>(x));
+  if constexpr (LANES >= 8) x = fminf(x, dpp_mov<kDppRowHalfMirror>(x));
+  x = fminf(x, dpp_mov<kDppQuadXor1>(x));
+  x = fminf(x, dpp_mov<kDppQuadXor2>(x));
   return x;
+}
+
+// rint(fl(v / st)) computed as rint(fl(v * inv)) with inv the hardware reciprocal of st
+// (relative error <= 2^-23), except near a half-integer.  With |v / st| <= 16 (true for
+// every element of a group and for -min / st), fl(v * inv) is within 16 * 3 * 2^-24 and
+// fl(v / st) within 16 * 2^-24 of the exact quotient, so the two are at most 2^-18 apart
+// and round to the same integer unless the product lies within 2^-18 of a half-integer.
+// r = |t - rint(t)| and r - 0.5 are exact (Sterbenz), so the test is exact; lanes inside
+// the band (about 1 in 10^5) and any non-finite case take the correctly rounded division.
+constexpr float kTieBand = 7.62939453125e-06f;  // 2^-17, twice the bound above
+
+__device__ __forceinline__ bool near_half(float t, float q) {
+  return !(fabsf(fabsf(t - q) - 0.5f) > kTieBand);
+}
+
+// The 8 quotients of a lane at once, so that the common case costs one branch per 8.
+__device__ __forceinline__ void round_quotients(const float (&v)[8], float st, float inv,
+                                                float (&q)[8]) {
+  bool any_near = false;
+  bool near[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = v[i] * inv;
+    q[i] = rintf(t);
+    near[i] = near_half(t, q[i]);
+    any_near |= near[i];
+  }
+  if (any_near) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (near[i]) q[i] = rintf(v[i] / st);
+  }
 }
 
 // Quantise the lane's 8 scaled values v[] of one group.  On return code[] holds the
@@ -59,13 +113,15 @@ __device__ __forceinline__ void quantize8(const float (&v)[8], int w_bit, bool z
     const float top = (float)((1 << w_bit) - 1);
     float st = (hi - lo) / top;
     if (st == 0.0f) st = 1.0f;
-    float z = rintf(-lo / st);
+    const float inv = __builtin_amdgcn_rcpf(st);
+    const float tz = -lo * inv;
+    float z = rintf(tz);
+    if (near_half(tz, z)) z = rintf(-lo / st);
     z = fminf(fmaxf(z, 0.0f), top);
+    float q[8];
+    round_quotients(v, st, inv, q);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float q = rintf(v[i] / st) + z;
-      code[i] = fminf(fmaxf(q, 0.0f), top);
-    }
+    for (int i = 0; i < 8; ++i) code[i] = fminf(fmaxf(q[i] + z, 0.0f), top);
     step = st;
     zero = z;
   } else {
@@ -77,12 +133,11 @@ __device__ __forceinline__ void quantize8(const float (&v)[8], int w_bit, bool z
     const float off = (float)(1 << (w_bit - 1));
     float st = m / qmax;
     if (st == 0.0f) st = 1.0f;
+    const float inv = __builtin_amdgcn_rcpf(st);
+    float q[8];
+    round_quotients(v, st, inv, q);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float q = rintf(v[i] / st);
-      q = fminf(fmaxf(q, -qmax), qmax);
-      code[i] = q + off;
-    }
+    for (int i = 0; i < 8; ++i) code[i] = fminf(fmaxf(q[i], -qmax), qmax) + off;
     step = st;
     zero = off;
   }
