@@ -196,7 +196,7 @@ def output_error_loss(dW64: np.ndarray, X16: np.ndarray, row_block: int = 1024) 
     in blocks only to bound memory (the sum is over rows, so blocking changes nothing but
     rounding order).
     """
-    X64 = np.asarray(X16).astype(F64)
+    X64 = np.asarray(X16, dtype=F64)     # no copy when the caller already passes fp64
     total = F64(0.0)
     for r0 in range(0, dW64.shape[0], row_block):
         Y = dW64[r0:r0 + row_block] @ X64.T
@@ -235,8 +235,9 @@ def search_scales(W16, X16, a32, alphas32, cfg: QConfig):
     s_table [n_alpha][K], losses [n_alpha] (float64), best (int), s_star [K] (float32)."""
     s_table = scale_family(a32, alphas32)
     losses = np.empty(len(alphas32), dtype=F64)
+    X64 = np.asarray(X16, dtype=F64)     # exact widening, done once for all grid points
     for k in range(len(alphas32)):
-        losses[k] = output_error_loss(delta_weight(W16, s_table[k], cfg), X16)
+        losses[k] = output_error_loss(delta_weight(W16, s_table[k], cfg), X64)
     best = select_best(losses)
     if best >= 0:
         s_star = s_table[best].copy()

@@ -1,0 +1,88 @@
+"""The four large workloads at full size, in the launch configuration the benchmark uses
+(whole alpha grid in one pass), against the CPU oracle.
+
+The oracle cannot evaluate these layers whole in a test (up to 6e14 flop in fp64), so:
+  - statistics are compared bit for bit on the full activations;
+  - the per-alpha losses, the chosen alpha and its scales are compared on a seeded subset
+    of output rows: the loss is a sum of per-row terms, so the GPU search run on W[rows]
+    must match the oracle on W[rows] exactly as for a small layer;
+  - at full size the loss must be additive over a split of the rows (two GPU searches on
+    the halves add up to the full one), and it must be finite with status OK;
+  - the packed codes, scales and zeros of the full layer (packed with the chosen scales)
+    must equal the oracle's on the subset rows, bit for bit.
+Inputs are the seeded synthetic stand-ins for calibration data described in synth/.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import weight_only_quantization_act_amd as awq
+from oracle import awq_oracle as O
+from synth import CONFIGS, alpha_grid, make_layer, row_subset
+from tests.gpu_util import check_search, dev, host, ocfg, requires_gpu, say
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+CASES = [("c3", 0, 512), ("c3", 1, 512), ("c4", 0, 256), ("c5", 0, 512)]
+
+
+@pytest.mark.parametrize("cfg_name,layer,rows", CASES, ids=[f"{c}_{l}" for c, l, _ in CASES])
+def test_full_size_layer(cfg_name, layer, rows):
+    spec = CONFIGS[cfg_name][layer]
+    M, K, N = spec.out_features, spec.in_features, spec.n_tokens
+    say(f"{spec.name}: generating W {M}x{K}, X {N}x{K}")
+    L = make_layer(spec)
+    cfg = awq.qconfig(spec.w_bit, spec.group_size, spec.zero_point)
+    alphas = alpha_grid(spec.n_alpha)
+    Wd, Xd = dev(L.W), dev(L.X)
+
+    say(f"{spec.name}: statistics")
+    a = awq.awq_act_stats(Xd)
+    a_h = host(a)
+    assert np.array_equal(a_h.view(np.uint32), O.act_stats(L.X).view(np.uint32))
+
+    say(f"{spec.name}: full search (GPU)")
+    ws = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, len(alphas), 0), dtype=torch.uint8,
+                     device="cuda")
+    full = awq.awq_search_scales(Wd, Xd, a, alphas, cfg, workspace=ws)
+    lf = host(full["losses"]).copy()
+    best = int(host(full["best"])[0])
+    assert int(host(full["status"])[0]) == awq.AWQ_OK and np.all(np.isfinite(lf))
+    assert best == int(np.argmin(lf))
+    s_star = host(full["s"]).copy()
+    del ws
+    torch.cuda.empty_cache()
+
+    say(f"{spec.name}: additivity over row halves")
+    h = (M // 2) // 256 * 256
+    top = awq.awq_search_scales(Wd[:h].contiguous(), Xd, a, alphas, cfg)
+    bot = awq.awq_search_scales(Wd[h:].contiguous(), Xd, a, alphas, cfg)
+    assert np.allclose(lf, host(top["losses"]) + host(bot["losses"]), rtol=1e-12, atol=0)
+    del top, bot
+    torch.cuda.empty_cache()
+
+    say(f"{spec.name}: pack of the full layer")
+    codes, scales, zeros = awq.awq_quantize_pack(Wd, full["s"], cfg)
+    sub = row_subset(spec, rows)
+    c_sub, s_sub, z_sub = host(codes)[sub], host(scales)[sub], host(zeros)[sub]
+    del codes, scales, zeros
+
+    say(f"{spec.name}: search on {len(sub)} seeded rows (GPU and oracle)")
+    Wsub = np.ascontiguousarray(L.W[sub])
+    res_sub = awq.awq_search_scales(dev(Wsub), Xd, a, alphas, cfg)
+    torch.cuda.synchronize()
+    del Wd, Xd
+    torch.cuda.empty_cache()
+    orc = O.search_scales(Wsub, L.X, a_h, alphas, ocfg(cfg))
+    lg, lo, bg, bo = check_search(res_sub, orc, f"{spec.name} rows")
+    say(f"{spec.name}: subset losses max rel err {np.max(np.abs(lg - lo) / lo):.2e}; "
+        f"subset best gpu {bg} oracle {bo}; full-layer best {best}")
+
+    pk, sc, zr = O.quantize_pack(Wsub, s_star, ocfg(cfg))
+    assert np.array_equal(c_sub, pk)
+    assert np.array_equal(s_sub.view(np.uint16), sc.view(np.uint16))
+    assert np.array_equal(z_sub.view(np.uint16), zr.view(np.uint16))
+    del L
+    gc.collect()
