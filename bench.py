@@ -18,6 +18,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -33,14 +34,14 @@ def parse():
     p.add_argument("--config", default="c2", help="workload name (c1 .. c5)")
     p.add_argument("--layer", type=int, default=0, help="layer index within the workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=256,
+    p.add_argument("--cpu-rows", type=int, default=4096,
                    help="rows of W in the oracle's timed sample")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after timing, run one device-to-device copy of this many MiB (a kernel of "
                         "known traffic, used to scale the HBM byte counters)")
-    p.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                                                          "profiles", "loss_gemm_c2_traffic.json"),
-                   help="HBM bytes per loss-product launch measured with rocprofv3 counters")
+    p.add_argument("--traffic-summary", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                             "profiles", "loss_gemm_c2_counters.md"),
+                   help="rocprofv3 counter summary holding the HBM bytes per loss-product launch")
     return p.parse_args()
 
 
@@ -186,15 +187,18 @@ def main():
     fq_bytes = 2.0 * M * K + 4.0 * K * nA + 2.0 * M * K * nA
     pack_bytes = 2.0 * M * K + 4.0 * K + M * K / 2 + 4.0 * M * K / g
 
+    # HBM bytes per launch from the committed counter summary, valid only for the kernel
+    # source and workload it was measured on (null otherwise).
     traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            with open(args.traffic_json) as f:
-                tj = json.load(f)
-            if tj.get("workload") == spec.name and tj.get("kernel_source_sha") == _kernel_sha():
-                traffic = tj.get("hbm_bytes_per_launch")
-        except Exception:  # noqa: BLE001
-            traffic = None
+    if os.path.exists(args.traffic_summary):
+        kv = {}
+        with open(args.traffic_summary) as f:
+            for ln in f:
+                m = re.match(r"^(kernel_source_sha|workload|hbm_bytes_per_launch): (\S+)\s*$", ln)
+                if m:
+                    kv[m.group(1)] = m.group(2)
+        if kv.get("workload") == spec.name and kv.get("kernel_source_sha") == _kernel_sha():
+            traffic = float(kv["hbm_bytes_per_launch"])
 
     line = {
         "metric": "AWQ layers/s at 4096x4096; loss-GEMM TFLOP/s & MFMA util; pack GB/s",
