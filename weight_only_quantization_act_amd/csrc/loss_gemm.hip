@@ -49,6 +49,9 @@
 #ifndef LOSS_WN
 #define LOSS_WN 4
 #endif
+#ifndef LOSS_SCHED
+#define LOSS_SCHED 0
+#endif
 
 namespace awq {
 
@@ -209,9 +212,13 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     else return sm3;
   };
 
+  // LDS byte addresses of the stage buffers (uniform, computed once).
+  const unsigned lds_stage[4] = {lds_addr(sm0), lds_addr(sm1), lds_addr(sm2), lds_addr(sm3)};
+
   auto dma_stage = [&](auto st, int k0) {
-    uint8_t* sa = stage_ptr(st);
-    uint8_t* sb = sa + S::A_BYTES;
+    constexpr int ST = decltype(st)::value;
+    const unsigned la = lds_stage[ST] + (unsigned)(wave * S::DMA_A) * 1024u;
+    const unsigned lb = lds_stage[ST] + (unsigned)S::A_BYTES + (unsigned)(wave * S::DMA_B) * 1024u;
     const bool k_ok0 = k0 + dma_lchunk_even * 8 < K;
     const bool k_ok1 = k0 + dma_lchunk_odd * 8 < K;
     const unsigned va0 = k_ok0 ? vo_a0 : kOutOfRange, va1 = k_ok1 ? vo_a1 : kOutOfRange;
@@ -219,12 +226,10 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     const unsigned kbytes = (unsigned)k0 * 2u;
 #pragma unroll
     for (int j = 0; j < S::DMA_A; ++j)
-      dma16(rsrc_a, lds_addr(sa + (wave * S::DMA_A + j) * 1024), (j & 1) ? va1 : va0,
-            kbytes + j * dma_row_stride);
+      dma16(rsrc_a, la + j * 1024u, (j & 1) ? va1 : va0, kbytes + j * dma_row_stride);
 #pragma unroll
     for (int j = 0; j < S::DMA_B; ++j)
-      dma16(rsrc_b, lds_addr(sb + (wave * S::DMA_B + j) * 1024), (j & 1) ? vb1 : vb0,
-            kbytes + j * dma_row_stride);
+      dma16(rsrc_b, lb + j * 1024u, (j & 1) ? vb1 : vb0, kbytes + j * dma_row_stride);
   };
 
   // ---- fragment reads: MFMA 32x32x16 f16 operand = row (l mod 32), channels
@@ -257,6 +262,19 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // Interleave one k-step's MFMAs with the LDS reads of the next step's fragments so
+  // that neither the matrix pipe nor the LDS sees a burst.
+  auto interleave = [&]() {
+#if LOSS_SCHED
+    constexpr int NM = S::MI * S::NI, ND = S::MI + S::NI;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
+      if (i < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+#endif
+  };
+
   auto mma = [&](const Frag& f) {
 #pragma unroll
     for (int mi = 0; mi < S::MI; ++mi)
@@ -265,7 +283,9 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
   };
 
-  const int nk = (K + S::BK - 1) / S::BK;
+  // k-tiles rounded up to a multiple of NS: the padding tiles lie past in_features, read
+  // as zeros and add nothing, and the NS-unrolled loop below then has a single exit.
+  const int nk = ((K + S::BK * S::NS - 1) / (S::BK * S::NS)) * S::NS;
 
   // ---- pipeline: NS stages in flight; a stage buffer is refilled right after the
   //      barrier that follows the last fragment read from it.  DMAs are issued for
@@ -298,24 +318,27 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     for (int ks = 0; ks + 2 < S::KSTEPS; ks += 2) {
       load_frag(st, ks + 1, f1);
       mma(f0);
+      interleave();
       load_frag(st, ks + 2, f0);
       mma(f1);
+      interleave();
     }
     load_frag(st, S::KSTEPS - 1, f1);
     mma(f0);
+    interleave();
     // stage kt+1 has landed (own DMAs) and this wave's reads of stage kt are done
     __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 2) * S::PER_STAGE>::value);
     __builtin_amdgcn_s_barrier();
     dma_stage(st, (kt + S::NS) * S::BK);
-    if (kt + 1 < nk) load_frag(NEXT{}, 0, f0);
+    load_frag(NEXT{}, 0, f0);  // after the last k-tile this reads a slot nobody uses
     mma(f1);
   };
 
   for (int kt = 0; kt < nk; kt += S::NS) {
     step(I0{}, kt);
-    if constexpr (S::NS > 1) { if (kt + 1 >= nk) break; step(I1{}, kt + 1); }
-    if constexpr (S::NS > 2) { if (kt + 2 >= nk) break; step(I2{}, kt + 2); }
-    if constexpr (S::NS > 3) { if (kt + 3 >= nk) break; step(I3{}, kt + 3); }
+    if constexpr (S::NS > 1) step(I1{}, kt + 1);
+    if constexpr (S::NS > 2) step(I2{}, kt + 2);
+    if constexpr (S::NS > 3) step(I3{}, kt + 3);
   }
   __builtin_amdgcn_s_waitcnt(WaitVmLgkm<0>::value);  // no LDS write may outlive the block
 
