@@ -288,3 +288,113 @@ def run_layer(W16, X16, alphas32, cfg: QConfig):
     packed, scales, zeros = quantize_pack(W16, res["s_star"], cfg)
     res.update({"a": a32, "packed": packed, "scales": scales, "zeros": zeros})
     return res
+
+
+# --------------------------------------------------------------------------------------
+# Variants of the statistic and of the scale family (widening beyond the mean |x| / a^alpha
+# path).  Each is a separate reading of a page; the search itself is unchanged.
+# --------------------------------------------------------------------------------------
+def act_stat_max_abs(X16: np.ndarray) -> np.ndarray:
+    """a_i = max_t |x_{t,i}| [GPTQ-AWQ §3 二.2 (s = (max|A|)^alpha)].  Exact in fp32."""
+    X16 = np.asarray(X16)
+    if X16.shape[0] <= 0:
+        raise ValueError("needs at least one token")
+    return np.abs(X16).max(axis=0).astype(F32)
+
+
+def act_stat_rms_ratio(X16: np.ndarray, channel_chunk: int = 1024) -> np.ndarray:
+    """a_i = E|x_i| / sqrt(E[x_i^2]) [AWQ-blog §1.2 (importance score)], fp64, rounded to
+    fp32.  Reading: a channel whose E[x^2] is 0 gets a_i = 0."""
+    X16 = np.asarray(X16)
+    N, K = X16.shape
+    if N <= 0:
+        raise ValueError("needs at least one token")
+    out = np.empty(K, dtype=F32)
+    for c0 in range(0, K, channel_chunk):
+        c1 = min(K, c0 + channel_chunk)
+        col = X16[:, c0:c1].astype(F64)
+        m1 = np.abs(col).sum(axis=0) / F64(N)
+        m2 = (col * col).sum(axis=0) / F64(N)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            r = np.where(m2 > 0, m1 / np.sqrt(m2), F64(0.0))
+        out[c0:c1] = r.astype(F32)
+    return out
+
+
+def act_stat_ema_mean(X16: np.ndarray, batch_tokens: int, momentum: float = 0.9) -> np.ndarray:
+    """Exponential moving average of the per-batch mean |x| over consecutive batches of
+    `batch_tokens` tokens: e <- momentum * e + (1 - momentum) * mean_batch |x|, starting
+    from e = 0 [AWQ-blog §2.1 (calibration statistics pseudo-code, momentum 0.9)].
+    Reading: batches are consecutive token ranges, the last may be shorter; fp64
+    throughout, rounded to fp32 at the end.  (The page's running max of amax|x| over
+    batches is the global max, i.e. act_stat_max_abs.)"""
+    X16 = np.asarray(X16)
+    N, K = X16.shape
+    if N <= 0 or batch_tokens <= 0:
+        raise ValueError("needs tokens and a positive batch size")
+    mom = F64(momentum)
+    keep = F64(1.0) - mom
+    e = np.zeros(K, dtype=F64)
+    for t0 in range(0, N, batch_tokens):
+        blk = X16[t0:t0 + batch_tokens].astype(F64)
+        m = np.abs(blk).sum(axis=0) / F64(blk.shape[0])
+        e = mom * e + keep * m
+    return e.astype(F32)
+
+
+def percentile_linear(a32: np.ndarray, percentile: float) -> float:
+    """The p-th percentile with linear interpolation between order statistics, in fp64:
+    position (p/100)(K-1) in the sorted values [AWQ-tut 显著识别 (threshold at a high
+    percentile of the importance scores)]."""
+    v = np.sort(np.asarray(a32, dtype=F32)).astype(F64)
+    pos = F64(percentile) / F64(100.0) * F64(v.size - 1)
+    lo = int(np.floor(pos))
+    hi = min(lo + 1, v.size - 1)
+    frac = pos - F64(lo)
+    return float(v[lo] + frac * (v[hi] - v[lo]))
+
+
+def threshold_scales(a32: np.ndarray, percentile: float, factor: float) -> np.ndarray:
+    """Fixed-factor protection: s_i = factor for channels whose statistic exceeds the
+    percentile threshold, 1 otherwise [AWQ-tut 显著识别 (indicator 1_i = [a_i > tau]),
+    缩放保护 (protect by a factor s > 1), Python 演示 (70th percentile, factor 2)]."""
+    tau = percentile_linear(a32, percentile)
+    a64 = np.asarray(a32, dtype=F32).astype(F64)
+    return np.where(a64 > tau, F32(factor), F32(1.0)).astype(F32)
+
+
+def search_scale_table(W16, X16, s_table32, cfg: QConfig):
+    """The search of search_scales over an explicit table of candidate scale vectors."""
+    s_table32 = np.asarray(s_table32, dtype=F32)
+    losses = np.empty(s_table32.shape[0], dtype=F64)
+    X64 = np.asarray(X16, dtype=F64)
+    for k in range(s_table32.shape[0]):
+        losses[k] = output_error_loss(delta_weight(W16, s_table32[k], cfg), X64)
+    best = select_best(losses)
+    s_star = s_table32[best].copy() if best >= 0 else np.ones(s_table32.shape[1], F32)
+    return {"s_table": s_table32, "losses": losses, "best": best, "s_star": s_star}
+
+
+def hadamard_matrix(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix H_n (n a power of two): H_1 = [1],
+    H_2m = [[H_m, H_m], [H_m, -H_m]] (fp64)."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("n must be a power of two")
+    H = np.ones((1, 1), dtype=F64)
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def hadamard_rotate(A16: np.ndarray, block: int) -> np.ndarray:
+    """Rotate every row of A (fp16 [rows][K]) by the block-diagonal orthogonal matrix whose
+    blocks are H_block / sqrt(block) along K [AWQ-notes §5.1 (WX = (WR)(R^T X) for
+    orthogonal R; normalised Hadamard spreads an outlier), §5.2 (structured fast
+    rotation)].  Computed in fp64 as an explicit product, rounded to fp16."""
+    A = np.asarray(A16).astype(F64)
+    R, K = A.shape
+    if K % block:
+        raise ValueError("block must divide in_features")
+    Hn = hadamard_matrix(block) / np.sqrt(F64(block))
+    out = (A.reshape(R, K // block, block) @ Hn).reshape(R, K)
+    return out.astype(np.float16)

@@ -468,4 +468,126 @@ def pin_group_metadata_overhead():
     assert abs(total - fig["overhead_bytes"]) <= fig["rel_tol"] * fig["overhead_bytes"]
 
 
+
+
+# ---------------------------------------------------------------- statistic / scale variants
+def pin_max_abs_stat():
+    """max |x| per channel over tokens [GPTQ-AWQ §3 二.2]: exact on constructed columns."""
+    X = np.array([[1.0, -2.0, 0.0], [-3.0, 0.5, 0.0], [2.5, -0.25, 0.0]], F16)
+    assert np.array_equal(O.act_stat_max_abs(X), np.array([3.0, 2.0, 0.0], F32))
+
+
+def pin_rms_ratio_stat():
+    """E|x| / sqrt(E x^2) [AWQ-blog §1.2]: 1 for constant magnitude, sqrt(2/pi) for N(0,1),
+    1/sqrt(2) for Student-t(4), 0 for an all-zero channel."""
+    rng = np.random.default_rng(31)
+    N = 64
+    X = (np.sign(rng.standard_normal((N, 3))) * np.array([0.5, 7.25, 0.0])).astype(F16)
+    r = O.act_stat_rms_ratio(X)
+    assert r[0] == 1.0 and r[1] == 1.0 and r[2] == 0.0
+    n = 2_000_000
+    rn = float(O.act_stat_rms_ratio(rng.standard_normal((n, 1)).astype(F16))[0])
+    assert abs(rn - math.sqrt(2 / math.pi)) < 2e-3
+    rt = float(O.act_stat_rms_ratio(rng.standard_t(4.0, (n, 1)).astype(F16))[0])
+    assert abs(rt - 1 / math.sqrt(2)) < 1e-2
+
+
+def pin_ema_stat():
+    """EMA of batch means with momentum 0.9 from 0 [AWQ-blog §2.1]: equal batch means m
+    give (1 - 0.9^n) m; two batches give 0.1 (0.9 m1 + m2); one batch gives 0.1 m."""
+    mom = _golden("deployment_figures.json")["ema_statistics"]["momentum"]
+    m = 3.0
+    X = np.full((40, 2), m, F16)
+    X[:, 1] = -m
+    e = O.act_stat_ema_mean(X, 8, mom)          # 5 batches of 8 tokens
+    assert np.allclose(e, (1 - mom ** 5) * m, rtol=1e-6)
+    X2 = np.concatenate([np.full((10, 1), 1.0, F16), np.full((10, 1), 4.0, F16)])
+    e2 = O.act_stat_ema_mean(X2, 10, mom)
+    assert np.allclose(e2, (1 - mom) * (mom * 1.0 + 4.0), rtol=1e-6)
+    assert np.allclose(O.act_stat_ema_mean(X2, 20, mom), (1 - mom) * 2.5, rtol=1e-6)
+    # a short last batch averages over its own tokens
+    X3 = np.concatenate([np.full((8, 1), 2.0, F16), np.full((3, 1), 5.0, F16)])
+    assert np.allclose(O.act_stat_ema_mean(X3, 8, mom), (1 - mom) * (mom * 2.0 + 5.0), rtol=1e-6)
+
+
+def pin_percentile_threshold():
+    """The threshold is the linear-interpolation percentile (checked against numpy's
+    routine), and with the tutorial's demo layout [AWQ-tut Python 演示: 70th percentile,
+    factor 2, 128 channels half at base activation 0.3 and half at 5.0] the protected
+    channels are exactly the top 30% by rank, all from the high half, scaled by 2."""
+    rng = np.random.default_rng(32)
+    for K in (5, 64, 1000):
+        a = np.abs(rng.standard_normal(K)).astype(F32)
+        for p in (0, 37.5, 70, 85, 99, 100):
+            assert math.isclose(O.percentile_linear(a, p),
+                                float(np.percentile(a.astype(F64), p, method="linear")),
+                                rel_tol=1e-12, abs_tol=1e-15)
+    demo = _golden("deployment_figures.json")["protection_demo"]
+    K = demo["n_channels"]
+    base = np.ones(K)
+    base[: K // 2] = demo["low_base"]
+    base[K // 2:] = demo["high_base"]
+    X = (rng.standard_normal((256, K)) * demo["noise"] + base).astype(F16)
+    a = O.act_stats(X)
+    s = O.threshold_scales(a, demo["percentile"], demo["factor"])
+    prot = s == F32(demo["factor"])
+    pos = demo["percentile"] / 100 * (K - 1)
+    assert prot.sum() == K - (math.floor(pos) + 1)
+    assert np.all(prot[: K // 2] == 0)
+    assert np.all(s[~prot] == 1.0)
+    ranks = np.argsort(np.argsort(a))
+    assert np.array_equal(prot, ranks > math.floor(pos))
+
+
+def pin_scale_table_search():
+    """Searching an explicit table equals searching the alpha family it came from; a
+    table of all-ones scales gives the plain quantiser's loss."""
+    rng = np.random.default_rng(33)
+    W = (rng.standard_normal((16, 256)) * 0.02).astype(F16)
+    X = rng.standard_normal((40, 256)).astype(F16)
+    X[:, 3] *= 30
+    a = O.act_stats(X)
+    al = (np.arange(6) / 5).astype(F32)
+    cfg = _cfg(4, 128, 1)
+    r1 = O.search_scales(W, X, a, al, cfg)
+    r2 = O.search_scale_table(W, X, O.scale_family(a, al), cfg)
+    assert np.array_equal(r1["losses"], r2["losses"]) and r1["best"] == r2["best"]
+    r3 = O.search_scale_table(W, X, np.ones((1, 256), F32), cfg)
+    assert r3["losses"][0] == r1["losses"][0]
+
+
+def pin_hadamard_example():
+    """[AWQ-notes §5.1] the normalised 4x4 Hadamard maps [0.1, 0.2, 20, 0.1] to about
+    [10.2, 9.9, -9.9, -10.0] and keeps the squared norm 400.06."""
+    ex = _golden("awq_notes_examples.json")["hadamard_rotation"]
+    x = np.array([ex["before"]], F16)
+    y = O.hadamard_rotate(x, 4).astype(F64)[0]
+    assert np.allclose(y, ex["after"], atol=ex["tol_abs"])
+    assert abs(float(np.sum(y * y)) - ex["squared_norm"]) < 0.2
+    assert abs(float(np.sum(x.astype(F64) ** 2)) - ex["squared_norm"]) < 0.2
+
+
+def pin_hadamard_orthogonal():
+    """H_n is the Sylvester matrix (checked against scipy's construction), H H^T = n I, the
+    normalised block rotation is an involution, and with Q = identity the reparameterised
+    layer computes the same output: (W R)(X R)^T = W X^T [AWQ-notes §5.1]."""
+    from scipy.linalg import hadamard as scipy_hadamard
+    for n in (1, 2, 4, 16, 128):
+        H = O.hadamard_matrix(n)
+        assert np.array_equal(H, scipy_hadamard(n).astype(F64))
+        assert np.array_equal(H @ H.T, n * np.eye(n))
+    rng = np.random.default_rng(34)
+    A = (rng.standard_normal((6, 256)) * 0.5).astype(F16)
+    twice = O.hadamard_rotate(O.hadamard_rotate(A, 64), 64)
+    assert np.allclose(twice.astype(F64), A.astype(F64), atol=4e-3, rtol=4e-3)
+    W = rng.standard_normal((5, 128))
+    X = rng.standard_normal((7, 128))
+    R = O.hadamard_matrix(128) / np.sqrt(128.0)
+    assert np.allclose((W @ R) @ (X @ R).T, W @ X.T, atol=1e-10)
+    x = np.zeros((1, 128), F16)
+    x[0, 5] = 16.0                                  # one outlier spreads evenly
+    y = O.hadamard_rotate(x, 128).astype(F64)
+    assert np.allclose(np.abs(y), 16.0 / np.sqrt(128.0), rtol=1e-3)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -207,6 +207,69 @@ MUTANTS = {
 }
 
 
+def _max_signed(X16):
+    return np.asarray(X16).max(axis=0).astype(F32)
+
+
+def _rms_no_sqrt(X16, channel_chunk=1024):
+    X = np.asarray(X16).astype(F64)
+    m1 = np.abs(X).mean(axis=0)
+    m2 = (X * X).mean(axis=0)
+    with np.errstate(all="ignore"):
+        return np.where(m2 > 0, m1 / m2, 0.0).astype(F32)
+
+
+def _ema_swapped(X16, batch_tokens, momentum=0.9):
+    X16 = np.asarray(X16)
+    e = np.zeros(X16.shape[1])
+    for t0 in range(0, X16.shape[0], batch_tokens):
+        m = np.abs(X16[t0:t0 + batch_tokens].astype(F64)).mean(axis=0)
+        e = (1 - momentum) * e + momentum * m
+    return e.astype(F32)
+
+
+def _percentile_no_interp(a32, percentile):
+    v = np.sort(np.asarray(a32, F32)).astype(F64)
+    return float(v[int(percentile / 100 * (v.size - 1))])
+
+
+def _percentile_wrong_pos(a32, percentile):
+    v = np.sort(np.asarray(a32, F32)).astype(F64)
+    pos = min(percentile / 100 * v.size, v.size - 1)
+    lo = int(np.floor(pos)); hi = min(lo + 1, v.size - 1)
+    return float(v[lo] + (pos - lo) * (v[hi] - v[lo]))
+
+
+def _threshold_inverted(a32, percentile, factor):
+    tau = O.percentile_linear(a32, percentile)
+    return np.where(np.asarray(a32, F64) < tau, F32(factor), F32(1.0)).astype(F32)
+
+
+def _hadamard_wrong_sign(n):
+    H = np.ones((1, 1))
+    while H.shape[0] < n:
+        H = np.block([[H, H], [-H, H]])
+    return H
+
+
+def _hadamard_rotate_unnormalised(A16, block):
+    A = np.asarray(A16).astype(F64)
+    R, K = A.shape
+    return (A.reshape(R, K // block, block) @ O.hadamard_matrix(block)).reshape(R, K).astype(np.float16)
+
+
+MUTANTS.update({
+    "max_signed": ("act_stat_max_abs", _max_signed),
+    "rms_ratio_without_sqrt": ("act_stat_rms_ratio", _rms_no_sqrt),
+    "ema_momentum_swapped": ("act_stat_ema_mean", _ema_swapped),
+    "percentile_no_interpolation": ("percentile_linear", _percentile_no_interp),
+    "percentile_position_K": ("percentile_linear", _percentile_wrong_pos),
+    "threshold_inverted": ("threshold_scales", _threshold_inverted),
+    "hadamard_wrong_recursion": ("hadamard_matrix", _hadamard_wrong_sign),
+    "hadamard_unnormalised": ("hadamard_rotate", _hadamard_rotate_unnormalised),
+})
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
