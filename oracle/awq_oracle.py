@@ -390,11 +390,14 @@ def hadamard_rotate(A16: np.ndarray, block: int) -> np.ndarray:
     """Rotate every row of A (fp16 [rows][K]) by the block-diagonal orthogonal matrix whose
     blocks are H_block / sqrt(block) along K [AWQ-notes §5.1 (WX = (WR)(R^T X) for
     orthogonal R; normalised Hadamard spreads an outlier), §5.2 (structured fast
-    rotation)].  Computed in fp64 as an explicit product, rounded to fp16."""
+    rotation)].  The product with the +-1 matrix H is taken first, in fp64, where it is
+    exact for fp16 inputs (sums of at most 512 multiples of 2^-24 below 2^16 fit in 53
+    bits, whatever order or fused operations the matmul uses); the normalisation
+    1/sqrt(block) is then the one rounding, and the cast to fp16 rounds to nearest even."""
     A = np.asarray(A16).astype(F64)
     R, K = A.shape
     if K % block:
         raise ValueError("block must divide in_features")
-    Hn = hadamard_matrix(block) / np.sqrt(F64(block))
-    out = (A.reshape(R, K // block, block) @ Hn).reshape(R, K)
+    S = A.reshape(R, K // block, block) @ hadamard_matrix(block)
+    out = (S * (F64(1.0) / np.sqrt(F64(block)))).reshape(R, K)
     return out.astype(np.float16)
