@@ -34,6 +34,8 @@ def parse():
     p.add_argument("--config", default="c2", help="workload name (c1 .. c5)")
     p.add_argument("--layer", type=int, default=0, help="layer index within the workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip timing the statistic / threshold / rotation / table variants")
     p.add_argument("--cpu-rows", type=int, default=4096,
                    help="rows of W in the oracle's timed sample")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -236,6 +238,8 @@ def main():
         },
         "search_status": status,
     }
+    if not args.no_variants:
+        line["variants"] = time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N)
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib * (1 << 20) // 2, dtype=torch.float16, device="cuda")
         dst = torch.empty_like(src)
@@ -246,6 +250,43 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layer, alphas, cfg, args.cpu_rows)
     print(json.dumps(line), flush=True)
+
+
+def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, reps=20):
+    """Average time per call of the widened entry points on the same layer, measured
+    after the timed region (HIP events around `reps` back-to-back calls)."""
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(sptr)
+        for _ in range(reps):
+            fn()
+        e1.record(sptr)
+        torch.cuda.synchronize()
+        return e0.elapsed_ms(e1) / reps
+
+    out = {}
+    x_bytes = 2.0 * N * K + 4.0 * K
+    for name, mode, extra in [("stat_max_abs", awq.AWQ_STAT_MAX_ABS, ()),
+                              ("stat_rms_ratio", awq.AWQ_STAT_RMS_RATIO, ()),
+                              ("stat_ema_mean_b512", awq.AWQ_STAT_EMA_MEAN, (512, 0.9))]:
+        ms = timed(lambda: awq.awq_act_stats_ex(Xd, mode, *extra))
+        out[name] = {"ms": ms, "GB/s": x_bytes / (ms * 1e-3) / 1e9}
+    a = awq.awq_act_stats(Xd)
+    out["threshold_scales"] = {"ms": timed(lambda: awq.awq_threshold_scales(a, 70.0, 2.0)),
+                               "in_features": K}
+    Xr = torch.empty_like(Xd)
+    ms = timed(lambda: awq.awq_hadamard_rotate(Xd, 128, out=Xr))
+    out["hadamard_rotate_X_b128"] = {"ms": ms, "GB/s": 4.0 * N * K / (ms * 1e-3) / 1e9}
+    table = torch.stack([awq.awq_threshold_scales(a, p, f) for p in (50.0, 70.0, 85.0, 95.0, 99.0)
+                         for f in (1.5, 2.0, 3.0, 4.0)]).contiguous()
+    ws = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, table.shape[0], 0), dtype=torch.uint8,
+                     device="cuda")
+    ms = timed(lambda: awq.awq_search_scale_table(Wd, Xd, table, cfg, workspace=ws))
+    out["search_scale_table_20_threshold_rows"] = {"ms": ms}
+    return out
 
 
 def _kernel_sha():

@@ -83,6 +83,24 @@ size_t awq_act_stats_workspace_bytes(int64_t n_tokens, int64_t in_features);
 int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* a_out,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Other statistics (same workspace convention, sized by the _ex query):
+ *   AWQ_STAT_MEAN_ABS   mean |x|                                     (as awq_act_stats)
+ *   AWQ_STAT_MAX_ABS    max |x| over tokens [GPTQ-AWQ §3 二.2: s = (max|A|)^alpha]; exact
+ *   AWQ_STAT_RMS_RATIO  mean|x| / sqrt(mean x^2) in fp64 [AWQ-blog §1.2 importance score];
+ *                       0 for an all-zero channel; the fp64 sum of squares is not exact,
+ *                       so results may differ from another summation order by 1 ulp
+ *   AWQ_STAT_EMA_MEAN   e <- momentum*e + (1-momentum)*mean_batch|x| from e = 0 over
+ *                       consecutive batches of batch_tokens tokens (the last may be short)
+ *                       [AWQ-blog §2.1, momentum 0.9]; fp64, exact batch sums
+ * batch_tokens and momentum (in [0,1)) are read only for AWQ_STAT_EMA_MEAN.  The page's
+ * running max of max|x| over batches equals AWQ_STAT_MAX_ABS. */
+enum { AWQ_STAT_MEAN_ABS = 0, AWQ_STAT_MAX_ABS = 1, AWQ_STAT_RMS_RATIO = 2, AWQ_STAT_EMA_MEAN = 3 };
+size_t awq_act_stats_ex_workspace_bytes(int64_t n_tokens, int64_t in_features,
+                                        int32_t statistic, int64_t batch_tokens);
+int awq_act_stats_ex(const void* X, int64_t n_tokens, int64_t in_features, int32_t statistic,
+                     int64_t batch_tokens, double momentum, float* a_out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------------
  * A2-A5  scale search over an alpha grid
  *   For every alpha_k:  s_k = a^alpha_k (a_i == 0 -> 1)            [AWQ-notes §4.1]
@@ -120,6 +138,37 @@ int awq_search_scales(const void* W, const void* X, const float* a,
                       float* s_out, double* losses_out, int32_t* best_out,
                       int32_t* status_out, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* The same search over an explicit table of candidate scale vectors instead of a^alpha
+ * (e.g. fixed-factor protection scales, or scales built from another statistic).
+ *   s_table     fp32 [n_cand][in], device, 16-byte aligned, every entry > 0 (not checked)
+ *   n_cand      1 .. AWQ_MAX_ALPHA; other arguments as for awq_search_scales, and the
+ *               workspace is sized by awq_workspace_bytes(..., n_cand, batch). */
+int awq_search_scale_table(const void* W, const void* X, const float* s_table, int32_t n_cand,
+                           int64_t out_features, int64_t in_features, int64_t n_tokens,
+                           const awq_qconfig* cfg, float* s_out, double* losses_out,
+                           int32_t* best_out, int32_t* status_out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Fixed-factor protection scales: s_i = factor if a_i is above the percentile threshold of
+ * a, else 1 [AWQ-tut 显著识别 (indicator of channels above a high percentile, 70-90),
+ * 缩放保护 (protect by a factor > 1), Python 演示 (70th percentile, factor 2)].  The
+ * threshold interpolates linearly between order statistics at position
+ * (percentile/100)(K-1), in fp64; the comparison is made in fp64.  Non-finite a sort last.
+ *   a fp32 [in], s_out fp32 [in] (device); 1 <= in <= 32768; percentile in [0, 100];
+ *   factor finite and > 0. */
+int awq_threshold_scales(const float* a, int64_t in_features, double percentile, float factor,
+                         float* s_out, void* stream);
+
+/* Blockwise Hadamard rotation along the input dimension: every row of A is multiplied by
+ * the block-diagonal orthogonal matrix with blocks H_block / sqrt(block) (Sylvester order),
+ * so (W R)(X R)^T = W X^T when W and X are both rotated [AWQ-notes §5.1 (rotation keeps the
+ * product and spreads an outlier channel), §5.2 (fast structured rotation)].
+ *   A, out fp16 [rows][in] (device, 16-byte aligned; out may equal A); block a power of
+ *   two in [2, 512] dividing in; in a multiple of 8.  fp32 butterflies, fp16 (nearest
+ *   even) results. */
+int awq_hadamard_rotate(const void* A, int64_t rows, int64_t in_features, int32_t block,
+                        void* out, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * A3 alone: dW = W - Q(W diag(s)) diag(s)^-1 rounded to fp16, the operand the search's

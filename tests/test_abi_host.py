@@ -36,7 +36,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in awq_act.h but not exported"
     assert set(names) == set(_lib._SIGNATURES)
@@ -142,3 +142,59 @@ def test_pack_and_fake_quant_validation(L):
 
 def test_profile_hook_set_and_clear(L):
     assert L.awq_set_profile_events(None, None, None, None) == E["OK"]
+
+
+def test_stats_ex_validation(L):
+    f = L.awq_act_stats_ex
+    q = awq.awq_act_stats_ex_workspace_bytes
+    ws = q(64, 256, awq.AWQ_STAT_EMA_MEAN, 16)
+    assert ws > 0 and ws % 256 == 0
+    assert q(64, 256, 4, 0) == 0 and q(64, 256, -1, 0) == 0
+    assert q(64, 256, awq.AWQ_STAT_EMA_MEAN, 0) == 0
+    # the RMS ratio keeps two sums per split, so it needs more scratch than the mean
+    assert q(4096, 4096, awq.AWQ_STAT_RMS_RATIO, 0) > q(4096, 4096, awq.AWQ_STAT_MEAN_ABS, 0)
+    assert q(4096, 4096, awq.AWQ_STAT_MEAN_ABS, 0) == awq.awq_act_stats_workspace_bytes(4096, 4096)
+    assert f(P, 64, 256, 4, 0, 0.9, P, P, 1 << 30, None) == E["CONFIG"]
+    assert f(P, 64, 256, awq.AWQ_STAT_EMA_MEAN, 0, 0.9, P, P, 1 << 30, None) == E["SHAPE"]
+    assert f(P, 64, 256, awq.AWQ_STAT_EMA_MEAN, 16, 1.0, P, P, 1 << 30, None) == E["CONFIG"]
+    assert f(P, 64, 256, awq.AWQ_STAT_EMA_MEAN, 16, -0.1, P, P, 1 << 30, None) == E["CONFIG"]
+    assert f(P, 64, 256, awq.AWQ_STAT_EMA_MEAN, 16, float("nan"), P, P, 1 << 30, None) == E["CONFIG"]
+    assert f(P, 64, 256, awq.AWQ_STAT_EMA_MEAN, 16, 0.9, P, P, ws - 1, None) == E["WORKSPACE"]
+    assert f(P, 64, 256, awq.AWQ_STAT_MAX_ABS, 0, 0.0, None, P, 1 << 30, None) == E["NULL"]
+    assert f(P_ODD, 64, 256, awq.AWQ_STAT_MAX_ABS, 0, 0.0, P, P, 1 << 30, None) == E["ALIGN"]
+
+
+def test_table_threshold_hadamard_validation(L):
+    t = L.awq_search_scale_table
+    need = awq.awq_workspace_bytes(256, 256, 64, awq.qconfig(), 3, 1)
+
+    def tab(W=P, X=P, S=P, n=3, M=256, K=256, N=64, cfg=None, ws_bytes=1 << 40, s=P, ws=P):
+        return t(W, X, S, n, M, K, N, cfg if cfg is not None else _cfg(), s, P, P, P, ws,
+                 ws_bytes, None)
+
+    assert tab(S=None) == E["NULL"]
+    assert tab(ws=None) == E["WORKSPACE"]
+    assert tab(n=0) == E["ALPHA"] and tab(n=65) == E["ALPHA"]
+    assert tab(cfg=_cfg(4, 96)) == E["CONFIG"]
+    assert tab(K=200) == E["SHAPE"]
+    assert tab(ws_bytes=need - 1) == E["WORKSPACE"]
+    assert tab(S=ctypes.c_void_p(0x10008)) == E["ALIGN"]   # the table needs 16 bytes
+    th = L.awq_threshold_scales
+    assert th(None, 16, 70.0, 2.0, P, None) == E["NULL"]
+    assert th(P, 0, 70.0, 2.0, P, None) == E["SHAPE"]
+    assert th(P, 32769, 70.0, 2.0, P, None) == E["SHAPE"]
+    assert th(P, 16, 100.5, 2.0, P, None) == E["CONFIG"]
+    assert th(P, 16, float("nan"), 2.0, P, None) == E["CONFIG"]
+    assert th(P, 16, 70.0, 0.0, P, None) == E["CONFIG"]
+    assert th(P, 16, 70.0, float("inf"), P, None) == E["CONFIG"]
+    assert th(ctypes.c_void_p(0x10002), 16, 70.0, 2.0, P, None) == E["ALIGN"]
+    h = L.awq_hadamard_rotate
+    assert h(None, 4, 128, 64, P, None) == E["NULL"]
+    assert h(P, 4, 128, 3, P, None) == E["CONFIG"]
+    assert h(P, 4, 128, 1024, P, None) == E["CONFIG"]
+    assert h(P, 4, 96, 64, P, None) == E["SHAPE"]          # block does not divide K
+    assert h(P, 4, 4, 4, P, None) == E["SHAPE"]            # K not a multiple of 8
+    assert h(P, -1, 128, 64, P, None) == E["SHAPE"]
+    assert h(P, 1 << 20, 1 << 12, 64, P, None) == E["SHAPE"]
+    assert h(P_ODD, 4, 128, 64, P, None) == E["ALIGN"]
+    assert h(P, 0, 128, 64, P, None) == E["OK"]            # empty: nothing to do

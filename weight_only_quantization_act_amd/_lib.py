@@ -48,7 +48,17 @@ _SIGNATURES = {
     "awq_fake_quant_delta": (ctypes.c_int, [_vp, _vp, _i64, _i64, _cfgp, _vp, _vp]),
     "awq_quantize_pack": (ctypes.c_int, [_vp, _vp, _i64, _i64, _cfgp, _vp, _vp, _vp, _vp]),
     "awq_set_profile_events": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
+    "awq_act_stats_ex_workspace_bytes": (_sz, [_i64, _i64, _i32, _i64]),
+    "awq_act_stats_ex": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i64, ctypes.c_double, _vp, _vp,
+                                        _sz, _vp]),
+    "awq_search_scale_table": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _cfgp, _vp,
+                                              _vp, _vp, _vp, _vp, _sz, _vp]),
+    "awq_threshold_scales": (ctypes.c_int, [_vp, _i64, ctypes.c_double, ctypes.c_float, _vp,
+                                            _vp]),
+    "awq_hadamard_rotate": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
 }
+
+AWQ_STAT_MEAN_ABS, AWQ_STAT_MAX_ABS, AWQ_STAT_RMS_RATIO, AWQ_STAT_EMA_MEAN = 0, 1, 2, 3
 
 _LIB: Optional[ctypes.CDLL] = None
 
@@ -114,6 +124,12 @@ def _buf(nbytes: int, device) -> torch.Tensor:
 # ---------------------------------------------------------------------------------------
 def awq_act_stats_workspace_bytes(n_tokens: int, in_features: int) -> int:
     return int(lib().awq_act_stats_workspace_bytes(n_tokens, in_features))
+
+
+def awq_act_stats_ex_workspace_bytes(n_tokens: int, in_features: int, statistic: int,
+                                     batch_tokens: int = 0) -> int:
+    return int(lib().awq_act_stats_ex_workspace_bytes(n_tokens, in_features, statistic,
+                                                      batch_tokens))
 
 
 def awq_act_stats(X: torch.Tensor, out: Optional[torch.Tensor] = None,
@@ -223,3 +239,72 @@ def quantize_layer(W: torch.Tensor, X: torch.Tensor, alphas: Sequence[float],
     codes, scales, zeros = awq_quantize_pack(W, res["s"], cfg, stream=stream)
     res.update({"a": a, "codes": codes, "scales": scales, "zeros": zeros})
     return res
+
+
+def awq_act_stats_ex(X: torch.Tensor, statistic: int, batch_tokens: int = 0, momentum: float = 0.9,
+                     stream=None) -> torch.Tensor:
+    """Per-channel statistic of X fp16 [N, K] (see AWQ_STAT_*) -> fp32 [K]."""
+    _dev(X, torch.float16, "X")
+    N, K = X.shape
+    a = torch.empty(max(K, 1), dtype=torch.float32, device=X.device)
+    need = awq_act_stats_ex_workspace_bytes(N, K, statistic, batch_tokens)
+    ws = _buf(need, X.device)
+    st = lib().awq_act_stats_ex(_ptr(X), N, K, statistic, batch_tokens, float(momentum), _ptr(a),
+                                _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _check(st, "awq_act_stats_ex")
+    return a[:K]
+
+
+def awq_search_scale_table(W: torch.Tensor, X: torch.Tensor, s_table: torch.Tensor,
+                           cfg: awq_qconfig, workspace: Optional[torch.Tensor] = None,
+                           stream=None):
+    """The search over explicit candidate scales s_table fp32 [n_cand, K]."""
+    _dev(W, torch.float16, "W")
+    _dev(X, torch.float16, "X")
+    M, K = W.shape
+    N = X.shape[0]
+    _dev(s_table, torch.float32, "s_table")
+    n = s_table.shape[0]
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be [n_tokens, in_features] with W's in_features")
+    if s_table.dim() != 2 or s_table.shape[1] != K:
+        raise ValueError("s_table must be [n_cand, in_features]")
+    dev = W.device
+    s = torch.empty(max(K, 1), dtype=torch.float32, device=dev)
+    losses = torch.empty(max(n, 1), dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = _buf(awq_workspace_bytes(M, K, N, cfg, n, 0), dev)
+    st = lib().awq_search_scale_table(_ptr(W) if W.numel() else _ptr(workspace), _ptr(X),
+                                      _ptr(s_table) if s_table.numel() else _ptr(s), n, M, K, N,
+                                      ctypes.byref(cfg), _ptr(s), _ptr(losses), _ptr(best),
+                                      _ptr(status), _ptr(workspace), workspace.numel(),
+                                      _stream_ptr(stream))
+    _check(st, "awq_search_scale_table")
+    return {"s": s[:K], "losses": losses[:n], "best": best, "status": status}
+
+
+def awq_threshold_scales(a: torch.Tensor, percentile: float, factor: float,
+                         stream=None) -> torch.Tensor:
+    """s_i = factor where a_i exceeds the percentile threshold, else 1."""
+    _dev(a, torch.float32, "a")
+    K = a.shape[0]
+    s = torch.empty_like(a)
+    st = lib().awq_threshold_scales(_ptr(a), K, float(percentile), float(factor), _ptr(s),
+                                    _stream_ptr(stream))
+    _check(st, "awq_threshold_scales")
+    return s
+
+
+def awq_hadamard_rotate(A: torch.Tensor, block: int, out: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """Rows of A fp16 [R, K] times blockwise H_block / sqrt(block)."""
+    _dev(A, torch.float16, "A")
+    R, K = A.shape
+    out = torch.empty_like(A) if out is None else _dev(out, torch.float16, "out", (R, K))
+    if A.numel() == 0:
+        return out
+    st = lib().awq_hadamard_rotate(_ptr(A), R, K, int(block), _ptr(out), _stream_ptr(stream))
+    _check(st, "awq_hadamard_rotate")
+    return out

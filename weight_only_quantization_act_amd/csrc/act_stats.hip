@@ -1,7 +1,9 @@
 // Per-input-channel mean activation magnitude a_i = (1/N) sum_t |X[t][i]|.
 //
 // Pages: "AWQ" scholia-log notes §1.2 (a_i = E|x_i| from calibration activations);
-// "AWQ量化" tutorial, 激活感知 (importance = average absolute activation over N samples).
+// "AWQ量化" tutorial, 激活感知 (importance = average absolute activation over N samples);
+// ewbang.com GPTQ与AWQ §3 二.2 (max |A|); kwkr.cn AWQ 技术解析 §1.2 (E|a| / sqrt(E a^2)) and
+// §2.1 (EMA of batch means with momentum 0.9, running max).
 //
 // X is fp16 [N tokens][K channels], K contiguous, so a wave reading 64 consecutive
 // 16-byte chunks of one token row streams 1 KiB of contiguous HBM.  Pass 1: a block owns
@@ -9,6 +11,12 @@
 // each lane accumulates |x| for its 8 channels in fp64.  The 4 waves' sums are combined in
 // a fixed order through LDS and written as one fp64 partial per (slice, channel).
 // Pass 2 adds the slices in order, divides by N in fp64 and rounds to fp32.
+//
+// The same two passes compute the other statistics the pages name: max |x| (a running
+// max instead of a sum), E|x| / sqrt(E x^2) (a second fp64 sum of squares), and an
+// exponential moving average of per-batch mean |x| over consecutive token batches (the
+// splits are then whole batches cut into pieces, and pass 2 runs the recurrence over the
+// batches in order).
 //
 // fp16 values are integer multiples of 2^-24, so fp64 sums of them are exact while every
 // partial sum stays below 2^29; in that range the result does not depend on the order
@@ -31,31 +39,61 @@ constexpr int kMaxSplits = 128;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <bool VEC>
+// max that keeps a NaN once one is seen (a plain fmax would drop it), so a NaN activation
+// propagates into the statistic as it does for the sums.
+__device__ __forceinline__ double nan_max(double m, double v) {
+  return (v > m || v != v) ? v : m;
+}
+
+// Quantities a statistic needs per (split, channel): q0 = sum |x| (or max |x| for the max
+// statistic) and, for the RMS ratio, q1 = sum x^2.
+template <int MODE>
+struct StatQ {
+  static constexpr int NQ = (MODE == kStatRmsRatio) ? 2 : 1;
+};
+
+// Split s covers tokens [b*B + j*tpb, min(+tpb, (b+1)*B, N)) with b = s / sub, j = s % sub:
+// whole batches of B tokens, each cut into `sub` pieces (B = N, one batch, except for the
+// EMA statistic).
+template <bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void k_act_stats_partial(const uint16_t* __restrict__ X,
-                                                                int N, int K,
-                                                                int tokens_per_split,
-                                                                double* __restrict__ part) {
-  __shared__ double red[kTokenLanes][kChunkLanes][8];
+                                                                int N, int K, int B, int sub,
+                                                                int tpb,
+                                                                double* __restrict__ part,
+                                                                int splits) {
+  constexpr int NQ = StatQ<MODE>::NQ;
+  __shared__ double red[NQ][kTokenLanes][kChunkLanes][8];
   const int lc = threadIdx.x % kChunkLanes;
   const int lt = threadIdx.x / kChunkLanes;
   const int col0 = (blockIdx.x * kChunkLanes + lc) * 8;
   const int split = blockIdx.y;
-  const int t0 = split * tokens_per_split;
-  const int t1 = min(N, t0 + tokens_per_split);
+  const int b = split / sub, j = split - (split / sub) * sub;
+  const long long t0l = (long long)b * B + (long long)j * tpb;
+  const int t0 = (int)min(t0l, (long long)N);
+  const int t1 = (int)min(min(t0l + tpb, (long long)(b + 1) * B), (long long)N);
 
-  double acc[8];
+  double q0[8], q1[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+  for (int i = 0; i < 8; ++i) q0[i] = q1[i] = 0.0;
+
+  auto add = [&](int i, float xf) {
+    const double x = (double)xf;
+    if constexpr (MODE == kStatMaxAbs) {
+      q0[i] = nan_max(q0[i], fabs(x));
+    } else {
+      q0[i] += fabs(x);
+      if constexpr (MODE == kStatRmsRatio) q1[i] += x * x;
+    }
+  };
 
   if (VEC) {
     if (col0 < K) {
       for (int t = t0 + lt; t < t1; t += kTokenLanes) {
         const u32x4 raw = *(const u32x4*)(X + (size_t)t * K + col0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[2 * j] += fabs((double)h2f((uint16_t)(raw[j] & 0xffffu)));
-          acc[2 * j + 1] += fabs((double)h2f((uint16_t)(raw[j] >> 16)));
+        for (int jj = 0; jj < 4; ++jj) {
+          add(2 * jj, h2f((uint16_t)(raw[jj] & 0xffffu)));
+          add(2 * jj + 1, h2f((uint16_t)(raw[jj] >> 16)));
         }
       }
     }
@@ -63,79 +101,169 @@ __global__ __launch_bounds__(kThreads) void k_act_stats_partial(const uint16_t* 
     for (int t = t0 + lt; t < t1; t += kTokenLanes) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (col0 + i < K) acc[i] += fabs((double)h2f(X[(size_t)t * K + col0 + i]));
+        if (col0 + i < K) add(i, h2f(X[(size_t)t * K + col0 + i]));
     }
   }
 
 #pragma unroll
-  for (int i = 0; i < 8; ++i) red[lt][lc][i] = acc[i];
+  for (int i = 0; i < 8; ++i) {
+    red[0][lt][lc][i] = q0[i];
+    if constexpr (NQ > 1) red[NQ - 1][lt][lc][i] = q1[i];
+  }
   __syncthreads();
   if (lt == 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      double s = red[0][lc][i];
+    for (int q = 0; q < NQ; ++q)
 #pragma unroll
-      for (int u = 1; u < kTokenLanes; ++u) s += red[u][lc][i];
-      if (col0 + i < K) part[(size_t)split * K + col0 + i] = s;
-    }
+      for (int i = 0; i < 8; ++i) {
+        double v = red[q][0][lc][i];
+#pragma unroll
+        for (int u = 1; u < kTokenLanes; ++u)
+          v = (MODE == kStatMaxAbs) ? nan_max(v, red[q][u][lc][i]) : v + red[q][u][lc][i];
+        if (col0 + i < K) part[((size_t)q * splits + split) * K + col0 + i] = v;
+      }
   }
 }
 
-// Pass 2: a block owns 64 channels; its 4 waves take interleaved slices of the splits
-// (wave u sums splits u, u+4, u+8, ... in order) and the 4 sums are added in a fixed
-// order.  Reads are 64 consecutive doubles per wave instruction.
+// Pass 2 (mean, max, RMS ratio): a block owns 64 channels; its 4 waves take interleaved
+// slices of the splits (wave u: splits u, u+4, ... in order) and the 4 partial results are
+// combined in a fixed order.
+template <int MODE>
 __global__ __launch_bounds__(kThreads) void k_act_stats_finalize(const double* __restrict__ part,
                                                                  int splits, int N, int K,
                                                                  float* __restrict__ a) {
-  __shared__ double red[kTokenLanes][kChunkLanes];
+  constexpr int NQ = StatQ<MODE>::NQ;
+  __shared__ double red[NQ][kTokenLanes][kChunkLanes];
   const int lc = threadIdx.x % kChunkLanes;
   const int lt = threadIdx.x / kChunkLanes;
   const int i = blockIdx.x * kChunkLanes + lc;
-  double s = 0.0;
+  double s0 = 0.0, s1 = 0.0;
   if (i < K) {
 #pragma unroll 4
-    for (int p = lt; p < splits; p += kTokenLanes) s += part[(size_t)p * K + i];
+    for (int p = lt; p < splits; p += kTokenLanes) {
+      const double v = part[(size_t)p * K + i];
+      s0 = (MODE == kStatMaxAbs) ? nan_max(s0, v) : s0 + v;
+      if constexpr (NQ > 1) s1 += part[((size_t)splits + p) * K + i];
+    }
   }
-  red[lt][lc] = s;
+  red[0][lt][lc] = s0;
+  if constexpr (NQ > 1) red[NQ - 1][lt][lc] = s1;
   __syncthreads();
   if (lt == 0 && i < K) {
-    double t = red[0][lc];
+    double t0 = red[0][0][lc], t1 = (NQ > 1) ? red[NQ - 1][0][lc] : 0.0;
 #pragma unroll
-    for (int u = 1; u < kTokenLanes; ++u) t += red[u][lc];
-    a[i] = (float)(t / (double)N);
+    for (int u = 1; u < kTokenLanes; ++u) {
+      t0 = (MODE == kStatMaxAbs) ? nan_max(t0, red[0][u][lc]) : t0 + red[0][u][lc];
+      if constexpr (NQ > 1) t1 += red[NQ - 1][u][lc];
+    }
+    double r;
+    if constexpr (MODE == kStatMeanAbs) {
+      r = t0 / (double)N;
+    } else if constexpr (MODE == kStatMaxAbs) {
+      r = t0;
+    } else {  // RMS ratio: mean |x| / sqrt(mean x^2); 0 for an all-zero channel
+      const double m1 = t0 / (double)N, m2 = t1 / (double)N;
+      r = (m2 > 0.0) ? m1 / sqrt(m2) : 0.0;
+    }
+    a[i] = (float)r;
   }
+}
+
+// Pass 2 (EMA): per channel, batch sums (pieces added in order) -> batch mean ->
+// e = momentum * e + (1 - momentum) * mean, from e = 0, over the batches in order.
+__global__ __launch_bounds__(kThreads) void k_act_stats_ema(const double* __restrict__ part,
+                                                            int n_batches, int sub, int N, int B,
+                                                            int K, double momentum,
+                                                            float* __restrict__ a) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= K) return;
+  const double keep = 1.0 - momentum;
+  double e = 0.0;
+  for (int b = 0; b < n_batches; ++b) {
+    double sum = 0.0;
+    for (int j = 0; j < sub; ++j) sum += part[(size_t)(b * sub + j) * K + i];
+    const int cnt = (int)min((long long)B, (long long)N - (long long)b * B);
+    const double m = sum / (double)cnt;
+    e = momentum * e + keep * m;
+  }
+  a[i] = (float)e;
 }
 
 }  // namespace
 
-int stats_splits(int64_t N, int64_t K) {
-  if (N <= 0 || K <= 0) return 1;
+StatsPlan stats_plan(int64_t N, int64_t K, int mode, int64_t batch_tokens) {
+  StatsPlan p{};
+  p.nq = (mode == kStatRmsRatio) ? 2 : 1;
+  if (N <= 0 || K <= 0) {
+    p.B = (int)(N > 0 ? N : 1); p.n_batches = 1; p.sub = 1; p.tpb = p.B; p.splits = 1;
+    return p;
+  }
   const int64_t col_blocks = (K + kChunkLanes * 8 - 1) / (kChunkLanes * 8);
-  int64_t by_blocks = (kTargetBlocks + col_blocks - 1) / col_blocks;
-  int64_t by_tokens = (N + kMinTokensPerSplit - 1) / kMinTokensPerSplit;
-  int64_t s = by_blocks < by_tokens ? by_blocks : by_tokens;
-  if (s > kMaxSplits) s = kMaxSplits;
-  if (s < 1) s = 1;
-  return (int)s;
+  const int64_t target = (kTargetBlocks + col_blocks - 1) / col_blocks;
+  if (mode == kStatEmaMean) {
+    const int64_t B = batch_tokens < N ? batch_tokens : N;  // one batch if it covers all
+    p.B = (int)B;
+    p.n_batches = (int)((N + B - 1) / B);
+    int64_t sub = target / p.n_batches;
+    const int64_t by_tokens = (B + kMinTokensPerSplit - 1) / kMinTokensPerSplit;
+    if (sub > by_tokens) sub = by_tokens;
+    if (sub < 1) sub = 1;
+    p.sub = (int)sub;
+    p.tpb = (int)((B + sub - 1) / sub);
+    p.splits = p.n_batches * p.sub;
+  } else {
+    int64_t by_tokens = (N + kMinTokensPerSplit - 1) / kMinTokensPerSplit;
+    int64_t s = target < by_tokens ? target : by_tokens;
+    if (s > kMaxSplits) s = kMaxSplits;
+    if (s < 1) s = 1;
+    p.B = (int)N;
+    p.n_batches = 1;
+    p.sub = (int)s;
+    p.tpb = (int)((N + s - 1) / s);
+    p.splits = (int)s;
+  }
+  return p;
 }
 
-hipError_t launch_act_stats(const uint16_t* X, int N, int K, float* a_out, double* partials,
-                            int splits, hipStream_t stream) {
-  if (K <= 0) return hipSuccess;
-  const int tps = (N + splits - 1) / splits;
+template <int MODE>
+static hipError_t launch_stats_mode(const uint16_t* X, int N, int K, const StatsPlan& p,
+                                    double momentum, float* a_out, double* partials,
+                                    hipStream_t stream) {
   const int col_blocks = (K + kChunkLanes * 8 - 1) / (kChunkLanes * 8);
-  dim3 grid(col_blocks, splits);
+  dim3 grid(col_blocks, p.splits);
   if (K % 8 == 0)
-    hipLaunchKernelGGL(k_act_stats_partial<true>, grid, dim3(kThreads), 0, stream, X, N, K, tps,
-                       partials);
+    hipLaunchKernelGGL((k_act_stats_partial<true, MODE>), grid, dim3(kThreads), 0, stream, X, N, K,
+                       p.B, p.sub, p.tpb, partials, p.splits);
   else
-    hipLaunchKernelGGL(k_act_stats_partial<false>, grid, dim3(kThreads), 0, stream, X, N, K,
-                       tps, partials);
+    hipLaunchKernelGGL((k_act_stats_partial<false, MODE>), grid, dim3(kThreads), 0, stream, X, N,
+                       K, p.B, p.sub, p.tpb, partials, p.splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_act_stats_finalize, dim3((K + kChunkLanes - 1) / kChunkLanes),
-                     dim3(kThreads), 0, stream, partials, splits, N, K, a_out);
+  if constexpr (MODE == kStatEmaMean) {
+    hipLaunchKernelGGL(k_act_stats_ema, dim3((K + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                       stream, partials, p.n_batches, p.sub, N, p.B, K, momentum, a_out);
+  } else {
+    hipLaunchKernelGGL(k_act_stats_finalize<MODE>, dim3((K + kChunkLanes - 1) / kChunkLanes),
+                       dim3(kThreads), 0, stream, partials, p.splits, N, K, a_out);
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_act_stats(const uint16_t* X, int N, int K, int mode, const StatsPlan& plan,
+                            double momentum, float* a_out, double* partials, hipStream_t stream) {
+  if (K <= 0) return hipSuccess;
+  switch (mode) {
+    case kStatMeanAbs:
+      return launch_stats_mode<kStatMeanAbs>(X, N, K, plan, momentum, a_out, partials, stream);
+    case kStatMaxAbs:
+      return launch_stats_mode<kStatMaxAbs>(X, N, K, plan, momentum, a_out, partials, stream);
+    case kStatRmsRatio:
+      return launch_stats_mode<kStatRmsRatio>(X, N, K, plan, momentum, a_out, partials, stream);
+    case kStatEmaMean:
+      return launch_stats_mode<kStatEmaMean>(X, N, K, plan, momentum, a_out, partials, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace awq

@@ -84,6 +84,48 @@ inline int record(void* ev, hipStream_t st) {
   return hip_status(hipEventRecord((hipEvent_t)ev, st));
 }
 
+// The search over nc candidate scale vectors s_table [nc][K] (device): fake quantisation,
+// loss product and selection, in batches of as many candidates as the workspace holds.
+// Arguments are already validated.  The workspace layout is the one awq_workspace_bytes
+// describes (its s-table slot is unused when the caller supplies the table).
+int run_search(const void* W, const void* X, const float* s_table, int64_t M, int64_t K,
+               int64_t N, const awq_qconfig* cfg, int nc, float* s_out, double* losses_out,
+               int32_t* best_out, int32_t* status_out, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  ProfileHook hook = g_hook;
+  g_hook = ProfileHook();
+  hipStream_t sm = (hipStream_t)stream;
+  SearchLayout L = search_layout(M, K, N, nc);
+  char* ws = (char*)workspace;
+  double* partials = (double*)(ws + L.p_off);
+  uint16_t* dW = (uint16_t*)(ws + L.dw_off);
+  int batch = nc;
+  if (L.dw_bytes_per_alpha > 0) {
+    const size_t fit = (workspace_bytes - L.dw_off) / L.dw_bytes_per_alpha;
+    if (fit < (size_t)batch) batch = (int)fit;
+  }
+  int st;
+  if (L.tiles > 0) {
+    for (int k0 = 0; k0 < nc; k0 += batch) {
+      const int nb = nc - k0 < batch ? nc - k0 : batch;
+      const bool first = (k0 == 0);
+      if (first && (st = record(hook.fq_start, sm))) return st;
+      st = hip_status(awq::launch_fake_quant_delta((const uint16_t*)W, s_table + (size_t)k0 * K,
+                                                   (int)M, (int)K, nb, cfg->w_bit,
+                                                   cfg->group_size, cfg->zero_point, dW, sm));
+      if (st) return st;
+      if (first && (st = record(hook.fq_stop, sm))) return st;
+      if (first && (st = record(hook.gemm_start, sm))) return st;
+      st = hip_status(awq::launch_loss_gemm(dW, (const uint16_t*)X, (int)M, (int)N, (int)K, nb,
+                                            partials + (size_t)k0 * L.tiles, sm));
+      if (st) return st;
+    }
+    if ((st = record(hook.gemm_stop, sm))) return st;
+  }
+  return hip_status(awq::launch_reduce_select(partials, nc, (int)L.tiles, s_table, (int)K,
+                                              losses_out, best_out, status_out, s_out, sm));
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,27 +146,49 @@ const char* awq_status_str(int status) {
   }
 }
 
-size_t awq_act_stats_workspace_bytes(int64_t n_tokens, int64_t in_features) {
+size_t awq_act_stats_ex_workspace_bytes(int64_t n_tokens, int64_t in_features,
+                                        int32_t statistic, int64_t batch_tokens) {
   if (token_shape(n_tokens, in_features) != AWQ_OK) return 0;
-  const int splits = awq::stats_splits(n_tokens, in_features);
-  return round_up((size_t)splits * (size_t)in_features * sizeof(double), kAlign) + kAlign;
+  if (statistic < AWQ_STAT_MEAN_ABS || statistic > AWQ_STAT_EMA_MEAN) return 0;
+  if (statistic == AWQ_STAT_EMA_MEAN && batch_tokens < 1) return 0;
+  const awq::StatsPlan p = awq::stats_plan(n_tokens, in_features, statistic, batch_tokens);
+  return round_up((size_t)p.nq * (size_t)p.splits * (size_t)in_features * sizeof(double),
+                  kAlign) + kAlign;
 }
 
-int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* a_out,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+size_t awq_act_stats_workspace_bytes(int64_t n_tokens, int64_t in_features) {
+  return awq_act_stats_ex_workspace_bytes(n_tokens, in_features, AWQ_STAT_MEAN_ABS, 0);
+}
+
+int awq_act_stats_ex(const void* X, int64_t n_tokens, int64_t in_features, int32_t statistic,
+                     int64_t batch_tokens, double momentum, float* a_out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   if (!X || !a_out) return AWQ_E_NULL;
   if (!workspace) return AWQ_E_WORKSPACE;
   int st = token_shape(n_tokens, in_features);
   if (st != AWQ_OK) return st;
-  if (workspace_bytes < awq_act_stats_workspace_bytes(n_tokens, in_features)) return AWQ_E_WORKSPACE;
+  if (statistic < AWQ_STAT_MEAN_ABS || statistic > AWQ_STAT_EMA_MEAN) return AWQ_E_CONFIG;
+  if (statistic == AWQ_STAT_EMA_MEAN) {
+    if (batch_tokens < 1 || batch_tokens >= kMaxElems) return AWQ_E_SHAPE;
+    if (!(momentum >= 0.0 && momentum < 1.0)) return AWQ_E_CONFIG;
+  }
+  if (workspace_bytes <
+      awq_act_stats_ex_workspace_bytes(n_tokens, in_features, statistic, batch_tokens))
+    return AWQ_E_WORKSPACE;
   if (!aligned(X, in_features % 8 == 0 ? 16 : 2) || !aligned(a_out, 4) || !aligned(workspace, 8))
     return AWQ_E_ALIGN;
   if (in_features == 0) return AWQ_OK;
   if ((st = device_ptr(X)) || (st = device_ptr(a_out)) || (st = device_ptr(workspace))) return st;
-  const int splits = awq::stats_splits(n_tokens, in_features);
+  const awq::StatsPlan p = awq::stats_plan(n_tokens, in_features, statistic, batch_tokens);
   return hip_status(awq::launch_act_stats((const uint16_t*)X, (int)n_tokens, (int)in_features,
-                                          a_out, (double*)workspace, splits,
+                                          statistic, p, momentum, a_out, (double*)workspace,
                                           (hipStream_t)stream));
+}
+
+int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* a_out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  return awq_act_stats_ex(X, n_tokens, in_features, AWQ_STAT_MEAN_ABS, 0, 0.0, a_out, workspace,
+                          workspace_bytes, stream);
 }
 
 size_t awq_workspace_bytes(int64_t out_features, int64_t in_features, int64_t n_tokens,
@@ -171,40 +235,67 @@ int awq_search_scales(const void* W, const void* X, const float* a, int64_t out_
     return st;
   if (status_out && (st = device_ptr(status_out))) return st;
 
-  ProfileHook hook = g_hook;
-  g_hook = ProfileHook();
-  hipStream_t sm = (hipStream_t)stream;
-  SearchLayout L = search_layout(M, K, N, n_alpha);
-  char* ws = (char*)workspace;
-  float* s_table = (float*)(ws + L.s_off);
-  double* partials = (double*)(ws + L.p_off);
-  uint16_t* dW = (uint16_t*)(ws + L.dw_off);
-  int batch = n_alpha;
-  if (L.dw_bytes_per_alpha > 0) {
-    const size_t fit = (workspace_bytes - L.dw_off) / L.dw_bytes_per_alpha;
-    if (fit < (size_t)batch) batch = (int)fit;
-  }
+  if ((st = hip_status(awq::launch_make_scales(a, (int)K, al, n_alpha,
+                                               (float*)workspace, (hipStream_t)stream))))
+    return st;
+  return run_search(W, X, (const float*)workspace, M, K, N, cfg, n_alpha, s_out, losses_out,
+                    best_out, status_out, workspace, workspace_bytes, stream);
+}
 
-  if ((st = hip_status(awq::launch_make_scales(a, (int)K, al, n_alpha, s_table, sm)))) return st;
-  if (L.tiles > 0) {
-    for (int k0 = 0; k0 < n_alpha; k0 += batch) {
-      const int nb = n_alpha - k0 < batch ? n_alpha - k0 : batch;
-      const bool first = (k0 == 0);
-      if (first && (st = record(hook.fq_start, sm))) return st;
-      st = hip_status(awq::launch_fake_quant_delta((const uint16_t*)W, s_table + (size_t)k0 * K,
-                                                   (int)M, (int)K, nb, cfg->w_bit,
-                                                   cfg->group_size, cfg->zero_point, dW, sm));
-      if (st) return st;
-      if (first && (st = record(hook.fq_stop, sm))) return st;
-      if (first && (st = record(hook.gemm_start, sm))) return st;
-      st = hip_status(awq::launch_loss_gemm(dW, (const uint16_t*)X, (int)M, (int)N, (int)K, nb,
-                                            partials + (size_t)k0 * L.tiles, sm));
-      if (st) return st;
-    }
-    if ((st = record(hook.gemm_stop, sm))) return st;
-  }
-  return hip_status(awq::launch_reduce_select(partials, n_alpha, (int)L.tiles, s_table, (int)K,
-                                              losses_out, best_out, status_out, s_out, sm));
+int awq_search_scale_table(const void* W, const void* X, const float* s_table, int32_t n_cand,
+                           int64_t out_features, int64_t in_features, int64_t n_tokens,
+                           const awq_qconfig* cfg, float* s_out, double* losses_out,
+                           int32_t* best_out, int32_t* status_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const int64_t M = out_features, K = in_features, N = n_tokens;
+  if (!W || !X || !s_table || !cfg || !s_out || !losses_out || !best_out) return AWQ_E_NULL;
+  if (!workspace) return AWQ_E_WORKSPACE;
+  if (!cfg_valid(cfg)) return AWQ_E_CONFIG;
+  int st = weight_shape(M, K, cfg);
+  if (st != AWQ_OK) return st;
+  if ((st = token_shape(N, K)) != AWQ_OK) return st;
+  if (n_cand < 1 || n_cand > AWQ_MAX_ALPHA) return AWQ_E_ALPHA;
+  if (K > 0 && (int64_t)n_cand * K >= kMaxElems) return AWQ_E_SHAPE;
+  if (workspace_bytes < awq_workspace_bytes(M, K, N, cfg, n_cand, 1)) return AWQ_E_WORKSPACE;
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(s_table, 16) || !aligned(s_out, 4) ||
+      !aligned(losses_out, 8) || !aligned(best_out, 4) || !aligned(status_out, 4) ||
+      !aligned(workspace, kAlign))
+    return AWQ_E_ALIGN;
+  if ((st = device_ptr(W)) || (st = device_ptr(X)) || (st = device_ptr(s_table)) ||
+      (st = device_ptr(s_out)) || (st = device_ptr(losses_out)) || (st = device_ptr(best_out)) ||
+      (st = device_ptr(workspace)))
+    return st;
+  if (status_out && (st = device_ptr(status_out))) return st;
+  return run_search(W, X, s_table, M, K, N, cfg, n_cand, s_out, losses_out, best_out, status_out,
+                    workspace, workspace_bytes, stream);
+}
+
+int awq_threshold_scales(const float* a, int64_t in_features, double percentile, float factor,
+                         float* s_out, void* stream) {
+  if (!a || !s_out) return AWQ_E_NULL;
+  if (in_features < 1 || in_features > awq::kMaxThresholdK) return AWQ_E_SHAPE;
+  if (!(percentile >= 0.0 && percentile <= 100.0)) return AWQ_E_CONFIG;
+  if (!(factor > 0.0f) || !isfinite(factor)) return AWQ_E_CONFIG;
+  if (!aligned(a, 4) || !aligned(s_out, 4)) return AWQ_E_ALIGN;
+  int st;
+  if ((st = device_ptr(a)) || (st = device_ptr(s_out))) return st;
+  return hip_status(awq::launch_threshold_scales(a, (int)in_features, percentile, factor, s_out,
+                                                 (hipStream_t)stream));
+}
+
+int awq_hadamard_rotate(const void* A, int64_t rows, int64_t in_features, int32_t block,
+                        void* out, void* stream) {
+  if (!A || !out) return AWQ_E_NULL;
+  if (block < 2 || block > 512 || (block & (block - 1))) return AWQ_E_CONFIG;
+  if (rows < 0 || in_features < 0 || in_features % block || in_features % 8) return AWQ_E_SHAPE;
+  if (rows >= kMaxElems || (in_features > 0 && rows >= kMaxElems / in_features))
+    return AWQ_E_SHAPE;
+  if (!aligned(A, 16) || !aligned(out, 16)) return AWQ_E_ALIGN;
+  if (rows == 0 || in_features == 0) return AWQ_OK;
+  int st;
+  if ((st = device_ptr(A)) || (st = device_ptr(out))) return st;
+  return hip_status(awq::launch_hadamard((const uint16_t*)A, (int)rows, (int)in_features, block,
+                                         (uint16_t*)out, (hipStream_t)stream));
 }
 
 int awq_fake_quant_delta(const void* W, const float* s, int64_t out_features,

@@ -16,10 +16,18 @@ inline int64_t loss_tiles_m(int64_t M) { return (M + kLossBM - 1) / kLossBM; }
 inline int64_t loss_tiles_n(int64_t N) { return (N + kLossBN - 1) / kLossBN; }
 
 // ---- statistics ----------------------------------------------------------------------
-// Number of token splits the two-pass statistics reduction uses for an N x K input.
-int stats_splits(int64_t N, int64_t K);
-hipError_t launch_act_stats(const uint16_t* X, int N, int K, float* a_out, double* partials,
-                            int splits, hipStream_t stream);
+constexpr int kStatMeanAbs = 0;   // mean |x|
+constexpr int kStatMaxAbs = 1;    // max |x|
+constexpr int kStatRmsRatio = 2;  // mean |x| / sqrt(mean x^2)
+constexpr int kStatEmaMean = 3;   // EMA of per-batch mean |x|
+// Token splits of the two-pass reduction: batches of B tokens (B = N except for the
+// EMA statistic), each cut into `sub` pieces of tpb tokens; nq fp64 partials per split.
+struct StatsPlan {
+  int B, n_batches, sub, tpb, splits, nq;
+};
+StatsPlan stats_plan(int64_t N, int64_t K, int mode, int64_t batch_tokens);
+hipError_t launch_act_stats(const uint16_t* X, int N, int K, int mode, const StatsPlan& plan,
+                            double momentum, float* a_out, double* partials, hipStream_t stream);
 
 // ---- scales, fake quantisation, packing ------------------------------------------------
 constexpr int kMaxAlpha = 64;
@@ -32,6 +40,13 @@ hipError_t launch_make_scales(const float* a, int K, const AlphaList& alphas, in
 hipError_t launch_fake_quant_delta(const uint16_t* W, const float* s_table, int M, int K,
                                    int nb, int w_bit, int group_size, int zero_point,
                                    uint16_t* dW, hipStream_t stream);
+// s_i = factor where a_i exceeds the linear-interpolation percentile of a, else 1.
+constexpr int kMaxThresholdK = 32768;
+hipError_t launch_threshold_scales(const float* a, int K, double percentile, float factor,
+                                   float* s_out, hipStream_t stream);
+// Rotate each row of A [rows][K] by blockwise normalised Hadamard matrices along K.
+hipError_t launch_hadamard(const uint16_t* A, int rows, int K, int block, uint16_t* out,
+                           hipStream_t stream);
 hipError_t launch_quant_pack(const uint16_t* W, const float* s, int M, int K, int w_bit,
                              int group_size, int zero_point, uint8_t* codes,
                              uint16_t* scales, uint16_t* zeros, hipStream_t stream);
