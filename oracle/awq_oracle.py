@@ -32,6 +32,7 @@ Readings taken where the pages leave a step open (each repeated at its function)
   loss          sum of squares of the output error, via Delta Y = Delta W X
   argmin        over finite losses, first index on ties; none finite -> index -1, s := 1
   packing       two 4-bit slots per byte, even input channel in the low nibble
+  W4A16 product y = x~ W_dequant^T with x~ = fl16(fl32(x / s)) when s is given, fp64
 """
 from __future__ import annotations
 
@@ -288,6 +289,42 @@ def run_layer(W16, X16, alphas32, cfg: QConfig):
     packed, scales, zeros = quantize_pack(W16, res["s_star"], cfg)
     res.update({"a": a32, "packed": packed, "scales": scales, "zeros": zeros})
     return res
+
+
+# --------------------------------------------------------------------------------------
+# Consumer of the packed format: the W4A16 product at inference
+# --------------------------------------------------------------------------------------
+def fold_inverse_scales(X16: np.ndarray, s32: np.ndarray) -> np.ndarray:
+    """x~ = x / s: the S^-1 that the pages fold into the preceding operation
+    [AWQ-notes §4.3].  Reading: one fp32 division per element, then rounded to fp16, the
+    dtype the preceding operation would emit."""
+    X32 = np.asarray(X16).astype(F32)
+    return (X32 / np.asarray(s32, dtype=F32)[None, :]).astype(np.float16)
+
+
+def dequantize_packed(packed: np.ndarray, scales16: np.ndarray, zeros16: np.ndarray,
+                      group_size: int) -> np.ndarray:
+    """W_dequant = (c - z) * step for every weight, from the packed codes and the stored
+    fp16 step and zero of its group [AWQ-blog §1.2 (W_dequant = W_int4 x scale_fp16);
+    GPTQ-AWQ §3 (weights stay 4-bit and are dequantised on the fly for fp16 compute)].
+    fp64, where it is exact ((c - z) is a small integer and the step an fp16)."""
+    codes = unpack_nibbles(packed).astype(F64)
+    M, K = codes.shape
+    step = np.asarray(scales16, dtype=np.float16).astype(F64)
+    zero = np.asarray(zeros16, dtype=np.float16).astype(F64)
+    cg = codes.reshape(M, K // group_size, group_size)
+    return ((cg - zero[:, :, None]) * step[:, :, None]).reshape(M, K)
+
+
+def w4a16_matmul(packed, scales16, zeros16, X16, group_size: int, s32=None) -> np.ndarray:
+    """y[t][m] = sum_i W_dequant[m][i] * x~[t][i] for fp16 activations X [T][K]: the
+    product the packed layer serves at inference, with x~ = X when S^-1 has already been
+    folded into the preceding operation and x~ = fold_inverse_scales(X, s) otherwise
+    [AutoAWQ-70B §四 (GEMM kernels for batches, GEMV for single requests);
+    AWQ-blog §4.2 (dequantisation fused into the product)].  fp64 [T][M]."""
+    Xt = np.asarray(X16) if s32 is None else fold_inverse_scales(X16, s32)
+    Wd = dequantize_packed(packed, scales16, zeros16, group_size)
+    return Xt.astype(F64) @ Wd.T
 
 
 # --------------------------------------------------------------------------------------

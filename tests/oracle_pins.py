@@ -590,4 +590,58 @@ def pin_hadamard_orthogonal():
     assert np.allclose(np.abs(y), 16.0 / np.sqrt(128.0), rtol=1e-3)
 
 
+def pin_w4a16_bruteforce():
+    """The W4A16 product read byte by byte in plain Python loops (channel i of row m in
+    byte i // 2, low nibble for even i [AWQ-blog §4.2]; weight (c - z) * step of its
+    group [AWQ-blog §1.2]) equals the oracle's vectorised product, and a unit activation
+    returns one column of the dequantised weights."""
+    rng = np.random.default_rng(40)
+    M, K, T, g = 3, 64, 2, 32
+    packed = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    scales = (rng.uniform(0.001, 0.05, (M, K // g))).astype(np.float16)
+    zeros = rng.integers(0, 16, (M, K // g)).astype(np.float16)
+    X = rng.standard_normal((T, K)).astype(np.float16)
+    y = O.w4a16_matmul(packed, scales, zeros, X, g)
+    for t in range(T):
+        for m in range(M):
+            acc = 0.0
+            for i in range(K):
+                byte = int(packed[m, i // 2])
+                c = (byte >> 4) if (i % 2) else (byte & 15)
+                w = (c - float(zeros[m, i // g])) * float(scales[m, i // g])
+                acc += w * float(X[t, i])
+            assert math.isclose(acc, y[t, m], rel_tol=1e-12, abs_tol=1e-12), (t, m)
+    e = np.zeros((1, K), np.float16)
+    e[0, 37] = 1.0
+    col = O.w4a16_matmul(packed, scales, zeros, e, g)[0]
+    byte = packed[:, 18].astype(int)
+    want = ((byte >> 4) - zeros[:, 1].astype(F64)) * scales[:, 1].astype(F64)
+    assert np.array_equal(col, want)
+
+
+def pin_w4a16_reproduces_layer():
+    """Quantise-and-pack W S, fold S^-1 into the activations [AWQ-notes §4.3], and the
+    packed product gives back x W^T to within the quantiser's error: every weight is off by
+    at most half a step (pinned above) plus the fp16 rounding of the stored step, and every
+    folded activation by the fp16 rounding of x / s."""
+    rng = np.random.default_rng(41)
+    M, K, T = 24, 256, 5
+    W = (rng.standard_normal((M, K)) * 0.02).astype(np.float16)
+    X = rng.standard_normal((T, K)).astype(np.float16)
+    X[:, 9] *= 40
+    for cfg in (_cfg(4, 128, 1), _cfg(4, 64, 0), _cfg(3, 32, 1)):
+        s = O.scale_family(O.act_stats(X), np.array([0.5], F32))[0]
+        packed, scales, zeros = O.quantize_pack(W, s, cfg)
+        y = O.w4a16_matmul(packed, scales, zeros, X, cfg.group_size, s32=s)
+        exact = X.astype(F64) @ W.astype(F64).T
+        _, step32, _ = O.quantize(W, s, cfg)
+        half = np.repeat(step32.astype(F64), cfg.group_size, axis=1) * (0.5 + 16 * 2.0 ** -11)
+        xt = np.abs(X.astype(F64) / s.astype(F64)[None, :])
+        ws = np.abs(W.astype(F64) * s.astype(F64)[None, :])
+        bound = xt @ half.T * (1 + 2.0 ** -10) + xt @ ws.T * 2.0 ** -10
+        assert np.all(np.abs(y - exact) <= bound), float(np.max(np.abs(y - exact) / bound))
+        # and the bound is not vacuous: the error is a real fraction of it
+        assert np.max(np.abs(y - exact) / bound) > 0.05
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

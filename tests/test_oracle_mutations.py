@@ -258,6 +258,39 @@ def _hadamard_rotate_unnormalised(A16, block):
     return (A.reshape(R, K // block, block) @ O.hadamard_matrix(block)).reshape(R, K).astype(np.float16)
 
 
+def _dequant_packed_no_zero(packed, scales16, zeros16, group_size):
+    codes = O.unpack_nibbles(packed).astype(F64)
+    M, K = codes.shape
+    st = np.asarray(scales16, np.float16).astype(F64)
+    return (codes.reshape(M, K // group_size, group_size) * st[:, :, None]).reshape(M, K)
+
+
+def _dequant_packed_tiled(packed, scales16, zeros16, group_size):
+    codes = O.unpack_nibbles(packed).astype(F64)
+    st = np.tile(np.asarray(scales16, np.float16).astype(F64), (1, group_size))
+    z = np.tile(np.asarray(zeros16, np.float16).astype(F64), (1, group_size))
+    return (codes - z) * st
+
+
+def _unpack_swapped(packed):
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((packed.shape[0], 2 * packed.shape[1]), dtype=np.uint8)
+    out[:, 0::2] = packed >> 4
+    out[:, 1::2] = packed & 0x0F
+    return out
+
+
+def _fold_multiplies(X16, s32):
+    return (np.asarray(X16).astype(F32) * np.asarray(s32, F32)[None, :]).astype(np.float16)
+
+
+MUTANTS.update({
+    "w4a16_zero_not_subtracted": ("dequantize_packed", _dequant_packed_no_zero),
+    "w4a16_groups_tiled": ("dequantize_packed", _dequant_packed_tiled),
+    "unpack_nibbles_swapped": ("unpack_nibbles", _unpack_swapped),
+    "fold_multiplies_by_s": ("fold_inverse_scales", _fold_multiplies),
+})
+
 MUTANTS.update({
     "max_signed": ("act_stat_max_abs", _max_signed),
     "rms_ratio_without_sqrt": ("act_stat_rms_ratio", _rms_no_sqrt),
