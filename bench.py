@@ -240,6 +240,7 @@ def main():
     }
     if not args.no_variants:
         line["variants"] = time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N)
+        line["w4a16"] = time_w4a16(awq, torch, out, res["s"], Xd, cfg, sptr, M, K)
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib * (1 << 20) // 2, dtype=torch.float16, device="cuda")
         dst = torch.empty_like(src)
@@ -286,6 +287,56 @@ def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, reps=20):
                      device="cuda")
     ms = timed(lambda: awq.awq_search_scale_table(Wd, Xd, table, cfg, workspace=ws))
     out["search_scale_table_20_threshold_rows"] = {"ms": ms}
+    return out
+
+
+def w4a16_bytes(M, K, g, T, with_s):
+    """HBM bytes one W4A16 product must move: codes, fp16 step and zero per group, the
+    activations, s if given, and the fp16 output."""
+    return M * K / 2 + 4.0 * M * K / g + 2.0 * T * K + (4.0 * K if with_s else 0.0) + 2.0 * T * M
+
+
+def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, reps=50):
+    """The packed layer's W4A16 product at decode batches 1 and 4: on the layer just packed,
+    and on a 28672 x 8192 packed layer (the 70B-class MLP shape) of seeded random codes."""
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(sptr)
+        for _ in range(reps):
+            fn()
+        e1.record(sptr)
+        torch.cuda.synchronize()
+        return e0.elapsed_ms(e1) / reps
+
+    out = {}
+    codes, scales, zeros = packed
+    g = cfg.group_size
+    for T in (1, 4):
+        x = Xd[:T].contiguous()
+        ms = timed(lambda: awq.awq_w4a16_matmul(x, codes, scales, zeros, cfg, s=s))
+        b = w4a16_bytes(M, K, g, T, True)
+        out[f"{M}x{K}_T{T}"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+    M2, K2 = 28672, 8192
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20250)
+    c2 = torch.randint(0, 256, (M2, K2 // 2), dtype=torch.uint8, device="cuda", generator=gen)
+    sc2 = (torch.rand((M2, K2 // g), device="cuda", generator=gen) * 0.02 + 0.0005).half()
+    z2 = torch.randint(0, 16, (M2, K2 // g), device="cuda", generator=gen).half()
+    s2 = torch.rand((K2,), device="cuda", generator=gen) * 3 + 0.5
+    x2 = torch.randn((4, K2), device="cuda", generator=gen).half()
+    for T in (1, 4):
+        x = x2[:T].contiguous()
+        ms = timed(lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg, s=s2))
+        b = w4a16_bytes(M2, K2, g, T, True)
+        out[f"{M2}x{K2}_T{T}"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+        # S^-1 already folded into the activations (the deployed form): no division
+        ms = timed(lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg))
+        b = w4a16_bytes(M2, K2, g, T, False)
+        out[f"{M2}x{K2}_T{T}_folded"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9,
+                                          "bytes": b}
     return out
 
 

@@ -171,6 +171,26 @@ int awq_hadamard_rotate(const void* A, int64_t rows, int64_t in_features, int32_
                         void* out, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * W4A16 product of a packed layer (the consumer of awq_quantize_pack's output)
+ *   y[t][m] = sum_i (c[m][i] - z[m][g]) * step[m][g] * xt[t][i],   g = i / group_size,
+ *   xt = x when s is NULL (S^-1 already folded into the preceding operation
+ *   [AWQ-notes §4.3]), otherwise xt = fp16(fp32(x / s)) per element
+ *   [AWQ-blog §1.2 (dequantised weight = int4 code x fp16 scale), §4.2 (dequantisation
+ *   fused into the product); AutoAWQ-70B §四 (GEMV kernel for single requests)].
+ *   x        fp16 [n_tokens][in], device, 16-byte aligned
+ *   s        fp32 [in], device, 16-byte aligned, or NULL
+ *   codes    u8 [out][in/2], scales and zeros fp16 [out][in/group_size], as written by
+ *            awq_quantize_pack (zeros must hold integers in [0, 15]); codes 16-byte aligned
+ *   cfg      only group_size is read (codes occupy 4-bit slots for every w_bit)
+ *   y        fp16 [n_tokens][out], device (written)
+ * fp32 accumulation in a fixed order (bitwise repeatable), rounded to fp16 once.
+ * in_features <= 32768; n_tokens >= 0 (0 enqueues nothing); in_features = 0 gives y = 0.
+ * ---------------------------------------------------------------------------------- */
+int awq_w4a16_matmul(const void* x, const float* s, int64_t n_tokens, const void* codes,
+                     const void* scales, const void* zeros, int64_t out_features,
+                     int64_t in_features, const awq_qconfig* cfg, void* y, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * A3 alone: dW = W - Q(W diag(s)) diag(s)^-1 rounded to fp16, the operand the search's
  * loss product consumes [AWQ-tut 缩放保护 (W_hat = Q(s W)/s)].
  *   W fp16 [out][in], s fp32 [in], dW_out fp16 [out][in]; all device.

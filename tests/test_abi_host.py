@@ -36,7 +36,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in awq_act.h but not exported"
     assert set(names) == set(_lib._SIGNATURES)
@@ -198,3 +198,21 @@ def test_table_threshold_hadamard_validation(L):
     assert h(P, 1 << 20, 1 << 12, 64, P, None) == E["SHAPE"]
     assert h(P_ODD, 4, 128, 64, P, None) == E["ALIGN"]
     assert h(P, 0, 128, 64, P, None) == E["OK"]            # empty: nothing to do
+
+
+def test_w4a16_validation(L):
+    f = L.awq_w4a16_matmul
+
+    def call(x=P, s=None, T=2, c=P, sc=P, z=P, M=64, K=256, cfg=None, y=P):
+        return f(x, s, T, c, sc, z, M, K, cfg if cfg is not None else _cfg(), y, None)
+
+    assert call(x=None) == E["NULL"] and call(c=None) == E["NULL"] and call(y=None) == E["NULL"]
+    assert call(cfg=_cfg(4, 48)) == E["CONFIG"]
+    assert call(K=200) == E["SHAPE"]                   # not a multiple of the group
+    assert call(K=32768 + 128) == E["SHAPE"]           # beyond the GEMV's channel limit
+    assert call(T=-1) == E["SHAPE"]
+    assert call(x=P_ODD) == E["ALIGN"]
+    assert call(c=ctypes.c_void_p(0x10008)) == E["ALIGN"]
+    assert call(s=ctypes.c_void_p(0x10004)) == E["ALIGN"]
+    assert call(y=ctypes.c_void_p(0x10001)) == E["ALIGN"]
+    assert call(T=0) == E["OK"] and call(M=0) == E["OK"]

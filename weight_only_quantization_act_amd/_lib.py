@@ -56,6 +56,8 @@ _SIGNATURES = {
     "awq_threshold_scales": (ctypes.c_int, [_vp, _i64, ctypes.c_double, ctypes.c_float, _vp,
                                             _vp]),
     "awq_hadamard_rotate": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
+    "awq_w4a16_matmul": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _cfgp, _vp,
+                                        _vp]),
 }
 
 AWQ_STAT_MEAN_ABS, AWQ_STAT_MAX_ABS, AWQ_STAT_RMS_RATIO, AWQ_STAT_EMA_MEAN = 0, 1, 2, 3
@@ -308,3 +310,32 @@ def awq_hadamard_rotate(A: torch.Tensor, block: int, out: Optional[torch.Tensor]
     st = lib().awq_hadamard_rotate(_ptr(A), R, K, int(block), _ptr(out), _stream_ptr(stream))
     _check(st, "awq_hadamard_rotate")
     return out
+
+
+def awq_w4a16_matmul(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                     zeros: torch.Tensor, cfg: awq_qconfig, s: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y [T, M] fp16 = x~ [T, K] times the dequantised packed weights (x~ = x / s if s)."""
+    _dev(x, torch.float16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [n_tokens, in_features]")
+    T, K = x.shape
+    M = codes.shape[0]
+    _dev(codes, torch.uint8, "codes", (M, K // 2))
+    _dev(scales, torch.float16, "scales", (M, K // cfg.group_size))
+    _dev(zeros, torch.float16, "zeros", (M, K // cfg.group_size))
+    if s is not None:
+        _dev(s, torch.float32, "s", (K,))
+    y = out if out is not None else torch.empty((T, M), dtype=torch.float16, device=x.device)
+    _dev(y, torch.float16, "out", (T, M))
+    if T == 0 or M == 0:
+        return y
+    dummy = _buf(256, x.device) if (K == 0) else None
+    px = _ptr(x) if K else _ptr(dummy)
+    pc = _ptr(codes) if K else _ptr(dummy)
+    ps = _ptr(scales) if K else _ptr(dummy)
+    pz = _ptr(zeros) if K else _ptr(dummy)
+    st = lib().awq_w4a16_matmul(px, _ptr(s) if (s is not None and K) else None, T, pc, ps, pz,
+                                M, K, ctypes.byref(cfg), _ptr(y), _stream_ptr(stream))
+    _check(st, "awq_w4a16_matmul")
+    return y

@@ -298,6 +298,32 @@ int awq_hadamard_rotate(const void* A, int64_t rows, int64_t in_features, int32_
                                          (uint16_t*)out, (hipStream_t)stream));
 }
 
+int awq_w4a16_matmul(const void* x, const float* s, int64_t n_tokens, const void* codes,
+                     const void* scales, const void* zeros, int64_t out_features,
+                     int64_t in_features, const awq_qconfig* cfg, void* y, void* stream) {
+  const int64_t T = n_tokens, M = out_features, K = in_features;
+  if (!x || !codes || !scales || !zeros || !cfg || !y) return AWQ_E_NULL;
+  if (!cfg_valid(cfg)) return AWQ_E_CONFIG;
+  int st = weight_shape(M, K, cfg);
+  if (st != AWQ_OK) return st;
+  if (T < 0 || T >= kMaxElems || (K > 0 && T >= kMaxElems / K) ||
+      (M > 0 && T >= kMaxElems / M))
+    return AWQ_E_SHAPE;
+  if (K > awq::kGemvMaxK) return AWQ_E_SHAPE;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2) ||
+      !aligned(y, 2) || (s && !aligned(s, 16)))
+    return AWQ_E_ALIGN;
+  if (T == 0 || M == 0) return AWQ_OK;
+  if ((st = device_ptr(x)) || (st = device_ptr(codes)) || (st = device_ptr(scales)) ||
+      (st = device_ptr(zeros)) || (st = device_ptr(y)))
+    return st;
+  if (s && (st = device_ptr(s))) return st;
+  return hip_status(awq::launch_w4a16_gemv((const uint8_t*)codes, (const uint16_t*)scales,
+                                           (const uint16_t*)zeros, (const uint16_t*)x, s,
+                                           (int)T, (int)M, (int)K, cfg->group_size,
+                                           (uint16_t*)y, (hipStream_t)stream));
+}
+
 int awq_fake_quant_delta(const void* W, const float* s, int64_t out_features,
                          int64_t in_features, const awq_qconfig* cfg, void* dW_out,
                          void* stream) {

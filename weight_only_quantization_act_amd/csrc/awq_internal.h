@@ -51,6 +51,18 @@ hipError_t launch_quant_pack(const uint16_t* W, const float* s, int M, int K, in
                              int group_size, int zero_point, uint8_t* codes,
                              uint16_t* scales, uint16_t* zeros, hipStream_t stream);
 
+// ---- W4A16 product of a packed layer ----------------------------------------------------
+constexpr int kGemvMaxT = 4;      // tokens per GEMV pass (more tokens run in passes)
+constexpr int kGemvMaxK = 32768;  // one 32-channel code chunk per thread, 1024 threads
+struct GemvPlan {
+  int threads, rows;  // threads per block (K / 32 rounded up to waves), rows per block
+};
+GemvPlan w4a16_gemv_plan(int64_t M, int64_t K);
+// y [T][M] fp16 = x~ [T][K] times the dequantised packed weights; s may be null.
+hipError_t launch_w4a16_gemv(const uint8_t* codes, const uint16_t* scales,
+                             const uint16_t* zeros, const uint16_t* x, const float* s, int T,
+                             int M, int K, int group_size, uint16_t* y, hipStream_t stream);
+
 // ---- loss product and selection ------------------------------------------------------
 // partials[k * tiles + tm * tiles_n + tn] = sum over the tile of (dW_k X^T)^2.
 hipError_t launch_loss_gemm(const uint16_t* dW, const uint16_t* X, int M, int N, int K,
