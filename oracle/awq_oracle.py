@@ -33,6 +33,8 @@ Readings taken where the pages leave a step open (each repeated at its function)
   argmin        over finite losses, first index on ties; none finite -> index -1, s := 1
   packing       two 4-bit slots per byte, even input channel in the low nibble
   W4A16 product y = x~ W_dequant^T with x~ = fl16(fl32(x / s)) when s is given, fp64
+  clipping      per (row, group) ratio rho multiplies the group's range (hi, lo or max|v|)
+                in float32 before the step; chosen by the group's own output error
 """
 from __future__ import annotations
 
@@ -106,7 +108,7 @@ def scale_family(a32: np.ndarray, alphas32: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------------------
 # A3  group quantiser Q applied to the scaled weight W * diag(s)
 # --------------------------------------------------------------------------------------
-def quantize(W16: np.ndarray, s32: np.ndarray, cfg: QConfig):
+def quantize(W16: np.ndarray, s32: np.ndarray, cfg: QConfig, clip=None):
     """Group-wise uniform quantisation of v = W * s (float32, one rounding per op).
 
     [AWQ-tut 量化基础 (q = round(W/step), step = max|W| / (2^(b-1)-1));
@@ -121,6 +123,12 @@ def quantize(W16: np.ndarray, s32: np.ndarray, cfg: QConfig):
     Zero-point: hi = max(max_G v, 0), lo = min(min_G v, 0), step = (hi - lo) / (2^b - 1);
                 zero = clamp(rint(-lo/step), 0, 2^b-1); code = clamp(rint(v/step) + zero).
     A step that computes to 0 is replaced by 1.
+
+    clip (optional, float32 [M][K/g], each in (0, 1]) shrinks a group's range before the
+    step is taken -- hi and lo (zero-point) or max|v| (symmetric) are multiplied by the
+    ratio in float32 -- and values beyond the shrunk range are clipped by the clamp
+    [AWQ-notes closing note (the practical algorithm may add clipping); AWQ-notes §2.3
+    (Q includes rounding and clipping)].  Ratio 1 is the plain quantiser.
     """
     W16 = np.asarray(W16)
     M, K = W16.shape
@@ -134,6 +142,10 @@ def quantize(W16: np.ndarray, s32: np.ndarray, cfg: QConfig):
         top = F32(2 ** b - 1)
         hi = np.maximum(vg.max(axis=2, initial=-np.inf), F32(0.0))
         lo = np.minimum(vg.min(axis=2, initial=np.inf), F32(0.0))
+        if clip is not None:
+            r = np.asarray(clip, dtype=F32).reshape(M, K // g)
+            hi = (hi * r).astype(F32)
+            lo = (lo * r).astype(F32)
         step = ((hi - lo) / top).astype(F32)
         step[step == 0] = F32(1.0)
         zero = np.clip(np.rint(-lo / step), F32(0.0), top)
@@ -142,6 +154,8 @@ def quantize(W16: np.ndarray, s32: np.ndarray, cfg: QConfig):
     else:
         qmax = F32(2 ** (b - 1) - 1)
         mag = np.abs(vg).max(axis=2, initial=F32(0.0))
+        if clip is not None:
+            mag = (mag * np.asarray(clip, dtype=F32).reshape(M, K // g)).astype(F32)
         step = (mag / qmax).astype(F32)
         step[step == 0] = F32(1.0)
         q = np.clip(np.rint(vg / step[:, :, None]), -qmax, qmax)
@@ -163,7 +177,7 @@ def dequantize_scaled(codes: np.ndarray, step: np.ndarray, zero: np.ndarray,
 
 
 def fake_quant_weight(W16: np.ndarray, s32: np.ndarray, cfg: QConfig,
-                      identity_quantizer: bool = False) -> np.ndarray:
+                      identity_quantizer: bool = False, clip=None) -> np.ndarray:
     """Q(W S) S^-1 in float64: quantise the scaled weight, then divide each input channel
     by its scale [AWQ-tut 缩放保护 (W_hat = Q(s W)/s); AWQ-notes §2.2, §4.1].
 
@@ -173,16 +187,19 @@ def fake_quant_weight(W16: np.ndarray, s32: np.ndarray, cfg: QConfig,
     if identity_quantizer:
         d = (W16.astype(F32) * np.asarray(s32, dtype=F32)[None, :]).astype(F64)
     else:
-        codes, step, zero = quantize(W16, s32, cfg)
+        codes, step, zero = (quantize(W16, s32, cfg) if clip is None
+                             else quantize(W16, s32, cfg, clip=clip))
         d = dequantize_scaled(codes, step, zero, cfg.group_size).astype(F64)
     return d / s64[None, :]
 
 
 def delta_weight(W16: np.ndarray, s32: np.ndarray, cfg: QConfig,
-                 identity_quantizer: bool = False) -> np.ndarray:
+                 identity_quantizer: bool = False, clip=None) -> np.ndarray:
     """Delta W = W - Q(W S) S^-1 (float64) [AWQ-notes §1.1, weight error of the quantised
     layer; the sign does not matter for the squared loss]."""
-    return W16.astype(F64) - fake_quant_weight(W16, s32, cfg, identity_quantizer)
+    if clip is None:
+        return W16.astype(F64) - fake_quant_weight(W16, s32, cfg, identity_quantizer)
+    return W16.astype(F64) - fake_quant_weight(W16, s32, cfg, identity_quantizer, clip=clip)
 
 
 # --------------------------------------------------------------------------------------
@@ -269,7 +286,7 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
     return out
 
 
-def quantize_pack(W16, s32, cfg: QConfig):
+def quantize_pack(W16, s32, cfg: QConfig, clip=None):
     """Codes of Q(W S) packed two per byte, plus the per-group step as fp16 and the zero
     point as fp16 (an integer value) [AWQ-blog §1.2 (int4 codes with an fp16 scale,
     W = code * scale); AWQ-blog §2.1 (store the scale as FP16); AutoAWQ-70B §三
@@ -278,7 +295,8 @@ def quantize_pack(W16, s32, cfg: QConfig):
     The packed codes are of the *scaled* weight: S^-1 is folded into the preceding op
     [AWQ-notes §4.3].  Returns (packed uint8 [M][K/2], scales fp16 [M][K/g],
     zeros fp16 [M][K/g])."""
-    codes, step, zero = quantize(W16, s32, cfg)
+    codes, step, zero = (quantize(W16, s32, cfg) if clip is None
+                         else quantize(W16, s32, cfg, clip=clip))
     return pack_nibbles(codes), step.astype(np.float16), zero.astype(np.float16)
 
 
@@ -289,6 +307,46 @@ def run_layer(W16, X16, alphas32, cfg: QConfig):
     packed, scales, zeros = quantize_pack(W16, res["s_star"], cfg)
     res.update({"a": a32, "packed": packed, "scales": scales, "zeros": zeros})
     return res
+
+
+# --------------------------------------------------------------------------------------
+# Clip search after the scale search
+# --------------------------------------------------------------------------------------
+def clip_group_errors(W16, X16, s32, cfg: QConfig, ratios32) -> np.ndarray:
+    """e[k][m][j]: the output error that group j of row m contributes on its own when every
+    group's range is shrunk by ratio k, i.e. sum over tokens t of
+    (sum_{i in group j} dW_k[m][i] x_{t,i})^2 with dW_k = W - Q_k(W S) S^-1
+    [AWQ-notes §1.1 (output error of the weight error), closing note (clipping is searched
+    with the same kind of objective as the scales)].  Reading: the per-group objective is
+    the group's own partial product, so each (row, group) picks its ratio independently.
+    fp64 [n_ratio][M][K/g]."""
+    X64 = np.asarray(X16, dtype=F64)
+    W16 = np.asarray(W16)
+    M, K = W16.shape
+    g = cfg.group_size
+    ng = K // g
+    out = np.empty((len(ratios32), M, ng), dtype=F64)
+    for k, r in enumerate(np.asarray(ratios32, dtype=F32)):
+        dW = delta_weight(W16, s32, cfg, clip=np.full((M, ng), r, dtype=F32))
+        for j in range(ng):
+            Y = dW[:, j * g:(j + 1) * g] @ X64[:, j * g:(j + 1) * g].T
+            out[k, :, j] = np.sum(Y * Y, axis=1)
+    return out
+
+
+def clip_search(W16, X16, s32, cfg: QConfig, ratios32):
+    """For every (row, group) the ratio with the smallest group error (first on ties, so
+    the least clipping when the grid runs from 1 downwards; ratio 1 when no error is
+    finite).  Returns errors [n_ratio][M][K/g], best index [M][K/g] and the chosen
+    ratios float32 [M][K/g]."""
+    ratios32 = np.asarray(ratios32, dtype=F32)
+    e = clip_group_errors(W16, X16, s32, cfg, ratios32)
+    fin = np.isfinite(e)
+    masked = np.where(fin, e, np.inf)
+    best = np.argmin(masked, axis=0).astype(np.int32)
+    best[~fin.any(axis=0)] = -1
+    clip = np.where(best >= 0, ratios32[np.maximum(best, 0)], F32(1.0)).astype(F32)
+    return {"errors": e, "best": best, "clip": clip}
 
 
 # --------------------------------------------------------------------------------------

@@ -644,4 +644,82 @@ def pin_w4a16_reproduces_layer():
         assert np.max(np.abs(y - exact) / bound) > 0.05
 
 
+def pin_clip_ratio_one_and_range():
+    """Ratio 1 is the plain quantiser bit for bit; a ratio below 1 shrinks the range by
+    hand-checkable amounts and clamps the values beyond it [AWQ-notes §2.3 (Q rounds and
+    clips)]."""
+    rng = np.random.default_rng(50)
+    W = (rng.standard_normal((6, 256)) * 0.05).astype(np.float16)
+    s = np.exp(rng.uniform(-1, 1, 256)).astype(F32)
+    for cfg in (_cfg(4, 128, 1), _cfg(4, 64, 0), _cfg(3, 32, 1)):
+        ones = np.ones((6, 256 // cfg.group_size), F32)
+        a, b = O.quantize(W, s, cfg), O.quantize(W, s, cfg, clip=ones)
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    # zero-point, 4 bits: v in [-1, 2]; ratio 0.5 -> hi 1.0, lo -0.5, step 0.1, zero 5
+    v = np.linspace(-1.0, 2.0, 32).astype(np.float16)[None, :]
+    c, st, z = O.quantize(v, np.ones(32, F32), _cfg(4, 32, 1), clip=np.full((1, 1), 0.5, F32))
+    assert st[0, 0] == F32(F32(1.5) / F32(15)) and z[0, 0] == 5
+    deq = O.dequantize_scaled(c, st, z, 32)[0]
+    assert deq[-1] == F32(10 * st[0, 0]) and deq[0] == F32(-5 * st[0, 0])
+    inside = np.abs(v[0].astype(F32) - F32(0.25)) <= F32(0.7)
+    assert np.all(np.abs(deq[inside] - v[0].astype(F32)[inside]) <= st[0, 0] / 2 + 1e-7)
+    # symmetric, 4 bits: max|v| = 2 -> ratio 0.5 -> 1.0, step 1/7, 2.0 clamps to 7 steps
+    c, st, z = O.quantize(v, np.ones(32, F32), _cfg(4, 32, 0), clip=np.full((1, 1), 0.5, F32))
+    assert st[0, 0] == F32(F32(1.0) / F32(7))
+    assert O.dequantize_scaled(c, st, z, 32)[0, -1] == F32(7 * st[0, 0])
+
+
+def pin_clip_group_error_identities():
+    """The group error equals the quadratic form d^T (X_G^T X_G) d of the group's weight
+    error, and when the groups' activations have disjoint token supports (no cross terms)
+    the group errors add up to the layer's output-error loss [AWQ-notes §1.1]."""
+    rng = np.random.default_rng(51)
+    M, K, g = 5, 256, 64
+    cfg = _cfg(4, g, 1)
+    W = (rng.standard_normal((M, K)) * 0.03).astype(np.float16)
+    X = rng.standard_normal((40, K)).astype(np.float16)
+    s = np.exp(rng.uniform(-0.5, 0.5, K)).astype(F32)
+    ratios = np.array([1.0, 0.9, 0.75], F32)
+    e = O.clip_group_errors(W, X, s, cfg, ratios)
+    for k, r in enumerate(ratios):
+        d = O.delta_weight(W, s, cfg, clip=np.full((M, K // g), r, F32))
+        for j in range(K // g):
+            Xg = X[:, j * g:(j + 1) * g].astype(F64)
+            Gram = Xg.T @ Xg
+            dj = d[:, j * g:(j + 1) * g]
+            q = np.einsum("mi,ij,mj->m", dj, Gram, dj)
+            assert np.allclose(e[k, :, j], q, rtol=1e-10, atol=0)
+    Xd = np.zeros((4 * 10, K), np.float16)
+    for j in range(K // g):
+        Xd[10 * j:10 * (j + 1), j * g:(j + 1) * g] = X[10 * j:10 * (j + 1), j * g:(j + 1) * g]
+    e = O.clip_group_errors(W, Xd, s, cfg, ratios)
+    for k, r in enumerate(ratios):
+        d = O.delta_weight(W, s, cfg, clip=np.full((M, K // g), r, F32))
+        assert math.isclose(float(e[k].sum()), O.output_error_loss(d, Xd), rel_tol=1e-12)
+
+
+def pin_clip_search_choices():
+    """With identity activations (the group error is the squared weight error): a group
+    on the unclipped grid keeps ratio 1 (error 0); a group of even integers up to 6 with
+    one 15 is reproduced exactly at ratio 14/15 except the 15, which clips to 14, so that
+    ratio wins (error 1 against about 2.9 unclipped); equal ratios tie to the first."""
+    g = 32
+    cfg = _cfg(4, g, 0)
+    on_grid = (np.arange(-7, 8, dtype=F64)[np.arange(g) % 15] * 0.25).astype(np.float16)
+    ev = np.array([2.0, -2.0, 4.0, -4.0, 6.0, -6.0] * 6)[: g - 1]
+    outl = np.concatenate([ev, [15.0]]).astype(np.float16)
+    W = np.stack([on_grid, outl])
+    X = np.eye(g, dtype=np.float16)
+    s = np.ones(g, F32)
+    ratios = np.array([1.0, 14.0 / 15.0, 0.5], F32)
+    r = O.clip_search(W, X, s, cfg, ratios)
+    e = r["errors"]
+    assert r["best"][0, 0] == 0 and e[0, 0, 0] == 0.0 and e[1, 0, 0] > 0
+    assert r["best"][1, 0] == 1 and e[1, 1, 0] < e[0, 1, 0] / 2
+    assert abs(e[1, 1, 0] - 1.0) < 1e-3               # only the 15 -> 14 error remains
+    assert r["clip"][1, 0] == ratios[1]
+    tie = O.clip_search(W, X, s, cfg, np.array([1.0, 1.0, 0.5], F32))
+    assert tie["best"][0, 0] == 0
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -284,6 +284,45 @@ def _fold_multiplies(X16, s32):
     return (np.asarray(X16).astype(F32) * np.asarray(s32, F32)[None, :]).astype(np.float16)
 
 
+def _quantize_clip_divides(W16, s32, cfg, clip=None):
+    if clip is None:
+        return _orig_quantize(W16, s32, cfg)
+    return _orig_quantize(W16, s32, cfg, clip=1.0 / np.asarray(clip, F32))
+
+
+def _quantize_clip_ignored(W16, s32, cfg, clip=None):
+    return _orig_quantize(W16, s32, cfg)
+
+
+def _clip_errors_whole_row(W16, X16, s32, cfg, ratios32):
+    X64 = np.asarray(X16, F64)
+    M, K = np.asarray(W16).shape
+    ng = K // cfg.group_size
+    out = np.empty((len(ratios32), M, ng))
+    for k, r in enumerate(np.asarray(ratios32, F32)):
+        dW = O.delta_weight(W16, s32, cfg, clip=np.full((M, ng), r, F32))
+        Y = dW @ X64.T
+        out[k] = (np.sum(Y * Y, axis=1) / ng)[:, None]
+    return out
+
+
+_orig_clip_errors = O.clip_group_errors
+
+
+def _clip_search_argmax(W16, X16, s32, cfg, ratios32):
+    ratios32 = np.asarray(ratios32, F32)
+    e = _orig_clip_errors(W16, X16, s32, cfg, ratios32)
+    best = np.argmax(e, axis=0).astype(np.int32)
+    return {"errors": e, "best": best, "clip": ratios32[best]}
+
+
+MUTANTS.update({
+    "clip_divides_range": ("quantize", _quantize_clip_divides),
+    "clip_ignored": ("quantize", _quantize_clip_ignored),
+    "clip_error_whole_row": ("clip_group_errors", _clip_errors_whole_row),
+    "clip_search_argmax": ("clip_search", _clip_search_argmax),
+})
+
 MUTANTS.update({
     "w4a16_zero_not_subtracted": ("dequantize_packed", _dequant_packed_no_zero),
     "w4a16_groups_tiled": ("dequantize_packed", _dequant_packed_tiled),
