@@ -287,6 +287,15 @@ def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, reps=20):
                      device="cuda")
     ms = timed(lambda: awq.awq_search_scale_table(Wd, Xd, table, cfg, workspace=ws))
     out["search_scale_table_20_threshold_rows"] = {"ms": ms}
+    ratios = [1.0 - 0.025 * k for k in range(20)]
+    s_best = awq.awq_search_scales(Wd, Xd, a, [0.5], cfg)["s"]
+    ws_clip = torch.empty(awq.awq_clip_workspace_bytes(M, K, N, cfg), dtype=torch.uint8,
+                          device="cuda")
+    ms = timed(lambda: awq.awq_clip_search(Wd, Xd, s_best, ratios, cfg, workspace=ws_clip))
+    g = cfg.group_size
+    out["clip_search_20_ratios"] = {
+        "ms": ms, "gram_flops": 2.0 * N * K * g, "quadratic_flops": 2.0 * M * K * g * 20,
+        "TFLOP/s": (2.0 * N * K * g + 2.0 * M * K * g * 20) / (ms * 1e-3) / 1e12}
     return out
 
 

@@ -171,6 +171,40 @@ int awq_hadamard_rotate(const void* A, int64_t rows, int64_t in_features, int32_
                         void* out, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Clip search after the scale search
+ *   For every row m, group j and ratio rho_k of the grid: shrink the group's range of
+ *   v = W diag(s) by rho_k (hi and lo, or max|v|, multiplied in fp32), quantise as
+ *   awq_quantize_pack does (values beyond the range clamp), and score the group's own
+ *   output error e = sum_t (sum_{i in j} d_i x_{t,i})^2 with d = W - Q(v) / s.  The
+ *   chosen ratio is the first smallest finite e (ratio 1 when none is finite)
+ *   [AWQ-notes closing note (the practical algorithm may add clipping), §2.3 (Q rounds
+ *   and clips), §1.1 (output error = weight error times activations)].
+ *   The GPU evaluates e = d^T (X_j^T X_j) d with the group Gram matrices (fp64 sums,
+ *   stored fp32) and fp32 quadratic forms.
+ *   W fp16 [out][in], X fp16 [n_tokens][in] (16-byte aligned), s fp32 [in] (the chosen
+ *   scales, e.g. awq_search_scales' s_out), all device
+ *   ratios_host  fp32 [n_ratio], HOST memory, each in (0, 1]; n_ratio in [1, 64]
+ *   clip_out     fp32 [out][in/group_size], device (written: chosen ratios)
+ *   best_out     int32 [out][in/group_size] chosen indices (-1: none finite), or NULL
+ *   errors_out   fp32 [n_ratio][out][in/group_size] every group error, or NULL
+ *   workspace    device scratch of awq_clip_workspace_bytes(...) bytes, 256-byte aligned
+ * ---------------------------------------------------------------------------------- */
+size_t awq_clip_workspace_bytes(int64_t out_features, int64_t in_features, int64_t n_tokens,
+                                const awq_qconfig* cfg);
+int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_features,
+                    int64_t in_features, int64_t n_tokens, const awq_qconfig* cfg,
+                    const float* ratios_host, int32_t n_ratio, float* clip_out,
+                    int32_t* best_out, float* errors_out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+/* awq_quantize_pack with every group's range shrunk by its ratio clip[row][group]
+ * (fp32 [out][in/group_size], device, each in (0, 1]); ratio 1 everywhere gives
+ * awq_quantize_pack's output bit for bit. */
+int awq_quantize_pack_clipped(const void* W, const float* s, const float* clip,
+                              int64_t out_features, int64_t in_features, const awq_qconfig* cfg,
+                              uint8_t* codes_out, void* scales_out, void* zeros_out,
+                              void* stream);
+
+/* ------------------------------------------------------------------------------------
  * W4A16 product of a packed layer (the consumer of awq_quantize_pack's output)
  *   y[t][m] = sum_i (c[m][i] - z[m][g]) * step[m][g] * xt[t][i],   g = i / group_size,
  *   xt = x when s is NULL (S^-1 already folded into the preceding operation

@@ -36,7 +36,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in awq_act.h but not exported"
     assert set(names) == set(_lib._SIGNATURES)
@@ -216,3 +216,29 @@ def test_w4a16_validation(L):
     assert call(s=ctypes.c_void_p(0x10004)) == E["ALIGN"]
     assert call(y=ctypes.c_void_p(0x10001)) == E["ALIGN"]
     assert call(T=0) == E["OK"] and call(M=0) == E["OK"]
+
+
+def test_clip_validation(L):
+    f = L.awq_clip_search
+    need = awq.awq_clip_workspace_bytes(64, 256, 100, awq.qconfig())
+    assert need > 0 and need % 256 == 0
+
+    def call(W=P, X=P, s=P, M=64, K=256, N=100, cfg=None, ratios=(1.0, 0.9, 0.8), n=None,
+             clip=P, best=None, errors=None, ws=P, ws_bytes=1 << 40):
+        rl = (ctypes.c_float * max(1, len(ratios)))(*ratios)
+        return f(W, X, s, M, K, N, cfg if cfg is not None else _cfg(), rl,
+                 len(ratios) if n is None else n, clip, best, errors, ws, ws_bytes, None)
+
+    assert call(W=None) == E["NULL"] and call(clip=None) == E["NULL"]
+    assert call(ws=None) == E["WORKSPACE"] and call(ws_bytes=need - 1) == E["WORKSPACE"]
+    assert call(ratios=(1.0, 0.0)) == E["ALPHA"] and call(ratios=(1.5,)) == E["ALPHA"]
+    assert call(ratios=(float("nan"),)) == E["ALPHA"]
+    assert call(ratios=(), n=0) == E["ALPHA"] and call(ratios=tuple([0.5] * 65)) == E["ALPHA"]
+    assert call(cfg=_cfg(4, 48)) == E["CONFIG"] and call(K=200) == E["SHAPE"]
+    assert call(N=0) == E["SHAPE"]
+    assert call(X=P_ODD) == E["ALIGN"] and call(ws=ctypes.c_void_p(0x10010)) == E["ALIGN"]
+    assert call(M=0) == E["OK"]
+    g = L.awq_quantize_pack_clipped
+    assert g(P, P, None, 8, 128, _cfg(), P, P, P, None) == E["NULL"]
+    assert g(P, P, ctypes.c_void_p(0x10002), 8, 128, _cfg(), P, P, P, None) == E["ALIGN"]
+    assert g(P, P, P, 0, 128, _cfg(), P, P, P, None) == E["OK"]

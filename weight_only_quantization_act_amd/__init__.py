@@ -17,6 +17,9 @@ from ._lib import (  # noqa: F401
     awq_act_stats_ex,
     awq_act_stats_ex_workspace_bytes,
     awq_act_stats_workspace_bytes,
+    awq_clip_search,
+    awq_clip_workspace_bytes,
+    awq_quantize_pack_clipped,
     awq_hadamard_rotate,
     awq_search_scale_table,
     awq_threshold_scales,

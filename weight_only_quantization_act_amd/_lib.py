@@ -58,6 +58,11 @@ _SIGNATURES = {
     "awq_hadamard_rotate": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
     "awq_w4a16_matmul": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _cfgp, _vp,
                                         _vp]),
+    "awq_clip_workspace_bytes": (_sz, [_i64, _i64, _i64, _cfgp]),
+    "awq_clip_search": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _cfgp, _vp, _i32, _vp,
+                                       _vp, _vp, _vp, _sz, _vp]),
+    "awq_quantize_pack_clipped": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _cfgp, _vp, _vp, _vp,
+                                                 _vp]),
 }
 
 AWQ_STAT_MEAN_ABS, AWQ_STAT_MAX_ABS, AWQ_STAT_RMS_RATIO, AWQ_STAT_EMA_MEAN = 0, 1, 2, 3
@@ -339,3 +344,59 @@ def awq_w4a16_matmul(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
                                 M, K, ctypes.byref(cfg), _ptr(y), _stream_ptr(stream))
     _check(st, "awq_w4a16_matmul")
     return y
+
+
+def awq_clip_workspace_bytes(out_features: int, in_features: int, n_tokens: int,
+                             cfg: awq_qconfig) -> int:
+    return int(lib().awq_clip_workspace_bytes(out_features, in_features, n_tokens,
+                                              ctypes.byref(cfg)))
+
+
+def awq_clip_search(W: torch.Tensor, X: torch.Tensor, s: torch.Tensor, ratios: Sequence[float],
+                    cfg: awq_qconfig, want_errors: bool = False,
+                    workspace: Optional[torch.Tensor] = None, stream=None):
+    """Per (row, group) clip ratio after the scale search.  Returns device tensors
+    clip [M, K/g] fp32, best [M, K/g] int32 and (if asked) errors [n, M, K/g] fp32."""
+    _dev(W, torch.float16, "W")
+    _dev(X, torch.float16, "X")
+    M, K = W.shape
+    N = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be [n_tokens, in_features] with W's in_features")
+    _dev(s, torch.float32, "s", (K,))
+    n = len(ratios)
+    rl = (ctypes.c_float * max(1, n))(*[float(v) for v in ratios])
+    ng = K // cfg.group_size
+    dev = W.device
+    clip = torch.empty((M, ng), dtype=torch.float32, device=dev)
+    best = torch.empty((M, ng), dtype=torch.int32, device=dev)
+    errors = torch.empty((n, M, ng), dtype=torch.float32, device=dev) if want_errors else None
+    if workspace is None:
+        workspace = _buf(awq_clip_workspace_bytes(M, K, N, cfg), dev)
+    if M == 0 or K == 0:
+        return {"clip": clip, "best": best, "errors": errors}
+    st = lib().awq_clip_search(_ptr(W), _ptr(X), _ptr(s), M, K, N, ctypes.byref(cfg), rl, n,
+                               _ptr(clip), _ptr(best), _ptr(errors) if want_errors else None,
+                               _ptr(workspace), workspace.numel(), _stream_ptr(stream))
+    _check(st, "awq_clip_search")
+    return {"clip": clip, "best": best, "errors": errors}
+
+
+def awq_quantize_pack_clipped(W: torch.Tensor, s: torch.Tensor, clip: torch.Tensor,
+                              cfg: awq_qconfig, stream=None):
+    """awq_quantize_pack with per-(row, group) range ratios clip [M, K/g] fp32."""
+    _dev(W, torch.float16, "W")
+    M, K = W.shape
+    _dev(s, torch.float32, "s", (K,))
+    _dev(clip, torch.float32, "clip", (M, K // cfg.group_size))
+    dev = W.device
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // cfg.group_size), dtype=torch.float16, device=dev)
+    zeros = torch.empty((M, K // cfg.group_size), dtype=torch.float16, device=dev)
+    if M == 0 or K == 0:
+        return codes, scales, zeros
+    st = lib().awq_quantize_pack_clipped(_ptr(W), _ptr(s), _ptr(clip), M, K, ctypes.byref(cfg),
+                                         _ptr(codes), _ptr(scales), _ptr(zeros),
+                                         _stream_ptr(stream))
+    _check(st, "awq_quantize_pack_clipped")
+    return codes, scales, zeros

@@ -339,24 +339,100 @@ int awq_fake_quant_delta(const void* W, const float* s, int64_t out_features,
       cfg->group_size, cfg->zero_point, (uint16_t*)dW_out, (hipStream_t)stream));
 }
 
-int awq_quantize_pack(const void* W, const float* s, int64_t out_features, int64_t in_features,
-                      const awq_qconfig* cfg, uint8_t* codes_out, void* scales_out,
-                      void* zeros_out, void* stream) {
+namespace {
+int pack_impl(const void* W, const float* s, const float* clip, int64_t out_features,
+              int64_t in_features, const awq_qconfig* cfg, uint8_t* codes_out,
+              void* scales_out, void* zeros_out, void* stream) {
   if (!W || !s || !cfg || !codes_out || !scales_out || !zeros_out) return AWQ_E_NULL;
   if (!cfg_valid(cfg)) return AWQ_E_CONFIG;
   int st = weight_shape(out_features, in_features, cfg);
   if (st != AWQ_OK) return st;
   if (!aligned(W, 16) || !aligned(s, 16) || !aligned(codes_out, 4) || !aligned(scales_out, 2) ||
-      !aligned(zeros_out, 2))
+      !aligned(zeros_out, 2) || (clip && !aligned(clip, 4)))
     return AWQ_E_ALIGN;
   if (out_features == 0 || in_features == 0) return AWQ_OK;
   if ((st = device_ptr(W)) || (st = device_ptr(s)) || (st = device_ptr(codes_out)) ||
       (st = device_ptr(scales_out)) || (st = device_ptr(zeros_out)))
     return st;
-  return hip_status(awq::launch_quant_pack((const uint16_t*)W, s, (int)out_features,
+  if (clip && (st = device_ptr(clip))) return st;
+  return hip_status(awq::launch_quant_pack((const uint16_t*)W, s, clip, (int)out_features,
                                            (int)in_features, cfg->w_bit, cfg->group_size,
                                            cfg->zero_point, codes_out, (uint16_t*)scales_out,
                                            (uint16_t*)zeros_out, (hipStream_t)stream));
+}
+}  // namespace
+
+int awq_quantize_pack(const void* W, const float* s, int64_t out_features, int64_t in_features,
+                      const awq_qconfig* cfg, uint8_t* codes_out, void* scales_out,
+                      void* zeros_out, void* stream) {
+  return pack_impl(W, s, nullptr, out_features, in_features, cfg, codes_out, scales_out,
+                   zeros_out, stream);
+}
+
+int awq_quantize_pack_clipped(const void* W, const float* s, const float* clip,
+                              int64_t out_features, int64_t in_features, const awq_qconfig* cfg,
+                              uint8_t* codes_out, void* scales_out, void* zeros_out,
+                              void* stream) {
+  if (!clip) return AWQ_E_NULL;
+  return pack_impl(W, s, clip, out_features, in_features, cfg, codes_out, scales_out, zeros_out,
+                   stream);
+}
+
+size_t awq_clip_workspace_bytes(int64_t out_features, int64_t in_features, int64_t n_tokens,
+                                const awq_qconfig* cfg) {
+  if (!cfg_valid(cfg)) return 0;
+  if (weight_shape(out_features, in_features, cfg) != AWQ_OK) return 0;
+  if (token_shape(n_tokens, in_features) != AWQ_OK) return 0;
+  const size_t kg = (size_t)in_features * cfg->group_size;
+  const int splits = awq::gram_splits(n_tokens, in_features, cfg->group_size);
+  return round_up(kg * sizeof(float), kAlign) + round_up((size_t)splits * kg * sizeof(double),
+                                                        kAlign);
+}
+
+int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_features,
+                    int64_t in_features, int64_t n_tokens, const awq_qconfig* cfg,
+                    const float* ratios_host, int32_t n_ratio, float* clip_out,
+                    int32_t* best_out, float* errors_out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const int64_t M = out_features, K = in_features, N = n_tokens;
+  if (!W || !X || !s || !cfg || !ratios_host || !clip_out) return AWQ_E_NULL;
+  if (!workspace) return AWQ_E_WORKSPACE;
+  if (!cfg_valid(cfg)) return AWQ_E_CONFIG;
+  int st = weight_shape(M, K, cfg);
+  if (st != AWQ_OK) return st;
+  if ((st = token_shape(N, K)) != AWQ_OK) return st;
+  if (n_ratio < 1 || n_ratio > awq::kMaxClip) return AWQ_E_ALPHA;
+  awq::ClipList rl;
+  memset(&rl, 0, sizeof(rl));
+  for (int k = 0; k < n_ratio; ++k) {
+    const float v = ratios_host[k];
+    if (!(v > 0.0f && v <= 1.0f)) return AWQ_E_ALPHA;  // also rejects NaN
+    rl.v[k] = v;
+  }
+  if (errors_out && K > 0 && (int64_t)n_ratio * M >= kMaxElems / (K / cfg->group_size))
+    return AWQ_E_SHAPE;
+  if (workspace_bytes < awq_clip_workspace_bytes(M, K, N, cfg)) return AWQ_E_WORKSPACE;
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(s, 4) || !aligned(clip_out, 4) ||
+      !aligned(best_out, 4) || !aligned(errors_out, 4) || !aligned(workspace, kAlign))
+    return AWQ_E_ALIGN;
+  if (M == 0 || K == 0) return AWQ_OK;
+  if ((st = device_ptr(W)) || (st = device_ptr(X)) || (st = device_ptr(s)) ||
+      (st = device_ptr(clip_out)) || (st = device_ptr(workspace)))
+    return st;
+  if (best_out && (st = device_ptr(best_out))) return st;
+  if (errors_out && (st = device_ptr(errors_out))) return st;
+  const size_t kg = (size_t)K * cfg->group_size;
+  float* G = (float*)workspace;
+  double* partials = (double*)((char*)workspace + round_up(kg * sizeof(float), kAlign));
+  const int splits = awq::gram_splits(N, K, cfg->group_size);
+  if ((st = hip_status(awq::launch_group_gram((const uint16_t*)X, (int)N, (int)K,
+                                              cfg->group_size, splits, partials, G,
+                                              (hipStream_t)stream))))
+    return st;
+  return hip_status(awq::launch_clip_search((const uint16_t*)W, s, G, (int)M, (int)K,
+                                            cfg->w_bit, cfg->group_size, cfg->zero_point, rl,
+                                            n_ratio, clip_out, best_out, errors_out,
+                                            (hipStream_t)stream));
 }
 
 int awq_set_profile_events(void* gemm_start, void* gemm_stop, void* fq_start, void* fq_stop) {

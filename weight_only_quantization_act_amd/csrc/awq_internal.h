@@ -47,9 +47,27 @@ hipError_t launch_threshold_scales(const float* a, int K, double percentile, flo
 // Rotate each row of A [rows][K] by blockwise normalised Hadamard matrices along K.
 hipError_t launch_hadamard(const uint16_t* A, int rows, int K, int block, uint16_t* out,
                            hipStream_t stream);
-hipError_t launch_quant_pack(const uint16_t* W, const float* s, int M, int K, int w_bit,
-                             int group_size, int zero_point, uint8_t* codes,
+// clip (nullable, fp32 [M][K/group_size]) shrinks each group's range by its ratio.
+hipError_t launch_quant_pack(const uint16_t* W, const float* s, const float* clip, int M,
+                             int K, int w_bit, int group_size, int zero_point, uint8_t* codes,
                              uint16_t* scales, uint16_t* zeros, hipStream_t stream);
+
+// ---- clip search ------------------------------------------------------------------------
+constexpr int kMaxClip = 64;
+struct ClipList {
+  float v[kMaxClip];
+};
+// Gram matrices of the activation groups: G[j] = X_j^T X_j (fp64 sums, stored fp32),
+// fp32 [K/g][g][g]; partials fp64 [splits][K/g][g][g].
+int gram_splits(int64_t N, int64_t K, int group_size);
+hipError_t launch_group_gram(const uint16_t* X, int N, int K, int group_size, int splits,
+                             double* partials, float* G, hipStream_t stream);
+// Per (row, group): the group's own output error d^T G_j d for every ratio, the first
+// smallest, its ratio (1 when none is finite); errors (nullable) fp32 [n][M][K/g].
+hipError_t launch_clip_search(const uint16_t* W, const float* s, const float* G, int M, int K,
+                              int w_bit, int group_size, int zero_point, const ClipList& ratios,
+                              int n_ratio, float* clip_out, int32_t* best_out, float* errors,
+                              hipStream_t stream);
 
 // ---- W4A16 product of a packed layer ----------------------------------------------------
 constexpr int kGemvMaxT = 4;      // tokens per GEMV pass (more tokens run in passes)

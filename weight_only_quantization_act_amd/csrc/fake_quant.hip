@@ -110,8 +110,9 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant_delta(
 
 template <int LANES>
 __global__ __launch_bounds__(kThreads) void k_quant_pack(
-    const uint16_t* __restrict__ W, const float* __restrict__ s_in, int M, int K, int w_bit,
-    int zero_point, uint8_t* __restrict__ codes_out, uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ W, const float* __restrict__ s_in,
+    const float* __restrict__ clip, int M, int K, int w_bit, int zero_point,
+    uint8_t* __restrict__ codes_out, uint16_t* __restrict__ scales,
     uint16_t* __restrict__ zeros) {
   const int chunk = blockIdx.x * kThreads + threadIdx.x;
   const int col0 = chunk * 8;
@@ -143,7 +144,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_pack(
     unpack8(raw, w);
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = w[i] * s[i];
-    quantize8<LANES>(v, w_bit, zp, code, st, z);
+    const float ratio = (clip != nullptr && col_ok) ? clip[(size_t)row * G + group] : 1.0f;
+    quantize8<LANES>(v, w_bit, zp, code, st, z, ratio);
     if (col_ok) {
       uint32_t packed = 0;
 #pragma unroll
@@ -192,23 +194,23 @@ hipError_t launch_fake_quant_delta(const uint16_t* W, const float* s_table, int 
   return hipGetLastError();
 }
 
-hipError_t launch_quant_pack(const uint16_t* W, const float* s, int M, int K, int w_bit,
-                             int group_size, int zero_point, uint8_t* codes,
+hipError_t launch_quant_pack(const uint16_t* W, const float* s, const float* clip, int M,
+                             int K, int w_bit, int group_size, int zero_point, uint8_t* codes,
                              uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
   if (M <= 0 || K <= 0) return hipSuccess;
   const int chunks = K / 8;
   dim3 grid((chunks + kThreads - 1) / kThreads, (M + kRowsPack - 1) / kRowsPack);
   switch (group_size) {
     case 32:
-      hipLaunchKernelGGL(k_quant_pack<4>, grid, dim3(kThreads), 0, stream, W, s, M, K, w_bit,
+      hipLaunchKernelGGL(k_quant_pack<4>, grid, dim3(kThreads), 0, stream, W, s, clip, M, K, w_bit,
                          zero_point, codes, scales, zeros);
       break;
     case 64:
-      hipLaunchKernelGGL(k_quant_pack<8>, grid, dim3(kThreads), 0, stream, W, s, M, K, w_bit,
+      hipLaunchKernelGGL(k_quant_pack<8>, grid, dim3(kThreads), 0, stream, W, s, clip, M, K, w_bit,
                          zero_point, codes, scales, zeros);
       break;
     case 128:
-      hipLaunchKernelGGL(k_quant_pack<16>, grid, dim3(kThreads), 0, stream, W, s, M, K, w_bit,
+      hipLaunchKernelGGL(k_quant_pack<16>, grid, dim3(kThreads), 0, stream, W, s, clip, M, K, w_bit,
                          zero_point, codes, scales, zeros);
       break;
     default:

@@ -97,10 +97,14 @@ __device__ __forceinline__ void round_quotients(const float (&v)[8], float st, f
 }
 
 // Quantise the lane's 8 scaled values v[] of one group.  On return code[] holds the
-// integer codes as floats (exact), and step/zero the group's parameters.
+// integer codes as floats (exact), and step/zero the group's parameters.  ratio (1 for no
+// clipping) multiplies the group's range (hi and lo, or max|v|) before the step is taken;
+// the clamps then clip the values beyond it.  Multiplying by 1 is exact, so ratio 1 is the
+// plain quantiser bit for bit.
 template <int LANES>
 __device__ __forceinline__ void quantize8(const float (&v)[8], int w_bit, bool zero_point,
-                                          float (&code)[8], float& step, float& zero) {
+                                          float (&code)[8], float& step, float& zero,
+                                          float ratio = 1.0f) {
   if (zero_point) {
     float hi = v[0], lo = v[0];
 #pragma unroll
@@ -108,8 +112,8 @@ __device__ __forceinline__ void quantize8(const float (&v)[8], int w_bit, bool z
       hi = fmaxf(hi, v[i]);
       lo = fminf(lo, v[i]);
     }
-    hi = fmaxf(group_max<LANES>(hi), 0.0f);
-    lo = fminf(group_min<LANES>(lo), 0.0f);
+    hi = fmaxf(group_max<LANES>(hi), 0.0f) * ratio;
+    lo = fminf(group_min<LANES>(lo), 0.0f) * ratio;
     const float top = (float)((1 << w_bit) - 1);
     float st = (hi - lo) / top;
     if (st == 0.0f) st = 1.0f;
@@ -128,7 +132,7 @@ __device__ __forceinline__ void quantize8(const float (&v)[8], int w_bit, bool z
     float m = fabsf(v[0]);
 #pragma unroll
     for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-    m = group_max<LANES>(m);
+    m = group_max<LANES>(m) * ratio;
     const float qmax = (float)((1 << (w_bit - 1)) - 1);
     const float off = (float)(1 << (w_bit - 1));
     float st = m / qmax;
