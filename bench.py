@@ -24,6 +24,9 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+# fp32 vector ALU without packed fp32 instructions (the kernels are built without them):
+# 256 CUs x 64 lanes per clock x 2 flops (FMA) x 2.4 GHz; packed math would double it.
+FP32_VALU_PEAK_TFLOPS = 78.6
 
 
 def parse():
@@ -274,28 +277,34 @@ def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, reps=20):
                               ("stat_rms_ratio", awq.AWQ_STAT_RMS_RATIO, ()),
                               ("stat_ema_mean_b512", awq.AWQ_STAT_EMA_MEAN, (512, 0.9))]:
         ms = timed(lambda: awq.awq_act_stats_ex(Xd, mode, *extra))
-        out[name] = {"ms": ms, "GB/s": x_bytes / (ms * 1e-3) / 1e9}
+        gbs = x_bytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
     a = awq.awq_act_stats(Xd)
     out["threshold_scales"] = {"ms": timed(lambda: awq.awq_threshold_scales(a, 70.0, 2.0)),
                                "in_features": K}
     Xr = torch.empty_like(Xd)
     ms = timed(lambda: awq.awq_hadamard_rotate(Xd, 128, out=Xr))
-    out["hadamard_rotate_X_b128"] = {"ms": ms, "GB/s": 4.0 * N * K / (ms * 1e-3) / 1e9}
+    gbs = 4.0 * N * K / (ms * 1e-3) / 1e9
+    out["hadamard_rotate_X_b128"] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
     table = torch.stack([awq.awq_threshold_scales(a, p, f) for p in (50.0, 70.0, 85.0, 95.0, 99.0)
                          for f in (1.5, 2.0, 3.0, 4.0)]).contiguous()
     ws = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, table.shape[0], 0), dtype=torch.uint8,
                      device="cuda")
     ms = timed(lambda: awq.awq_search_scale_table(Wd, Xd, table, cfg, workspace=ws))
-    out["search_scale_table_20_threshold_rows"] = {"ms": ms}
+    tf = 2.0 * M * N * K * table.shape[0] / (ms * 1e-3) / 1e12
+    out["search_scale_table_20_threshold_rows"] = {"ms": ms, "TFLOP/s": tf,
+                                                   "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS}
     ratios = [1.0 - 0.025 * k for k in range(20)]
     s_best = awq.awq_search_scales(Wd, Xd, a, [0.5], cfg)["s"]
     ws_clip = torch.empty(awq.awq_clip_workspace_bytes(M, K, N, cfg), dtype=torch.uint8,
                           device="cuda")
     ms = timed(lambda: awq.awq_clip_search(Wd, Xd, s_best, ratios, cfg, workspace=ws_clip))
     g = cfg.group_size
+    tf = (2.0 * N * K * g + 2.0 * M * K * g * 20) / (ms * 1e-3) / 1e12
     out["clip_search_20_ratios"] = {
         "ms": ms, "gram_flops": 2.0 * N * K * g, "quadratic_flops": 2.0 * M * K * g * 20,
-        "TFLOP/s": (2.0 * N * K * g + 2.0 * M * K * g * 20) / (ms * 1e-3) / 1e12}
+        "TFLOP/s": tf, "bound": "alu", "peak_TFLOP/s": FP32_VALU_PEAK_TFLOPS,
+        "frac_alu": tf / FP32_VALU_PEAK_TFLOPS}
     return out
 
 
@@ -327,7 +336,8 @@ def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, reps=50):
         x = Xd[:T].contiguous()
         ms = timed(lambda: awq.awq_w4a16_matmul(x, codes, scales, zeros, cfg, s=s))
         b = w4a16_bytes(M, K, g, T, True)
-        out[f"{M}x{K}_T{T}"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+        out[f"{M}x{K}_T{T}"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b,
+                                "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     M2, K2 = 28672, 8192
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20250)
@@ -335,17 +345,20 @@ def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, reps=50):
     sc2 = (torch.rand((M2, K2 // g), device="cuda", generator=gen) * 0.02 + 0.0005).half()
     z2 = torch.randint(0, 16, (M2, K2 // g), device="cuda", generator=gen).half()
     s2 = torch.rand((K2,), device="cuda", generator=gen) * 3 + 0.5
-    x2 = torch.randn((4, K2), device="cuda", generator=gen).half()
-    for T in (1, 4):
+    x2 = torch.randn((16, K2), device="cuda", generator=gen).half()
+    for T in (1, 4, 16):
         x = x2[:T].contiguous()
-        ms = timed(lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg, s=s2))
-        b = w4a16_bytes(M2, K2, g, T, True)
-        out[f"{M2}x{K2}_T{T}"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+        if T <= 4:
+            ms = timed(lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg, s=s2))
+            b = w4a16_bytes(M2, K2, g, T, True)
+            out[f"{M2}x{K2}_T{T}"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b,
+                                      "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         # S^-1 already folded into the activations (the deployed form): no division
         ms = timed(lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg))
         b = w4a16_bytes(M2, K2, g, T, False)
         out[f"{M2}x{K2}_T{T}_folded"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9,
-                                          "bytes": b}
+                                          "bytes": b,
+                                          "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     return out
 
 

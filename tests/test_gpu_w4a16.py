@@ -1,12 +1,15 @@
 """W4A16 product of a packed layer on the GPU (through the C ABI) against the fp64 oracle.
 
-Bar, derived from the kernel's arithmetic: the folded activations x~ = fp16(fp32(x / s))
+Bar, derived from the kernels' arithmetic: the folded activations x~ = fp16(fp32(x / s))
 are formed identically on both sides; every (c - z) and every fp16 x fp16 product is
-exact in fp32; a result passes through at most 32 dot-product roundings in a lane, one
-multiplication by the step, a 6-level lane tree and at most 15 wave additions, so the
-fp32 sum is within 64 * 2^-24 * sum_i |w_i x~_i| of the exact one; the final fp16
-rounding adds at most one fp16 ulp.  A wrong nibble, group, zero or token would break
-this by orders of magnitude.
+exact in fp32.  In the vector kernel a result passes through at most 32 dot-product
+roundings in a lane, one multiplication by the step and the chunk sum (at most 1024
+additions, bounded by their magnitudes); in the matrix-core kernel through the MFMA's
+own sums, one fused multiply-add per group (at most 64 per wave) and at most 15 wave
+additions.  Both stay within 256 * 2^-24 * sum_i |w_i x~_i| of the exact sum; the final
+fp16 rounding adds at most one fp16 ulp.  A wrong nibble, group, zero or token would
+break this by orders of magnitude.  With S^-1 folded (s = None) and two or more tokens
+the library takes the matrix-core kernel, otherwise the vector kernel.
 """
 import numpy as np
 import pytest
@@ -37,7 +40,7 @@ def _check(y_gpu, packed, scales, zeros, X, g, s=None, where=""):
     Xt = np.asarray(X) if s is None else O.fold_inverse_scales(X, s)
     Wd = O.dequantize_packed(packed, scales, zeros, g)
     mag = np.abs(Xt.astype(F64)) @ np.abs(Wd).T
-    E = 64 * 2.0 ** -24 * mag
+    E = 256 * 2.0 ** -24 * mag
     ulp = np.spacing((np.abs(y_ref) + E).astype(F16)).astype(F64)
     yg = np.asarray(y_gpu).astype(F64)
     assert yg.shape == y_ref.shape
@@ -61,6 +64,13 @@ CASES = [
     (40, 1024, 9, 64, True),        # three passes
     (9, 32768, 2, 128, False),      # the largest K: 1024 threads
     (33, 32, 1, 32, True),          # a single chunk
+    # folded activations, several tokens: the matrix-core kernel
+    (100, 1024, 16, 32, False),
+    (50, 2048, 16, 64, False),
+    (300, 4096, 7, 128, False),
+    (65, 640, 17, 128, False),      # 16 + 1 tokens: two passes
+    (200, 11008, 33, 128, False),   # three passes, 86 groups over the waves
+    (3, 32768, 4, 32, False),       # 1024 groups of 32
 ]
 
 
@@ -110,9 +120,18 @@ def test_w4a16_deterministic():
     packed, scales, zeros = _random_packed(rng, 512, 4096, 128)
     X = dev(rng.standard_normal((4, 4096)).astype(F16))
     cfg = awq.qconfig(4, 128, 1)
-    a = host(awq.awq_w4a16_matmul(X, dev(packed), dev(scales), dev(zeros), cfg)).copy()
-    b = host(awq.awq_w4a16_matmul(X, dev(packed), dev(scales), dev(zeros), cfg))
-    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    for T in (1, 4):
+        a = host(awq.awq_w4a16_matmul(X[:T], dev(packed), dev(scales), dev(zeros), cfg)).copy()
+        b = host(awq.awq_w4a16_matmul(X[:T], dev(packed), dev(scales), dev(zeros), cfg))
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    # a token's result does not depend on the other tokens of the batch (per-column sums)
+    y16 = host(awq.awq_w4a16_matmul(dev(rng.standard_normal((16, 4096)).astype(F16)),
+                                    dev(packed), dev(scales), dev(zeros), cfg))
+    Xb = rng.standard_normal((16, 4096)).astype(F16)
+    yb = host(awq.awq_w4a16_matmul(dev(Xb), dev(packed), dev(scales), dev(zeros), cfg))
+    yb3 = host(awq.awq_w4a16_matmul(dev(Xb[3:5]), dev(packed), dev(scales), dev(zeros), cfg))
+    assert np.array_equal(yb[3:5].view(np.uint16), yb3.view(np.uint16))
+    assert y16.shape == (16, 512)
 
 
 @pytest.mark.parametrize("name,w_bit,g,zp", [("c1", 4, 128, 0), ("q3", 3, 64, 1)])
@@ -160,3 +179,8 @@ def test_w4a16_full_size_sampled_rows(cfg_name):
         y = host(awq.awq_w4a16_matmul(dev(X[:T]), Pd, Sd, Zd, cfg, s=sd))
         _check(y[:, rows], packed[rows], scales[rows], zeros[rows], X[:T], g, s,
                f"{cfg_name} T={T}")
+    X16 = rng.standard_normal((16, K)).astype(F16)
+    for T in (1, 4, 16):                                 # S^-1 folded into x
+        y = host(awq.awq_w4a16_matmul(dev(X16[:T]), Pd, Sd, Zd, cfg))
+        _check(y[:, rows], packed[rows], scales[rows], zeros[rows], X16[:T], g, None,
+               f"{cfg_name} folded T={T}")

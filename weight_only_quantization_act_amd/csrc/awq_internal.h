@@ -76,6 +76,13 @@ struct GemvPlan {
   int threads, rows;  // threads per block (K / 32 rounded up to waves), rows per block
 };
 GemvPlan w4a16_gemv_plan(int64_t M, int64_t K);
+// Folded activations (s == null) and at least this many tokens take the matrix-core kernel.
+#ifndef AWQ_W4A16_MFMA_MIN_T
+#define AWQ_W4A16_MFMA_MIN_T 2
+#endif
+constexpr int kW4a16MfmaMinT = AWQ_W4A16_MFMA_MIN_T;
+int w4a16_mfma_tiles(int64_t M);  // 16-row tiles per wave of the matrix-core kernel
+int w4a16_mfma_waves(int64_t M, int64_t K, int group_size);
 // y [T][M] fp16 = x~ [T][K] times the dequantised packed weights; s may be null.
 hipError_t launch_w4a16_gemv(const uint8_t* codes, const uint16_t* scales,
                              const uint16_t* zeros, const uint16_t* x, const float* s, int T,

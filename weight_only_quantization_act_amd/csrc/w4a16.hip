@@ -251,6 +251,197 @@ hipError_t launch_gemv(const uint8_t* codes, const uint16_t* scales, const uint1
   return hipErrorInvalidValue;
 }
 
+// ---- small batches on the matrix cores ---------------------------------------------
+//
+// For 2..16 tokens the VALU kernel's cost grows with T (16 dot2 per 32 channels per token);
+// here one v_mfma_f32_16x16x32_f16 multiplies 16 rows x 32 channels by up to 16 tokens, so
+// the per-weight work (the nibble decode) does not depend on T.  MFMA 16x16x32 f16 lane
+// layout: A row (l mod 16) with k = 8 (l div 16) + e, B column (l mod 16) with the same k,
+// C row 4 (l div 16) + e, column (l mod 16).
+//   - A = (c - z) of 16 weight rows, exact in fp16 (decoded as in the VALU kernel, pairs
+//     (n, n + 4) of each code word), B = x~ of the tokens (lane column = token; columns
+//     >= T are zero), read from global memory and permuted into the same pair order.
+//   - The 32 k-values of one MFMA are 32 channels of one quantisation group: lane group
+//     q = l div 16 supplies channels q g/4 + 8 u + e of the group for MFMA u, u < g/32.
+//     A group's MFMAs accumulate into their own fp32 tile, which is then multiplied by the
+//     group's step for each row and added to the running fp32 result.
+//   - A wave covers 2 or 4 row tiles (32 or 64 rows), so each B fragment feeds 2 or 4
+//     MFMAs, and a range of groups; the (at most 8) waves of a block split the groups and
+//     their results are added through LDS in a fixed order.  Code words and B fragments of
+//     the next group are loaded while the current group is multiplied.
+//   - Step and zero of the wave's rows are staged per 8 groups in a wave-private LDS slice
+//     (two 2-byte loads per lane per group instead of one per row and MFMA).
+constexpr int kMfmaMaxT = 16;         // tokens per pass
+constexpr int kMfmaStageGroups = 8;   // groups of step/zero staged at once
+constexpr int kMfmaMaxWaves = 8;      // two 8-wave blocks fit a CU at 128 VGPRs
+constexpr int kMfmaTargetWaves = 4096;
+
+// Tile geometry: TILES 16-row tiles per wave (4 when the layer has rows for one block per
+// CU, else 2, for more blocks).  LDS per wave: the staged step and zero, then the
+// wave's result tiles for the cross-wave sum.
+template <int TILES>
+struct MfmaGeo {
+  static constexpr int ROWS = 16 * TILES;  // rows per block
+  static constexpr int STAGE_BYTES = kMfmaStageGroups * ROWS * 4;
+  static constexpr int LDS_PER_WAVE = 2 * STAGE_BYTES + TILES * 64 * 16;
+};
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <int GS, int kMfmaTiles>
+__global__ __launch_bounds__(kMfmaMaxWaves * 64) void k_w4a16_mfma(
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ zeros, const uint16_t* __restrict__ x, int M, int K, int T,
+    uint32_t nib, uint32_t one024, uint16_t* __restrict__ y) {
+  constexpr int WPL = GS / 32;  // code words (8 channels) per lane per group = MFMAs per group
+  using Geo = MfmaGeo<kMfmaTiles>;
+  constexpr int kMfmaRows = Geo::ROWS;
+  constexpr int kMfmaStageBytes = Geo::STAGE_BYTES;
+  constexpr int kMfmaLdsPerWave = Geo::LDS_PER_WAVE;
+  // dynamic LDS, per wave: step (fp32) and (1024 + z) as an fp16 pair per staged group and
+  // row, then the wave's result tiles for the cross-wave sum (kMfmaLdsPerWave bytes)
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float (*st_sh)[kMfmaRows] = (float (*)[kMfmaRows])(lds + (size_t)w * kMfmaLdsPerWave);
+  uint32_t (*zz_sh)[kMfmaRows] =
+      (uint32_t (*)[kMfmaRows])(lds + (size_t)w * kMfmaLdsPerWave + kMfmaStageBytes);
+  auto red = [&](int ww, int tl) -> floatx4* {
+    return (floatx4*)(lds + (size_t)ww * kMfmaLdsPerWave + 2 * kMfmaStageBytes) + tl * 64;
+  };
+  const int ar = lane & 15, q = lane >> 4;
+  const int m0 = blockIdx.x * kMfmaRows;
+  const int G = K / GS;
+  const int g0 = (int)(((long long)G * w) / nw), g1 = (int)(((long long)G * (w + 1)) / nw);
+  uint32_t one024_v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(one024_v) : "s"(one024));
+
+  floatx4 acc[kMfmaTiles];
+#pragma unroll
+  for (int i = 0; i < kMfmaTiles; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const bool tok = ar < T;
+  const uint16_t* xr = x + (size_t)(tok ? ar : 0) * K + q * (GS / 4);
+  const size_t crow = (size_t)(K >> 1);
+
+  // code words of the 4 row tiles and the B fragments of one group
+  struct GroupBufs {
+    uint32_t cw[kMfmaTiles][WPL];
+    half8 bf[WPL];
+  };
+  auto load_group = [&](int j, GroupBufs& gb) {
+#pragma unroll
+    for (int u = 0; u < WPL; ++u) {
+      uint32_t d0 = 0u, d1 = 0u, d2 = 0u, d3 = 0u;
+      if (tok) {
+        const u32x4 r = *(const u32x4*)(xr + (size_t)j * GS + 8 * u);
+        d0 = r[0]; d1 = r[1]; d2 = r[2]; d3 = r[3];
+      }
+      // B in code-word pair order: (c0, c4), (c1, c5), (c2, c6), (c3, c7)
+      const uint32_t p0 = (d0 & 0xffffu) | (d2 << 16), p1 = (d0 >> 16) | (d2 & 0xffff0000u);
+      const uint32_t p2 = (d1 & 0xffffu) | (d3 << 16), p3 = (d1 >> 16) | (d3 & 0xffff0000u);
+      const u32x4 pv = {p0, p1, p2, p3};
+      gb.bf[u] = __builtin_bit_cast(half8, pv);
+    }
+#pragma unroll
+    for (int tl = 0; tl < kMfmaTiles; ++tl) {
+      const int row = m0 + 16 * tl + ar;
+      if (row < M) {
+        const uint8_t* cp = codes + (size_t)row * crow + (size_t)j * (GS / 2) + q * (GS / 8);
+        if constexpr (WPL == 4) {
+          const u32x4 r = *(const u32x4*)cp;
+          gb.cw[tl][0] = r[0]; gb.cw[tl][1] = r[1]; gb.cw[tl][2] = r[2]; gb.cw[tl][3] = r[3];
+        } else if constexpr (WPL == 2) {
+          const uint2 r = *(const uint2*)cp;
+          gb.cw[tl][0] = r.x; gb.cw[tl][1] = r.y;
+        } else {
+          gb.cw[tl][0] = *(const uint32_t*)cp;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < WPL; ++u) gb.cw[tl][u] = 0x88888888u;  // any code; row dropped
+      }
+    }
+  };
+  // step and zero of rows m0 .. m0 + 63 for groups js .. js + ng - 1, into the wave's LDS
+  // slice.  Consecutive lanes take consecutive groups of one row, so a load instruction
+  // touches a few rows' metadata (not 64 rows).  LDS operations of a wave complete in
+  // order, so the slice's previous contents have been read by the time these writes land.
+  auto stage = [&](int js) {
+    const int ng = min(kMfmaStageGroups, g1 - js);
+    for (int idx = lane; idx < kMfmaRows * ng; idx += 64) {
+      const int r = idx / ng, jj = idx - (idx / ng) * ng;
+      const int row = m0 + r;
+      float stv = 0.0f;
+      uint32_t zzv = 0x64006400u;
+      if (row < M) {
+        const size_t gi = (size_t)row * G + js + jj;
+        stv = h2f(scales[gi]);
+        const uint16_t zh = f2h(h2f(zeros[gi]) + 1024.0f);
+        zzv = (uint32_t)zh | ((uint32_t)zh << 16);
+      }
+      st_sh[jj][r] = stv;
+      zz_sh[jj][r] = zzv;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the slice is written
+  };
+  auto compute_group = [&](int j, const GroupBufs& gb) {
+    const int jj = (j - g0) % kMfmaStageGroups;
+#pragma unroll
+    for (int tl = 0; tl < kMfmaTiles; ++tl) {
+      const h2 zz = as_h2(zz_sh[jj][16 * tl + ar]);
+      floatx4 cg = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < WPL; ++u) {
+        h2 dp[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) dp[n] = as_h2(((gb.cw[tl][u] >> (4 * n)) & nib) | one024_v) - zz;
+        const u32x4 av = {__builtin_bit_cast(uint32_t, dp[0]), __builtin_bit_cast(uint32_t, dp[1]),
+                          __builtin_bit_cast(uint32_t, dp[2]), __builtin_bit_cast(uint32_t, dp[3])};
+        cg = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), gb.bf[u], cg,
+                                                   0, 0, 0);
+      }
+      const floatx4 stv = *(const floatx4*)&st_sh[jj][16 * tl + 4 * q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[tl][e] = fmaf(stv[e], cg[e], acc[tl][e]);
+    }
+  };
+  // groups in pairs: while one group is multiplied, the next one's loads are in flight
+  GroupBufs ga, gb2;
+  if (g0 < g1) load_group(g0, ga);
+  for (int j = g0; j < g1; j += 2) {
+    if (j + 1 < g1) load_group(j + 1, gb2);
+    if ((j - g0) % kMfmaStageGroups == 0) stage(j);
+    compute_group(j, ga);
+    if (j + 1 >= g1) break;
+    if (j + 2 < g1) load_group(j + 2, ga);
+    if ((j + 1 - g0) % kMfmaStageGroups == 0) stage(j + 1);
+    compute_group(j + 1, gb2);
+  }
+#pragma unroll
+  for (int tl = 0; tl < kMfmaTiles; ++tl) red(w, tl)[lane] = acc[tl];
+  __syncthreads();
+  // waves added in order; tile tl is summed by lanes of wave tl (or of wave 0 for every
+  // tile when the block has fewer waves than tiles)
+  for (int tl = w; tl < kMfmaTiles; tl += nw) {
+    floatx4 v = red(0, tl)[lane];
+    for (int ww = 1; ww < nw; ++ww) {
+      const floatx4 o = red(ww, tl)[lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += o[e];
+    }
+    if (tok) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + 16 * tl + 4 * q + e;
+        if (row < M) y[(size_t)ar * M + row] = f2h(v[e]);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 GemvPlan w4a16_gemv_plan(int64_t M, int64_t K) {
@@ -268,6 +459,52 @@ GemvPlan w4a16_gemv_plan(int64_t M, int64_t K) {
   return p;
 }
 
+int w4a16_mfma_tiles(int64_t M) {
+  return (M + 63) / 64 >= 256 ? 4 : 2;
+}
+
+int w4a16_mfma_waves(int64_t M, int64_t K, int group_size) {
+  const int rows = 16 * w4a16_mfma_tiles(M);
+  const int64_t blocks = (M + rows - 1) / rows;
+  const int64_t G = K / group_size;
+  int64_t nw = (kMfmaTargetWaves + blocks - 1) / blocks;  // waves in total
+  if (nw > kMfmaMaxWaves) nw = kMfmaMaxWaves;
+  if (nw > G) nw = G;
+  if (nw < 1) nw = 1;
+  return (int)nw;
+}
+
+hipError_t launch_w4a16_mfma(const uint8_t* codes, const uint16_t* scales,
+                             const uint16_t* zeros, const uint16_t* x, int T, int M, int K,
+                             int group_size, uint16_t* y, hipStream_t stream) {
+  if (T <= 0 || M <= 0 || K <= 0) return hipSuccess;
+  const int nw = w4a16_mfma_waves(M, K, group_size);
+  const int tiles = w4a16_mfma_tiles(M);
+  const int blocks = (M + 16 * tiles - 1) / (16 * tiles);
+  for (int t0 = 0; t0 < T; t0 += kMfmaMaxT) {
+    const int tc = T - t0 < kMfmaMaxT ? T - t0 : kMfmaMaxT;
+    const uint16_t* xs = x + (size_t)t0 * K;
+    uint16_t* ys = y + (size_t)t0 * M;
+#define AWQ_MFMA(GS, TL)                                                                  \
+  hipLaunchKernelGGL((k_w4a16_mfma<GS, TL>), dim3(blocks), dim3(nw * 64),                  \
+                     (size_t)nw * MfmaGeo<TL>::LDS_PER_WAVE, stream, codes, scales, zeros, xs, \
+                     M, K, tc, 0x000F000Fu, 0x64006400u, ys)
+    switch (group_size * 8 + tiles) {
+      case 32 * 8 + 2: AWQ_MFMA(32, 2); break;
+      case 32 * 8 + 4: AWQ_MFMA(32, 4); break;
+      case 64 * 8 + 2: AWQ_MFMA(64, 2); break;
+      case 64 * 8 + 4: AWQ_MFMA(64, 4); break;
+      case 128 * 8 + 2: AWQ_MFMA(128, 2); break;
+      case 128 * 8 + 4: AWQ_MFMA(128, 4); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef AWQ_MFMA
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_w4a16_gemv(const uint8_t* codes, const uint16_t* scales,
                              const uint16_t* zeros, const uint16_t* x, const float* s, int T,
                              int M, int K, int group_size, uint16_t* y, hipStream_t stream) {
@@ -276,6 +513,9 @@ hipError_t launch_w4a16_gemv(const uint8_t* codes, const uint16_t* scales,
   int log2g = 0;
   while ((1 << log2g) < group_size) ++log2g;
   if ((1 << log2g) != group_size || group_size < 32) return hipErrorInvalidValue;
+  // S^-1 folded, several tokens: the matrix-core kernel
+  if (s == nullptr && T >= kW4a16MfmaMinT && K > 0)
+    return launch_w4a16_mfma(codes, scales, zeros, x, T, M, K, group_size, y, stream);
   const GemvPlan p = w4a16_gemv_plan(M, K);
   for (int t0 = 0; t0 < T; t0 += kGemvMaxT) {
     const int tc = T - t0 < kGemvMaxT ? T - t0 : kGemvMaxT;
