@@ -115,6 +115,55 @@ def cpu_baseline(layer, alphas, cfg, rows):
                        f"{t2 - t0:.1f} s")}
 
 
+def cpu_oracle_widened(layer, cfg, rows_table=64, rows_clip=8, rows_w4=512):
+    """The oracle (as it stands) timed on the widened rows, each on a bounded sample of the
+    same workload and scaled to it (rows are independent in every one of them)."""
+    import numpy as np
+    from oracle import awq_oracle as O
+    ocfg = O.QConfig(cfg.w_bit, cfg.group_size, cfg.zero_point)
+    W, X = layer.W, layer.X
+    M, K = W.shape
+    out = {}
+
+    def clock(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, (time.perf_counter() - t0) * 1e3
+
+    a, _ = clock(lambda: O.act_stats(X))
+    for name, fn in [("stat_max_abs", lambda: O.act_stat_max_abs(X)),
+                     ("stat_rms_ratio", lambda: O.act_stat_rms_ratio(X)),
+                     ("stat_ema_mean_b512", lambda: O.act_stat_ema_mean(X, 512, 0.9)),
+                     ("threshold_scales", lambda: O.threshold_scales(a, 70.0, 2.0)),
+                     ("hadamard_rotate_X_b128", lambda: O.hadamard_rotate(X, 128))]:
+        _, ms = clock(fn)
+        out[name] = {"ms": ms, "sample": "full input"}
+    table = np.stack([O.threshold_scales(a, p, f) for p in (50.0, 70.0, 85.0, 95.0, 99.0)
+                      for f in (1.5, 2.0, 3.0, 4.0)])
+    _, ms = clock(lambda: O.search_scale_table(W[:rows_table], X, table, ocfg))
+    out["search_scale_table_20_threshold_rows"] = {
+        "ms": ms * M / rows_table,
+        "sample": f"rows 0..{rows_table - 1} of {M}, scaled by {M / rows_table:g}"}
+    s_half = O.scale_family(a, np.array([0.5], np.float32))[0]
+    ratios = np.array([1.0 - 0.025 * k for k in range(20)], np.float32)
+    _, ms = clock(lambda: O.clip_search(W[:rows_clip], X, s_half, ocfg, ratios))
+    out["clip_search_20_ratios"] = {
+        "ms": ms * M / rows_clip, "sample": f"rows 0..{rows_clip - 1} of {M}, scaled by "
+                                             f"{M / rows_clip:g}"}
+    rng = np.random.default_rng(20250)
+    M2, K2, g = 28672, 8192, cfg.group_size
+    pk = rng.integers(0, 256, (rows_w4, K2 // 2), dtype=np.uint8)
+    sc = rng.uniform(0.0005, 0.02, (rows_w4, K2 // g)).astype(np.float16)
+    zr = rng.integers(0, 16, (rows_w4, K2 // g)).astype(np.float16)
+    x16 = rng.standard_normal((16, K2)).astype(np.float16)
+    for T in (1, 4, 16):
+        _, ms = clock(lambda: O.w4a16_matmul(pk, sc, zr, x16[:T], g))
+        out[f"w4a16_{M2}x{K2}_T{T}_folded"] = {
+            "ms": ms * M2 / rows_w4,
+            "sample": f"{rows_w4} of {M2} rows, scaled by {M2 / rows_w4:g}"}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -253,6 +302,8 @@ def main():
         line["calib_copy_bytes"] = {"read": src.numel() * 2, "write": dst.numel() * 2}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layer, alphas, cfg, args.cpu_rows)
+        if not args.no_variants:
+            line["cpu_oracle_widened"] = cpu_oracle_widened(layer, cfg)
     print(json.dumps(line), flush=True)
 
 
