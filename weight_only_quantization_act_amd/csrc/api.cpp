@@ -385,8 +385,9 @@ size_t awq_clip_workspace_bytes(int64_t out_features, int64_t in_features, int64
   if (token_shape(n_tokens, in_features) != AWQ_OK) return 0;
   const size_t kg = (size_t)in_features * cfg->group_size;
   const int splits = awq::gram_splits(n_tokens, in_features, cfg->group_size);
-  return round_up(kg * sizeof(float), kAlign) + round_up((size_t)splits * kg * sizeof(double),
-                                                        kAlign);
+  return 2 * round_up(kg * sizeof(uint16_t), kAlign) +
+         round_up((size_t)(in_features / cfg->group_size) * sizeof(int32_t), kAlign) +
+         round_up((size_t)splits * kg * sizeof(double), kAlign);
 }
 
 int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_features,
@@ -422,17 +423,22 @@ int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_fe
   if (best_out && (st = device_ptr(best_out))) return st;
   if (errors_out && (st = device_ptr(errors_out))) return st;
   const size_t kg = (size_t)K * cfg->group_size;
-  float* G = (float*)workspace;
-  double* partials = (double*)((char*)workspace + round_up(kg * sizeof(float), kAlign));
+  char* ws = (char*)workspace;
+  uint16_t* Ghi = (uint16_t*)ws;
+  uint16_t* Glo = (uint16_t*)(ws + round_up(kg * sizeof(uint16_t), kAlign));
+  int32_t* gexp = (int32_t*)(ws + 2 * round_up(kg * sizeof(uint16_t), kAlign));
+  double* partials = (double*)(ws + 2 * round_up(kg * sizeof(uint16_t), kAlign) +
+                               round_up((size_t)(K / cfg->group_size) * sizeof(int32_t),
+                                        kAlign));
   const int splits = awq::gram_splits(N, K, cfg->group_size);
   if ((st = hip_status(awq::launch_group_gram((const uint16_t*)X, (int)N, (int)K,
-                                              cfg->group_size, splits, partials, G,
-                                              (hipStream_t)stream))))
+                                              cfg->group_size, splits, partials, Ghi, Glo,
+                                              gexp, (hipStream_t)stream))))
     return st;
-  return hip_status(awq::launch_clip_search((const uint16_t*)W, s, G, (int)M, (int)K,
-                                            cfg->w_bit, cfg->group_size, cfg->zero_point, rl,
-                                            n_ratio, clip_out, best_out, errors_out,
-                                            (hipStream_t)stream));
+  return hip_status(awq::launch_clip_search((const uint16_t*)W, s, Ghi, Glo, gexp, (int)M,
+                                            (int)K, cfg->w_bit, cfg->group_size,
+                                            cfg->zero_point, rl, n_ratio, clip_out, best_out,
+                                            errors_out, (hipStream_t)stream));
 }
 
 int awq_set_profile_events(void* gemm_start, void* gemm_stop, void* fq_start, void* fq_stop) {

@@ -57,15 +57,19 @@ constexpr int kMaxClip = 64;
 struct ClipList {
   float v[kMaxClip];
 };
-// Gram matrices of the activation groups: G[j] = X_j^T X_j (fp64 sums, stored fp32),
-// fp32 [K/g][g][g]; partials fp64 [splits][K/g][g][g].
+// Gram matrices of the activation groups: G[j] = X_j^T X_j (fp64 sums over token splits,
+// partials fp64 [splits][K/g][g][g]), stored as G[j] 2^-gexp[j] = Ghi + Glo with Ghi, Glo
+// fp16 [K/g][g][g] and gexp int32 [K/g].
 int gram_splits(int64_t N, int64_t K, int group_size);
 hipError_t launch_group_gram(const uint16_t* X, int N, int K, int group_size, int splits,
-                             double* partials, float* G, hipStream_t stream);
+                             double* partials, uint16_t* Ghi, uint16_t* Glo, int32_t* gexp,
+                             hipStream_t stream);
 // Per (row, group): the group's own output error d^T G_j d for every ratio, the first
 // smallest, its ratio (1 when none is finite); errors (nullable) fp32 [n][M][K/g].
-hipError_t launch_clip_search(const uint16_t* W, const float* s, const float* G, int M, int K,
-                              int w_bit, int group_size, int zero_point, const ClipList& ratios,
+// n_ratio <= 64.
+hipError_t launch_clip_search(const uint16_t* W, const float* s, const uint16_t* Ghi,
+                              const uint16_t* Glo, const int32_t* gexp, int M, int K, int w_bit,
+                              int group_size, int zero_point, const ClipList& ratios,
                               int n_ratio, float* clip_out, int32_t* best_out, float* errors,
                               hipStream_t stream);
 

@@ -14,16 +14,22 @@
 //
 //   k_group_gram   fp64 sums of fp16 products (exact products, fp64 accumulation) over
 //                  token splits, one 64 x 64 (or g x g) tile of one group per block, a
-//                  4 x 4 (2 x 2) register tile per thread; k_gram_reduce adds the splits
-//                  in order and rounds to fp32.
-//   k_clip_search  one block per (group, row range).  A lane owns one (row, ratio) pair:
-//                  it quantises the row's group with its ratio in fp32 exactly as the pack
-//                  does, forms d = (v - Q(v)) / s, and evaluates d^T G d in fp32.  Every
-//                  lane needs the same Gram element at the same time, so G is read with
-//                  scalar loads into SGPRs, which the FMAs take as an operand (an LDS
-//                  broadcast would still return 1 KiB per wave per 16 bytes of G through the
-//                  LDS port and bound the kernel there).  Pairs of one row sit in one wave,
-//                  so the first smallest error is picked through LDS.
+//                  4 x 4 (2 x 2) register tile per thread.
+//   k_gram_split   adds the splits in order, scales the group's matrix by a power of two
+//                  into [2^13, 2^14) and splits it into fp16 hi + lo (G ~ hi + lo to about
+//                  2^-22 relative), with the exponent kept per group.
+//   k_clip_mfma    the quadratic forms on the matrix cores.  A lane pair (l, l ^ 32) owns one
+//                  (row, ratio) pair: it quantises the row's group with its ratio in fp32
+//                  exactly as the pack does, forms d = (v - Q(v)) / s, scales d by a power
+//                  of two into [2^9, 2^10) and splits it into fp16 hi + lo.  Then
+//                  U^T = G D^T comes from v_mfma_f32_32x32x16_f16 in three passes
+//                  (G_hi D_hi + G_hi D_lo + G_lo D_hi; every product is exact in fp32),
+//                  G's 32-row tiles as the A operand (from LDS) and 32 pairs as the B
+//                  operand.  The k-slots of each 16-channel step are permuted so that lane
+//                  half h supplies the channels whose bit 2 is h -- exactly the rows of U^T
+//                  it receives in C -- so e = sum_c U^T[c] d[c] is a lane-local sum plus one
+//                  exchange with the partner lane.  The power-of-two scales are undone
+//                  exactly; the first smallest error per row is picked through LDS.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -110,130 +116,260 @@ __global__ __launch_bounds__(kGramThreads) void k_group_gram(const uint16_t* __r
       out[(size_t)(ta * TS + ty * R + a) * g + tb * TS + tx * R + b] = acc[a][b];
 }
 
-__global__ __launch_bounds__(256) void k_gram_reduce(const double* __restrict__ partials,
-                                                     long long n, int splits,
-                                                     float* __restrict__ G) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  double v = partials[i];
-  for (int sp = 1; sp < splits; ++sp) v += partials[(size_t)sp * n + i];
-  G[i] = (float)v;
+// One block per group: G = sum of the split partials (in order), its largest magnitude,
+// the power of two 2^-ex that brings it into [2^13, 2^14), and the fp16 split of G 2^-ex.
+// A non-finite group keeps ex = 0, and its NaN / inf reaches the errors.
+__global__ __launch_bounds__(256) void k_gram_split(const double* __restrict__ partials,
+                                                    int g, int ngroups, int splits,
+                                                    uint16_t* __restrict__ Ghi,
+                                                    uint16_t* __restrict__ Glo,
+                                                    int32_t* __restrict__ gexp) {
+  __shared__ double mx[256];
+  __shared__ int ex_sh;
+  const int j = blockIdx.x;
+  const int tid = threadIdx.x;
+  const size_t gg = (size_t)g * g;
+  const size_t base = (size_t)j * gg;
+  const size_t stride = (size_t)ngroups * gg;  // one split's partials
+  double m = 0.0;
+  for (size_t i = tid; i < gg; i += 256) {
+    double v = partials[base + i];
+    for (int sp = 1; sp < splits; ++sp) v += partials[sp * stride + base + i];
+    const double a = fabs(v);
+    m = (a > m || a != a) ? a : m;
+  }
+  mx[tid] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) {
+      const double a = mx[tid + o];
+      mx[tid] = (a > mx[tid] || a != a) ? a : mx[tid];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int ex = 0;
+    const double top = mx[0];
+    if (top > 0.0 && top < INFINITY) {
+      int e2;
+      frexp(top, &e2);  // top = f 2^e2, f in [0.5, 1)
+      ex = e2 - 14;     // top 2^-ex in [2^13, 2^14)
+    }
+    ex_sh = ex;
+    gexp[j] = ex;
+  }
+  __syncthreads();
+  const int ex = ex_sh;
+  for (size_t i = tid; i < gg; i += 256) {
+    double v = partials[base + i];
+    for (int sp = 1; sp < splits; ++sp) v += partials[sp * stride + base + i];
+    const float vs = (float)ldexp(v, -ex);
+    const uint16_t hi = f2h(vs);
+    const uint16_t lo = f2h(vs - h2f(hi));
+    Ghi[base + i] = hi;
+    Glo[base + i] = lo;
+  }
 }
 
 constexpr int kClipThreads = 256;
 constexpr int kClipWaves = kClipThreads / 64;
+constexpr int kClipPairs = kClipWaves * 32;  // (row, ratio) pairs per pass of a block
 
-// One (row, ratio) pair per lane; rows_per_wave = 64 / n_ratio rows of pairs per wave.
-// red: [kClipWaves][64] errors of the current pass.
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Block: group j, rows [m_begin, m_end) in passes of kClipPairs / n_ratio rows.  Lane l of
+// wave w: pair 32 w + (l mod 32) of the pass, half h = l div 32, channels 8 b + 4 h + i of the
+// group (b < GS / 8, i < 4).  MFMA k-slot (h, e) of step s is channel 16 s + 4 h + e for
+// e < 4 and 16 s + 8 + 4 h + (e - 4) otherwise, in both operands.
 template <int GS>
-__global__ __launch_bounds__(kClipThreads) void k_clip_search(
-    const uint16_t* __restrict__ W, const float* __restrict__ s_in, const float* __restrict__ G,
-    int M, int K, int w_bit, int zero_point, ClipList ratios, int n_ratio, int rows_per_block,
-    float* __restrict__ clip_out, int32_t* __restrict__ best_out, float* __restrict__ errors) {
+__global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
+    const uint16_t* __restrict__ W, const float* __restrict__ s_in,
+    const uint16_t* __restrict__ Ghi, const uint16_t* __restrict__ Glo,
+    const int32_t* __restrict__ gexp, int M, int K, int w_bit, int zero_point,
+    ClipList ratios, int n_ratio, int rows_per_block, float* __restrict__ clip_out,
+    int32_t* __restrict__ best_out, float* __restrict__ errors) {
+  constexpr int GP = GS + 4;  // padded LDS row (fp16): 8-byte fragment reads hit 32 banks pairs
+  constexpr int KS = GS / 16;
+  constexpr int RT = GS / 32;
+  constexpr int NB = GS / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t gh[GS * GP];
+  __shared__ __attribute__((aligned(16))) uint16_t gl[GS * GP];
   __shared__ float ss[GS], rs[GS];
-  __shared__ float red[kClipWaves][64];
+  __shared__ float esh[kClipPairs];
   const int j = blockIdx.x;
-  const int ngroups = K / GS;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const float* __restrict__ Gj = G + (size_t)j * GS * GS;
+  const int G = K / GS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, pl = lane & 31;
+  const size_t gbase = (size_t)j * GS * GS;
+  for (int i = tid; i < GS * GS / 8; i += kClipThreads) {
+    const int r = i / (GS / 8), c8 = (i - r * (GS / 8)) * 8;
+    const u32x4 a = *(const u32x4*)(Ghi + gbase + (size_t)r * GS + c8);
+    const u32x4 b = *(const u32x4*)(Glo + gbase + (size_t)r * GS + c8);
+    *(uint2*)(gh + r * GP + c8) = make_uint2(a[0], a[1]);
+    *(uint2*)(gh + r * GP + c8 + 4) = make_uint2(a[2], a[3]);
+    *(uint2*)(gl + r * GP + c8) = make_uint2(b[0], b[1]);
+    *(uint2*)(gl + r * GP + c8 + 4) = make_uint2(b[2], b[3]);
+  }
+  __shared__ float rs_max_sh;
   for (int i = tid; i < GS; i += kClipThreads) {
     const float sv = s_in[j * GS + i];
     ss[i] = sv;
     rs[i] = 1.0f / sv;
   }
   __syncthreads();
-
-  const int rows_per_wave = 64 / n_ratio;
-  const int r_local = lane / n_ratio;
-  const int k = lane - r_local * n_ratio;
-  const bool active = r_local < rows_per_wave;
-  const int rows_per_pass = rows_per_wave * kClipWaves;
+  if (tid == 0) {
+    float mx = 0.0f;
+    for (int i = 0; i < GS; ++i) mx = fmaxf(mx, fabsf(rs[i]));
+    rs_max_sh = mx;
+  }
+  __syncthreads();
+  const float rs_max = rs_max_sh;
+  const int ex = gexp[j];
+  const int rows_per_pass = kClipPairs / n_ratio;
+  const int pair = wave * 32 + pl;
+  const int r_local = pair / n_ratio;
+  const int k = pair - r_local * n_ratio;
+  const float rho = ratios.v[k];
+  const bool zp = zero_point != 0;
   const int m_begin = blockIdx.y * rows_per_block;
   const int m_end = min(M, m_begin + rows_per_block);
-  const bool zp = zero_point != 0;
-  const float rho = active ? ratios.v[k] : 1.0f;
 
   for (int p0 = m_begin; p0 < m_end; p0 += rows_per_pass) {
-    const int m = p0 + wave * rows_per_wave + r_local;
-    const bool live = active && m < m_end;
-    float e = 0.0f;
-    if (live) {
-      float d[GS];
-      // scaled weights v = w * s (one rounding, as the pack computes them)
-      const uint16_t* wr = W + (size_t)m * K + (size_t)j * GS;
+    const int m = p0 + r_local;
+    const bool live = r_local < rows_per_pass && m < m_end;
+    // ---- the pair's weight error on the lane's channels ----------------------------------
+    uint2 raw[NB];
+    const uint16_t* wr = W + (size_t)(live ? m : 0) * K + (size_t)j * GS + 4 * h;
 #pragma unroll
-      for (int c = 0; c < GS; c += 8) {
-        const u32x4 raw = *(const u32x4*)(wr + c);
+    for (int b = 0; b < NB; ++b) raw[b] = live ? *(const uint2*)(wr + 8 * b) : make_uint2(0u, 0u);
+    // scaled weights v = w s (one rounding) of block b; s read 4 at a time from LDS
+    auto vblock = [&](int b, float (&v)[4]) {
+      const float4 sv = *(const float4*)&ss[8 * b + 4 * h];
+      v[0] = h2f((uint16_t)(raw[b].x & 0xffffu)) * sv.x;
+      v[1] = h2f((uint16_t)(raw[b].x >> 16)) * sv.y;
+      v[2] = h2f((uint16_t)(raw[b].y & 0xffffu)) * sv.z;
+      v[3] = h2f((uint16_t)(raw[b].y >> 16)) * sv.w;
+    };
+    // the group's step and zero with the range shrunk by rho, as in the pack
+    float hi = -INFINITY, lo = INFINITY;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          d[c + 2 * q] = h2f((uint16_t)(raw[q] & 0xffffu)) * ss[c + 2 * q];
-          d[c + 2 * q + 1] = h2f((uint16_t)(raw[q] >> 16)) * ss[c + 2 * q + 1];
-        }
+    for (int b = 0; b < NB; ++b) {
+      float v[4];
+      vblock(b, v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi = fmaxf(hi, v[i]);
+        lo = fminf(lo, v[i]);
       }
-      // the group's step and zero with the range shrunk by rho, as in the pack
-      float st, z, lo_code, hi_code;
-      if (zp) {
-        float hi = d[0], lo = d[0];
-#pragma unroll
-        for (int i = 1; i < GS; ++i) {
-          hi = fmaxf(hi, d[i]);
-          lo = fminf(lo, d[i]);
-        }
-        hi = fmaxf(hi, 0.0f) * rho;
-        lo = fminf(lo, 0.0f) * rho;
-        const float top = (float)((1 << w_bit) - 1);
-        st = (hi - lo) / top;
-        if (st == 0.0f) st = 1.0f;
-        z = fminf(fmaxf(rintf(-lo / st), 0.0f), top);
-        lo_code = 0.0f;
-        hi_code = top;
-      } else {
-        float mag = fabsf(d[0]);
-#pragma unroll
-        for (int i = 1; i < GS; ++i) mag = fmaxf(mag, fabsf(d[i]));
-        mag *= rho;
-        const float qmax = (float)((1 << (w_bit - 1)) - 1);
-        st = mag / qmax;
-        if (st == 0.0f) st = 1.0f;
-        z = (float)(1 << (w_bit - 1));
-        lo_code = z - qmax;
-        hi_code = z + qmax;
-      }
-      // d = (v - (code - z) * step) / s
-#pragma unroll
-      for (int i = 0; i < GS; ++i) {
-        const float code = fminf(fmaxf(rintf(d[i] / st) + z, lo_code), hi_code);
-        d[i] = (d[i] - (code - z) * st) * rs[i];
-      }
-      // e = d^T G d; row a of G is wave-uniform (scalar loads), d[a + 1] is fetched one
-      // row ahead
-      float da = d[0];
-      for (int a = 0; a < GS; ++a) {
-        const float dn = d[a + 1 < GS ? a + 1 : a];
-        const float* __restrict__ Ga = Gj + a * GS;
-        float u = 0.0f;
-#pragma unroll
-        for (int b = 0; b < GS; ++b) u = fmaf(Ga[b], d[b], u);
-        e = fmaf(da, u, e);
-        da = dn;
-      }
-      if (errors) errors[((size_t)k * M + m) * ngroups + j] = e;
+      if ((b & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the hoisted LDS reads
     }
-    red[wave][lane] = e;
+    hi = fmaxf(hi, __shfl_xor(hi, 32));
+    lo = fminf(lo, __shfl_xor(lo, 32));
+    const float vmax = fmaxf(fabsf(hi), fabsf(lo));
+    float st, z, lo_code, hi_code;
+    if (zp) {
+      const float top = (float)((1 << w_bit) - 1);
+      const float hr = fmaxf(hi, 0.0f) * rho, lr = fminf(lo, 0.0f) * rho;
+      st = (hr - lr) / top;
+      if (st == 0.0f) st = 1.0f;
+      z = fminf(fmaxf(rintf(-lr / st), 0.0f), top);
+      lo_code = 0.0f;
+      hi_code = top;
+    } else {
+      const float qmax = (float)((1 << (w_bit - 1)) - 1);
+      st = vmax * rho / qmax;
+      if (st == 0.0f) st = 1.0f;
+      z = (float)(1 << (w_bit - 1));
+      lo_code = z - qmax;
+      hi_code = z + qmax;
+    }
+    // |d| = |v - Q(v)| / s <= 2 max|v| max(1/s) = bound: scale by 2^kd so that the bound is
+    // below 2^14 (no fp16 overflow; values far below it only lose precision in terms that
+    // contribute little to e), then split d 2^kd into fp16 hi + lo (the B operand).
+    const float bound = 2.0f * vmax * rs_max;
+    int kd = 0;
+    if (bound > 0.0f && bound < INFINITY) {
+      int e2;
+      frexpf(bound, &e2);  // bound = f 2^e2, f in [0.5, 1)
+      kd = 14 - e2;
+    }
+    // k-step sk, dword q = channels of block b = 2 sk + (q >> 1), i = 2 (q & 1) .. + 1
+    uint32_t bhi[KS][4], blo[KS][4];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float v[4], dd[4];
+      vblock(b, v);
+      const float4 rv = *(const float4*)&rs[8 * b + 4 * h];
+      const float r4[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float code = fminf(fmaxf(rintf(v[i] / st) + z, lo_code), hi_code);
+        dd[i] = ldexpf((v[i] - (code - z) * st) * r4[i], kd);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const uint16_t h0 = f2h(dd[i]), h1 = f2h(dd[i + 1]);
+        const uint16_t l0 = f2h(dd[i] - h2f(h0)), l1 = f2h(dd[i + 1] - h2f(h1));
+        bhi[b >> 1][(b & 1) * 2 + (i >> 1)] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        blo[b >> 1][(b & 1) * 2 + (i >> 1)] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one block at a time
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- U^T = G D^T per 32-row tile of G, and e = sum_c U^T[c] d[c] ---------------------
+    float e_lane = 0.0f;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      floatx16 c = {};
+      const uint16_t* rh = gh + (32 * rt + pl) * GP + 4 * h;
+      const uint16_t* rl = gl + (32 * rt + pl) * GP + 4 * h;
+#pragma unroll
+      for (int sk = 0; sk < KS; ++sk) {
+        const uint2 h0 = *(const uint2*)(rh + 16 * sk), h1 = *(const uint2*)(rh + 16 * sk + 8);
+        const uint2 l0 = *(const uint2*)(rl + 16 * sk), l1 = *(const uint2*)(rl + 16 * sk + 8);
+        const u32x4 hv = {h0.x, h0.y, h1.x, h1.y}, lv = {l0.x, l0.y, l1.x, l1.y};
+        const half8 ahi = __builtin_bit_cast(half8, hv), alo = __builtin_bit_cast(half8, lv);
+        const u32x4 bh = {bhi[sk][0], bhi[sk][1], bhi[sk][2], bhi[sk][3]};
+        const u32x4 bl = {blo[sk][0], blo[sk][1], blo[sk][2], blo[sk][3]};
+        const half8 bhv = __builtin_bit_cast(half8, bh), blv = __builtin_bit_cast(half8, bl);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bhv, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, blv, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bhv, c, 0, 0, 0);
+      }
+      // C element i: row (channel) 32 rt + 8 (i div 4) + 4 h + (i mod 4) = channel 8 b + 4 h + i'
+      // of this lane with b = 4 rt + i div 4, i' = i mod 4
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int b = 4 * rt + (i >> 2), ii = i & 3;
+        const uint32_t ph = bhi[b >> 1][(b & 1) * 2 + (ii >> 1)];
+        const uint32_t pq = blo[b >> 1][(b & 1) * 2 + (ii >> 1)];
+        const int sh = (ii & 1) * 16;
+        const float dv = h2f((uint16_t)(ph >> sh)) + h2f((uint16_t)(pq >> sh));
+        e_lane = fmaf(c[i], dv, e_lane);
+      }
+      // one row tile at a time: keeps a single accumulator tile and its fragments live
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    e_lane += __shfl_xor(e_lane, 32);
+    const float e = ldexpf(e_lane, ex - 2 * kd);
+    if (live && h == 0) {
+      esh[pair] = e;
+      if (errors) errors[((size_t)k * M + m) * G + j] = e;
+    }
     __syncthreads();
-    if (live && k == 0) {
+    if (live && h == 0 && k == 0) {
       int best = -1;
       float be = 0.0f;
       for (int q = 0; q < n_ratio; ++q) {
-        const float v = red[wave][r_local * n_ratio + q];
+        const float v = esh[r_local * n_ratio + q];
         if (v == v && fabsf(v) != INFINITY && (best < 0 || v < be)) {
           best = q;
           be = v;
         }
       }
-      clip_out[(size_t)m * ngroups + j] = best >= 0 ? ratios.v[best] : 1.0f;
-      if (best_out) best_out[(size_t)m * ngroups + j] = best;
+      clip_out[(size_t)m * G + j] = best >= 0 ? ratios.v[best] : 1.0f;
+      if (best_out) best_out[(size_t)m * G + j] = best;
     }
     __syncthreads();
   }
@@ -253,7 +389,8 @@ int gram_splits(int64_t N, int64_t K, int group_size) {
 }
 
 hipError_t launch_group_gram(const uint16_t* X, int N, int K, int group_size, int splits,
-                             double* partials, float* G, hipStream_t stream) {
+                             double* partials, uint16_t* Ghi, uint16_t* Glo, int32_t* gexp,
+                             hipStream_t stream) {
   if (K <= 0) return hipSuccess;
   const int ts = group_size < 64 ? group_size : 64;
   const int tiles = (group_size / ts) * (group_size / ts);
@@ -269,28 +406,32 @@ hipError_t launch_group_gram(const uint16_t* X, int N, int K, int group_size, in
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long n = (long long)K * group_size;
-  hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     partials, n, splits, G);
+  hipLaunchKernelGGL(k_gram_split, dim3(K / group_size), dim3(256), 0, stream, partials,
+                     group_size, K / group_size, splits, Ghi, Glo, gexp);
   return hipGetLastError();
 }
 
-hipError_t launch_clip_search(const uint16_t* W, const float* s, const float* G, int M, int K,
-                              int w_bit, int group_size, int zero_point, const ClipList& ratios,
+hipError_t launch_clip_search(const uint16_t* W, const float* s, const uint16_t* Ghi,
+                              const uint16_t* Glo, const int32_t* gexp, int M, int K, int w_bit,
+                              int group_size, int zero_point, const ClipList& ratios,
                               int n_ratio, float* clip_out, int32_t* best_out, float* errors,
                               hipStream_t stream) {
   if (M <= 0 || K <= 0) return hipSuccess;
-  if (n_ratio < 1 || n_ratio > 64) return hipErrorInvalidValue;
-  const int rows_per_pass = (64 / n_ratio) * kClipWaves;
-  // about 4 passes per block, and enough blocks to fill the chip
-  int rows = rows_per_pass * 4;
+  if (n_ratio < 1 || n_ratio > kClipPairs / 2) return hipErrorInvalidValue;
+  const int rows_per_pass = kClipPairs / n_ratio;
+  // about 96 rows per block (the Gram matrix is staged once per block), fewer when the
+  // layer is small, so that the grid still fills the chip
   const int ngroups = K / group_size;
-  while (rows > rows_per_pass && (int64_t)ngroups * ((M + rows - 1) / rows) < 2048)
-    rows -= rows_per_pass;
+  int passes = (96 + rows_per_pass - 1) / rows_per_pass;
+  while (passes > 1 && (int64_t)ngroups * ((M + passes * rows_per_pass - 1) /
+                                           (passes * rows_per_pass)) < 1024)
+    --passes;
+  const int rows = passes * rows_per_pass;
   dim3 grid(ngroups, (M + rows - 1) / rows);
 #define AWQ_CLIP(GS)                                                                        \
-  hipLaunchKernelGGL(k_clip_search<GS>, grid, dim3(kClipThreads), 0, stream, W, s, G, M, K, \
-                     w_bit, zero_point, ratios, n_ratio, rows, clip_out, best_out, errors)
+  hipLaunchKernelGGL(k_clip_mfma<GS>, grid, dim3(kClipThreads), 0, stream, W, s, Ghi, Glo,   \
+                     gexp, M, K, w_bit, zero_point, ratios, n_ratio, rows, clip_out,          \
+                     best_out, errors)
   switch (group_size) {
     case 32: AWQ_CLIP(32); break;
     case 64: AWQ_CLIP(64); break;
