@@ -385,8 +385,9 @@ size_t awq_clip_workspace_bytes(int64_t out_features, int64_t in_features, int64
   if (token_shape(n_tokens, in_features) != AWQ_OK) return 0;
   const size_t kg = (size_t)in_features * cfg->group_size;
   const int splits = awq::gram_splits(n_tokens, in_features, cfg->group_size);
-  return 2 * round_up(kg * sizeof(uint16_t), kAlign) +
-         round_up((size_t)(in_features / cfg->group_size) * sizeof(int32_t), kAlign) +
+  const size_t ng = (size_t)(in_features / cfg->group_size);
+  return 2 * round_up(kg * sizeof(uint16_t), kAlign) + round_up(ng * sizeof(int32_t), kAlign) +
+         round_up(ng * awq::gram_chunks(cfg->group_size) * sizeof(double), kAlign) +
          round_up((size_t)splits * kg * sizeof(double), kAlign);
 }
 
@@ -426,14 +427,17 @@ int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_fe
   char* ws = (char*)workspace;
   uint16_t* Ghi = (uint16_t*)ws;
   uint16_t* Glo = (uint16_t*)(ws + round_up(kg * sizeof(uint16_t), kAlign));
-  int32_t* gexp = (int32_t*)(ws + 2 * round_up(kg * sizeof(uint16_t), kAlign));
-  double* partials = (double*)(ws + 2 * round_up(kg * sizeof(uint16_t), kAlign) +
-                               round_up((size_t)(K / cfg->group_size) * sizeof(int32_t),
-                                        kAlign));
+  const size_t ng = (size_t)(K / cfg->group_size);
+  size_t off = 2 * round_up(kg * sizeof(uint16_t), kAlign);
+  int32_t* gexp = (int32_t*)(ws + off);
+  off += round_up(ng * sizeof(int32_t), kAlign);
+  double* cmax = (double*)(ws + off);
+  off += round_up(ng * awq::gram_chunks(cfg->group_size) * sizeof(double), kAlign);
+  double* partials = (double*)(ws + off);
   const int splits = awq::gram_splits(N, K, cfg->group_size);
   if ((st = hip_status(awq::launch_group_gram((const uint16_t*)X, (int)N, (int)K,
-                                              cfg->group_size, splits, partials, Ghi, Glo,
-                                              gexp, (hipStream_t)stream))))
+                                              cfg->group_size, splits, partials, cmax, Ghi,
+                                              Glo, gexp, (hipStream_t)stream))))
     return st;
   return hip_status(awq::launch_clip_search((const uint16_t*)W, s, Ghi, Glo, gexp, (int)M,
                                             (int)K, cfg->w_bit, cfg->group_size,

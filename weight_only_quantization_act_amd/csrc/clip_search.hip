@@ -15,9 +15,10 @@
 //   k_group_gram   fp64 sums of fp16 products (exact products, fp64 accumulation) over
 //                  token splits, one 64 x 64 (or g x g) tile of one group per block, a
 //                  4 x 4 (2 x 2) register tile per thread.
-//   k_gram_split   adds the splits in order, scales the group's matrix by a power of two
-//                  into [2^13, 2^14) and splits it into fp16 hi + lo (G ~ hi + lo to about
-//                  2^-22 relative), with the exponent kept per group.
+//   k_gram_sum     adds the splits in order (over split 0) and takes per-chunk maxima;
+//   k_gram_split   scales the group's matrix by a power of two into [2^13, 2^14) and
+//                  splits it into fp16 hi + lo (G ~ hi + lo to about 2^-22 relative), with
+//                  the exponent kept per group.
 //   k_clip_mfma    the quadratic forms on the matrix cores.  A lane pair (l, l ^ 32) owns one
 //                  (row, ratio) pair: it quantises the row's group with its ratio in fp32
 //                  exactly as the pack does, forms d = (v - Q(v)) / s, scales d by a power
@@ -116,58 +117,67 @@ __global__ __launch_bounds__(kGramThreads) void k_group_gram(const uint16_t* __r
       out[(size_t)(ta * TS + ty * R + a) * g + tb * TS + tx * R + b] = acc[a][b];
 }
 
-// One block per group: G = sum of the split partials (in order), its largest magnitude,
-// the power of two 2^-ex that brings it into [2^13, 2^14), and the fp16 split of G 2^-ex.
-// A non-finite group keeps ex = 0, and its NaN / inf reaches the errors.
-__global__ __launch_bounds__(256) void k_gram_split(const double* __restrict__ partials,
-                                                    int g, int ngroups, int splits,
-                                                    uint16_t* __restrict__ Ghi,
-                                                    uint16_t* __restrict__ Glo,
-                                                    int32_t* __restrict__ gexp) {
+constexpr int kGramChunk = 1024;  // Gram entries per block of the two passes below
+
+__device__ __forceinline__ double nan_max64(double m, double a) {
+  return (a > m || a != a) ? a : m;
+}
+
+// Pass 1, block (group j, chunk c): G = sum of the split partials in order, written over
+// split 0, and the chunk's largest magnitude (NaN if any entry is NaN).
+__global__ __launch_bounds__(256) void k_gram_sum(double* __restrict__ partials, int g,
+                                                  int ngroups, int splits,
+                                                  double* __restrict__ cmax) {
   __shared__ double mx[256];
-  __shared__ int ex_sh;
-  const int j = blockIdx.x;
+  const int j = blockIdx.x, c = blockIdx.y, nc = gridDim.y;
   const int tid = threadIdx.x;
   const size_t gg = (size_t)g * g;
-  const size_t base = (size_t)j * gg;
+  const size_t base = (size_t)j * gg + (size_t)c * kGramChunk;
   const size_t stride = (size_t)ngroups * gg;  // one split's partials
+  const int n = (int)min((size_t)kGramChunk, gg - (size_t)c * kGramChunk);
   double m = 0.0;
-  for (size_t i = tid; i < gg; i += 256) {
+  for (int i = tid; i < n; i += 256) {
     double v = partials[base + i];
     for (int sp = 1; sp < splits; ++sp) v += partials[sp * stride + base + i];
-    const double a = fabs(v);
-    m = (a > m || a != a) ? a : m;
+    partials[base + i] = v;
+    m = nan_max64(m, fabs(v));
   }
   mx[tid] = m;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) {
-      const double a = mx[tid + o];
-      mx[tid] = (a > mx[tid] || a != a) ? a : mx[tid];
-    }
+    if (tid < o) mx[tid] = nan_max64(mx[tid], mx[tid + o]);
     __syncthreads();
   }
-  if (tid == 0) {
-    int ex = 0;
-    const double top = mx[0];
-    if (top > 0.0 && top < INFINITY) {
-      int e2;
-      frexp(top, &e2);  // top = f 2^e2, f in [0.5, 1)
-      ex = e2 - 14;     // top 2^-ex in [2^13, 2^14)
-    }
-    ex_sh = ex;
-    gexp[j] = ex;
+  if (tid == 0) cmax[(size_t)j * nc + c] = mx[0];
+}
+
+// Pass 2, block (group j, chunk c): the group's largest magnitude from its chunks, the
+// power of two 2^-ex that brings it into [2^13, 2^14), and the fp16 split of G 2^-ex.  A
+// non-finite group keeps ex = 0, and its NaN / inf reaches the errors.
+__global__ __launch_bounds__(256) void k_gram_split(const double* __restrict__ G64, int g,
+                                                    const double* __restrict__ cmax,
+                                                    uint16_t* __restrict__ Ghi,
+                                                    uint16_t* __restrict__ Glo,
+                                                    int32_t* __restrict__ gexp) {
+  const int j = blockIdx.x, c = blockIdx.y, nc = gridDim.y;
+  const int tid = threadIdx.x;
+  double top = 0.0;
+  for (int q = 0; q < nc; ++q) top = nan_max64(top, cmax[(size_t)j * nc + q]);
+  int ex = 0;
+  if (top > 0.0 && top < INFINITY) {
+    int e2;
+    frexp(top, &e2);  // top = f 2^e2, f in [0.5, 1)
+    ex = e2 - 14;     // top 2^-ex in [2^13, 2^14)
   }
-  __syncthreads();
-  const int ex = ex_sh;
-  for (size_t i = tid; i < gg; i += 256) {
-    double v = partials[base + i];
-    for (int sp = 1; sp < splits; ++sp) v += partials[sp * stride + base + i];
-    const float vs = (float)ldexp(v, -ex);
+  if (c == 0 && tid == 0) gexp[j] = ex;
+  const size_t gg = (size_t)g * g;
+  const size_t base = (size_t)j * gg + (size_t)c * kGramChunk;
+  const int n = (int)min((size_t)kGramChunk, gg - (size_t)c * kGramChunk);
+  for (int i = tid; i < n; i += 256) {
+    const float vs = (float)ldexp(G64[base + i], -ex);
     const uint16_t hi = f2h(vs);
-    const uint16_t lo = f2h(vs - h2f(hi));
     Ghi[base + i] = hi;
-    Glo[base + i] = lo;
+    Glo[base + i] = f2h(vs - h2f(hi));
   }
 }
 
@@ -388,9 +398,13 @@ int gram_splits(int64_t N, int64_t K, int group_size) {
   return (int)sp;
 }
 
+int gram_chunks(int group_size) {
+  return (group_size * group_size + kGramChunk - 1) / kGramChunk;
+}
+
 hipError_t launch_group_gram(const uint16_t* X, int N, int K, int group_size, int splits,
-                             double* partials, uint16_t* Ghi, uint16_t* Glo, int32_t* gexp,
-                             hipStream_t stream) {
+                             double* partials, double* cmax, uint16_t* Ghi, uint16_t* Glo,
+                             int32_t* gexp, hipStream_t stream) {
   if (K <= 0) return hipSuccess;
   const int ts = group_size < 64 ? group_size : 64;
   const int tiles = (group_size / ts) * (group_size / ts);
@@ -406,8 +420,14 @@ hipError_t launch_group_gram(const uint16_t* X, int N, int K, int group_size, in
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gram_split, dim3(K / group_size), dim3(256), 0, stream, partials,
-                     group_size, K / group_size, splits, Ghi, Glo, gexp);
+  const int nc = gram_chunks(group_size);
+  dim3 g2(K / group_size, nc);
+  hipLaunchKernelGGL(k_gram_sum, g2, dim3(256), 0, stream, partials, group_size,
+                     K / group_size, splits, cmax);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_gram_split, g2, dim3(256), 0, stream, partials, group_size, cmax, Ghi,
+                     Glo, gexp);
   return hipGetLastError();
 }
 
