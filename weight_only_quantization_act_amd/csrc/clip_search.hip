@@ -35,6 +35,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 #include "awq_internal.h"
 #include "quantizer.h"
 
@@ -183,15 +185,29 @@ __global__ __launch_bounds__(256) void k_gram_split(const double* __restrict__ G
 
 constexpr int kClipThreads = 256;
 constexpr int kClipWaves = kClipThreads / 64;
-constexpr int kClipPairs = kClipWaves * 32;  // (row, ratio) pairs per pass of a block
+constexpr int kClipMaxRows = 160;  // rows of one block (its per-row LDS tables)
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-// Block: group j, rows [m_begin, m_end) in passes of kClipPairs / n_ratio rows.  Lane l of
-// wave w: pair 32 w + (l mod 32) of the pass, half h = l div 32, channels 8 b + 4 h + i of the
-// group (b < GS / 8, i < 4).  MFMA k-slot (h, e) of step s is channel 16 s + 4 h + e for
-// e < 4 and 16 s + 8 + 4 h + (e - 4) otherwise, in both operands.
+// Order-preserving key of a finite error and its ratio index: the smallest key is the
+// smallest error, and among equal errors the first ratio.
+__device__ __forceinline__ unsigned long long clip_key(float e, int k) {
+  const uint32_t u = __float_as_uint(e);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)o << 32) | (uint32_t)k;
+}
+
+// Block: group j and rows [m_begin, m_begin + R).  Its R n_ratio (row, ratio) pairs, row
+// major, are cut into slices of 16; wave w takes slices w, w + 4, ... with no block-wide
+// synchronisation, and each row keeps its first smallest error through an LDS atomic
+// minimum.  In a slice, lane l takes pair 16 slice + (l mod 16) and quarter q = l div 16,
+// which owns the group's channels c with (c >> 2) & 3 == q, i.e. c = 16 b + 4 q + i
+// (b < GS / 16, i < 4).  MFMA 16x16x32 f16 (A row l mod 16, k-slots 8 q + e; B column
+// l mod 16, same k-slots; C column l mod 16, rows 4 q + e): k-slot (q, e) of 32-channel
+// step s is channel 32 s + 16 (e div 4) + 4 q + (e mod 4) in both operands, and the C rows
+// of G's 16-row tile rt are channels 16 rt + 4 q + e -- this lane's own channels, so the
+// epilogue is local.
 template <int GS>
 __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
     const uint16_t* __restrict__ W, const float* __restrict__ s_in,
@@ -199,18 +215,23 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
     const int32_t* __restrict__ gexp, int M, int K, int w_bit, int zero_point,
     ClipList ratios, int n_ratio, int rows_per_block, float* __restrict__ clip_out,
     int32_t* __restrict__ best_out, float* __restrict__ errors) {
-  constexpr int GP = GS + 4;  // padded LDS row (fp16): 8-byte fragment reads hit 32 banks pairs
-  constexpr int KS = GS / 16;
-  constexpr int RT = GS / 32;
-  constexpr int NB = GS / 8;
+  constexpr int GP = GS + 4;  // padded LDS row (fp16) of G
+  constexpr int KS = GS / 32;  // 32-channel k-steps
+  constexpr int RT = GS / 16;  // 16-row tiles of G
+  constexpr int NB = GS / 16;  // 16-channel blocks; a lane owns 4 channels of each
   __shared__ __attribute__((aligned(16))) uint16_t gh[GS * GP];
   __shared__ __attribute__((aligned(16))) uint16_t gl[GS * GP];
-  __shared__ float ss[GS], rs[GS];
-  __shared__ float esh[kClipPairs];
+  __shared__ __attribute__((aligned(16))) float ss[GS];
+  __shared__ __attribute__((aligned(16))) float rs[GS];
+  __shared__ float rng_hi[kClipMaxRows], rng_lo[kClipMaxRows];  // range of v = w s per row
+  __shared__ unsigned long long best_key[kClipMaxRows];
+  __shared__ float rs_max_sh;
   const int j = blockIdx.x;
   const int G = K / GS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, pl = lane & 31;
+  const int q4 = lane >> 4, pl = lane & 15;
+  const int m_begin = blockIdx.y * rows_per_block;
+  const int R = min(M - m_begin, rows_per_block);
   const size_t gbase = (size_t)j * GS * GS;
   for (int i = tid; i < GS * GS / 8; i += kClipThreads) {
     const int r = i / (GS / 8), c8 = (i - r * (GS / 8)) * 8;
@@ -221,78 +242,86 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
     *(uint2*)(gl + r * GP + c8) = make_uint2(b[0], b[1]);
     *(uint2*)(gl + r * GP + c8 + 4) = make_uint2(b[2], b[3]);
   }
-  __shared__ float rs_max_sh;
   for (int i = tid; i < GS; i += kClipThreads) {
     const float sv = s_in[j * GS + i];
     ss[i] = sv;
     rs[i] = 1.0f / sv;
   }
   __syncthreads();
-  if (tid == 0) {
+  // range of the scaled weights v = w s of every row of the block (shared by its ratios),
+  // one thread per row
+  for (int r = tid; r < R; r += kClipThreads) {
+    const uint16_t* w1 = W + (size_t)(m_begin + r) * K + (size_t)j * GS;
+    float hi = -INFINITY, lo = INFINITY;
+#pragma unroll 4
+    for (int c8 = 0; c8 < GS; c8 += 8) {
+      const u32x4 raw = *(const u32x4*)(w1 + c8);
+      const float4 s0 = *(const float4*)&ss[c8], s1 = *(const float4*)&ss[c8 + 4];
+      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = h2f((uint16_t)(raw[i >> 1] >> (16 * (i & 1)))) * sv[i];
+        hi = fmaxf(hi, v);
+        lo = fminf(lo, v);
+      }
+    }
+    rng_hi[r] = hi;
+    rng_lo[r] = lo;
+    best_key[r] = ~0ull;
+  }
+  if (wave == 0) {
     float mx = 0.0f;
-    for (int i = 0; i < GS; ++i) mx = fmaxf(mx, fabsf(rs[i]));
-    rs_max_sh = mx;
+    for (int c = lane; c < GS; c += 64) mx = fmaxf(mx, fabsf(rs[c]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0) rs_max_sh = mx;
   }
   __syncthreads();
   const float rs_max = rs_max_sh;
   const int ex = gexp[j];
-  const int rows_per_pass = kClipPairs / n_ratio;
-  const int pair = wave * 32 + pl;
-  const int r_local = pair / n_ratio;
-  const int k = pair - r_local * n_ratio;
-  const float rho = ratios.v[k];
   const bool zp = zero_point != 0;
-  const int m_begin = blockIdx.y * rows_per_block;
-  const int m_end = min(M, m_begin + rows_per_block);
+  const int P = R * n_ratio;
+  const int slices = (P + 15) / 16;
+  // the lane's raw weights, channels 16 b + 4 q + i of its pair's row (a dead lane past the
+  // last pair reads the last pair's row)
+  uint2 raw[NB];
+  auto load_raw = [&](int sl) {
+    const int rr = min(16 * sl + pl, P - 1) / n_ratio;
+    const uint16_t* wr = W + (size_t)(m_begin + rr) * K + (size_t)j * GS + 4 * q4;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) raw[b] = *(const uint2*)(wr + 16 * b);
+  };
+  if (wave < slices) load_raw(wave);
+  // -1 held in a register, so that d - hi stays one mixed-precision fused multiply-add
+  float neg_one;
+  asm volatile("s_mov_b32 %0, -1.0" : "=s"(neg_one));
 
-  for (int p0 = m_begin; p0 < m_end; p0 += rows_per_pass) {
-    const int m = p0 + r_local;
-    const bool live = r_local < rows_per_pass && m < m_end;
-    // ---- the pair's weight error on the lane's channels ----------------------------------
-    uint2 raw[NB];
-    const uint16_t* wr = W + (size_t)(live ? m : 0) * K + (size_t)j * GS + 4 * h;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) raw[b] = live ? *(const uint2*)(wr + 8 * b) : make_uint2(0u, 0u);
-    // scaled weights v = w s (one rounding) of block b; s read 4 at a time from LDS
-    auto vblock = [&](int b, float (&v)[4]) {
-      const float4 sv = *(const float4*)&ss[8 * b + 4 * h];
-      v[0] = h2f((uint16_t)(raw[b].x & 0xffffu)) * sv.x;
-      v[1] = h2f((uint16_t)(raw[b].x >> 16)) * sv.y;
-      v[2] = h2f((uint16_t)(raw[b].y & 0xffffu)) * sv.z;
-      v[3] = h2f((uint16_t)(raw[b].y >> 16)) * sv.w;
-    };
-    // the group's step and zero with the range shrunk by rho, as in the pack
-    float hi = -INFINITY, lo = INFINITY;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float v[4];
-      vblock(b, v);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hi = fmaxf(hi, v[i]);
-        lo = fminf(lo, v[i]);
-      }
-      if ((b & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the hoisted LDS reads
-    }
-    hi = fmaxf(hi, __shfl_xor(hi, 32));
-    lo = fminf(lo, __shfl_xor(lo, 32));
+  for (int sl = wave; sl < slices; sl += kClipWaves) {
+    const int pair = 16 * sl + pl;
+    const bool live = pair < P;
+    const int pc = live ? pair : P - 1;
+    const int r = pc / n_ratio;
+    const int k = pc - r * n_ratio;
+    const float rho = ratios.v[k];
+    const float hi = rng_hi[r], lo = rng_lo[r];
     const float vmax = fmaxf(fabsf(hi), fabsf(lo));
-    float st, z, lo_code, hi_code;
+    // the group's step and zero with the range shrunk by rho, as in the pack; the code
+    // relative to the zero, c - z, is clamped to [clo, chi]
+    float st, clo, chi;
     if (zp) {
       const float top = (float)((1 << w_bit) - 1);
       const float hr = fmaxf(hi, 0.0f) * rho, lr = fminf(lo, 0.0f) * rho;
       st = (hr - lr) / top;
       if (st == 0.0f) st = 1.0f;
-      z = fminf(fmaxf(rintf(-lr / st), 0.0f), top);
-      lo_code = 0.0f;
-      hi_code = top;
+      const float z = fminf(fmaxf(rintf(-lr / st), 0.0f), top);
+      clo = -z;
+      chi = top - z;
     } else {
       const float qmax = (float)((1 << (w_bit - 1)) - 1);
       st = vmax * rho / qmax;
       if (st == 0.0f) st = 1.0f;
-      z = (float)(1 << (w_bit - 1));
-      lo_code = z - qmax;
-      hi_code = z + qmax;
+      clo = -qmax;
+      chi = qmax;
     }
     // |d| = |v - Q(v)| / s <= 2 max|v| max(1/s) = bound: scale by 2^kd so that the bound is
     // below 2^14 (no fp16 overflow; values far below it only lose precision in terms that
@@ -304,84 +333,106 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
       frexpf(bound, &e2);  // bound = f 2^e2, f in [0.5, 1)
       kd = 14 - e2;
     }
-    // k-step sk, dword q = channels of block b = 2 sk + (q >> 1), i = 2 (q & 1) .. + 1
-    uint32_t bhi[KS][4], blo[KS][4];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float v[4], dd[4];
-      vblock(b, v);
-      const float4 rv = *(const float4*)&rs[8 * b + 4 * h];
+    // rint(v / st) as rint(v * (1/st)), except for a lane with an element whose product lies
+    // within 2^-17 of a half-integer (or is not finite): that lane redoes its elements with
+    // the correctly rounded division.  The two agree for |v / st| <= 16, and beyond that the
+    // clamp gives the same code either way (the argument of the pack's quantiser).  Adding
+    // the integer zero after rounding keeps the pack's tie rule.
+    const float inv = __builtin_amdgcn_rcpf(st);
+    // block b's 4 channels as two dwords of fp16 pairs: hi = d 2^kd rounded toward zero
+    // (two per instruction), lo = the exact remainder rounded toward zero, so that
+    // |hi + lo - d 2^kd| <= 2^-20 |d 2^kd| above the fp16 subnormal range
+    uint32_t bhi[NB][2], blo[NB][2];
+    auto quant_block = [&](int b, bool exact) {
+      const float4 sv = *(const float4*)&ss[16 * b + 4 * q4];
+      const float4 rv = *(const float4*)&rs[16 * b + 4 * q4];
+      const float s4[4] = {sv.x, sv.y, sv.z, sv.w};
       const float r4[4] = {rv.x, rv.y, rv.z, rv.w};
+      const uint32_t wp[2] = {raw[b].x, raw[b].y};
+      float dd[4];
+      bool near = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float code = fminf(fmaxf(rintf(v[i] / st) + z, lo_code), hi_code);
-        dd[i] = ldexpf((v[i] - (code - z) * st) * r4[i], kd);
+        const _Float16 wh = __builtin_bit_cast(_Float16, (uint16_t)(wp[i >> 1] >> (16 * (i & 1))));
+        const float v = fmaf((float)wh, s4[i], 0.0f);  // = w s (a zero's sign is immaterial)
+        const float t = v * inv;
+        float q = rintf(t);
+        const bool nr = !(fabsf(t - q) < 0.5f - kTieBand);
+        if (exact) {
+          if (nr) q = rintf(v / st);
+        } else {
+          near |= nr;
+        }
+        const float cz = __builtin_amdgcn_fmed3f(q, clo, chi);
+        dd[i] = ldexpf(fmaf(-cz, st, v) * r4[i], kd);
       }
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
-        const uint16_t h0 = f2h(dd[i]), h1 = f2h(dd[i + 1]);
-        const uint16_t l0 = f2h(dd[i] - h2f(h0)), l1 = f2h(dd[i + 1] - h2f(h1));
-        bhi[b >> 1][(b & 1) * 2 + (i >> 1)] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        blo[b >> 1][(b & 1) * 2 + (i >> 1)] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        const uint32_t ph = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(dd[i], dd[i + 1]));
+        const _Float16 h0 = __builtin_bit_cast(_Float16, (uint16_t)(ph & 0xffffu));
+        const _Float16 h1 = __builtin_bit_cast(_Float16, (uint16_t)(ph >> 16));
+        const float l0 = fmaf((float)h0, neg_one, dd[i]), l1 = fmaf((float)h1, neg_one, dd[i + 1]);
+        bhi[b][i >> 1] = ph;
+        blo[b][i >> 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(l0, l1));
       }
-      __builtin_amdgcn_sched_barrier(0);  // one block at a time
+      return near;
+    };
+    bool need = false;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) need |= quant_block(b, false);
+    if (need && live) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) quant_block(b, true);
     }
+    // the next slice's weights load during this slice's matrix phase
+    if (sl + kClipWaves < slices) load_raw(sl + kClipWaves);
     __builtin_amdgcn_sched_barrier(0);
-    // ---- U^T = G D^T per 32-row tile of G, and e = sum_c U^T[c] d[c] ---------------------
+    // ---- U^T = G D^T per 16-row tile of G, and e = sum_c U^T[c] d[c] ---------------------
     float e_lane = 0.0f;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      floatx16 c = {};
-      const uint16_t* rh = gh + (32 * rt + pl) * GP + 4 * h;
-      const uint16_t* rl = gl + (32 * rt + pl) * GP + 4 * h;
+      floatx4 c = {};
+      const uint16_t* rh = gh + (16 * rt + pl) * GP + 4 * q4;
+      const uint16_t* rl = gl + (16 * rt + pl) * GP + 4 * q4;
 #pragma unroll
       for (int sk = 0; sk < KS; ++sk) {
-        const uint2 h0 = *(const uint2*)(rh + 16 * sk), h1 = *(const uint2*)(rh + 16 * sk + 8);
-        const uint2 l0 = *(const uint2*)(rl + 16 * sk), l1 = *(const uint2*)(rl + 16 * sk + 8);
+        // k-slots e < 4: channel 32 sk + 4 q + e (block 2 sk); e >= 4: 32 sk + 16 + 4 q + e - 4
+        const uint2 h0 = *(const uint2*)(rh + 32 * sk), h1 = *(const uint2*)(rh + 32 * sk + 16);
+        const uint2 l0 = *(const uint2*)(rl + 32 * sk), l1 = *(const uint2*)(rl + 32 * sk + 16);
         const u32x4 hv = {h0.x, h0.y, h1.x, h1.y}, lv = {l0.x, l0.y, l1.x, l1.y};
         const half8 ahi = __builtin_bit_cast(half8, hv), alo = __builtin_bit_cast(half8, lv);
-        const u32x4 bh = {bhi[sk][0], bhi[sk][1], bhi[sk][2], bhi[sk][3]};
-        const u32x4 bl = {blo[sk][0], blo[sk][1], blo[sk][2], blo[sk][3]};
+        const u32x4 bh = {bhi[2 * sk][0], bhi[2 * sk][1], bhi[2 * sk + 1][0], bhi[2 * sk + 1][1]};
+        const u32x4 bl = {blo[2 * sk][0], blo[2 * sk][1], blo[2 * sk + 1][0], blo[2 * sk + 1][1]};
         const half8 bhv = __builtin_bit_cast(half8, bh), blv = __builtin_bit_cast(half8, bl);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bhv, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, blv, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bhv, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhv, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blv, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhv, c, 0, 0, 0);
       }
-      // C element i: row (channel) 32 rt + 8 (i div 4) + 4 h + (i mod 4) = channel 8 b + 4 h + i'
-      // of this lane with b = 4 rt + i div 4, i' = i mod 4
+      // C element e: row 16 rt + 4 q + e = channel of block rt, i = e of this lane
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int b = 4 * rt + (i >> 2), ii = i & 3;
-        const uint32_t ph = bhi[b >> 1][(b & 1) * 2 + (ii >> 1)];
-        const uint32_t pq = blo[b >> 1][(b & 1) * 2 + (ii >> 1)];
-        const int sh = (ii & 1) * 16;
-        const float dv = h2f((uint16_t)(ph >> sh)) + h2f((uint16_t)(pq >> sh));
-        e_lane = fmaf(c[i], dv, e_lane);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t ph = bhi[rt][e >> 1], pq = blo[rt][e >> 1];
+        const int sh = (e & 1) * 16;
+        const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(ph >> sh));
+        const _Float16 dl = __builtin_bit_cast(_Float16, (uint16_t)(pq >> sh));
+        e_lane = fmaf(c[e], (float)dl, fmaf(c[e], (float)dh, e_lane));
       }
-      // one row tile at a time: keeps a single accumulator tile and its fragments live
-      __builtin_amdgcn_sched_barrier(0);
     }
+    e_lane += __shfl_xor(e_lane, 16);
     e_lane += __shfl_xor(e_lane, 32);
-    const float e = ldexpf(e_lane, ex - 2 * kd);
-    if (live && h == 0) {
-      esh[pair] = e;
-      if (errors) errors[((size_t)k * M + m) * G + j] = e;
+    const float e = ldexpf(e_lane, ex - 2 * kd) + 0.0f;  // (+0 turns a -0 into +0)
+    if (live && q4 == 0) {
+      if (errors) errors[((size_t)k * M + m_begin + r) * G + j] = e;
+      if (fabsf(e) < INFINITY) atomicMin(&best_key[r], clip_key(e, k));
     }
-    __syncthreads();
-    if (live && h == 0 && k == 0) {
-      int best = -1;
-      float be = 0.0f;
-      for (int q = 0; q < n_ratio; ++q) {
-        const float v = esh[r_local * n_ratio + q];
-        if (v == v && fabsf(v) != INFINITY && (best < 0 || v < be)) {
-          best = q;
-          be = v;
-        }
-      }
-      clip_out[(size_t)m * G + j] = best >= 0 ? ratios.v[best] : 1.0f;
-      if (best_out) best_out[(size_t)m * G + j] = best;
-    }
-    __syncthreads();
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += kClipThreads) {
+    const unsigned long long key = best_key[r];
+    const int best = key == ~0ull ? -1 : (int)(uint32_t)key;
+    const size_t o = (size_t)(m_begin + r) * G + j;
+    clip_out[o] = best >= 0 ? ratios.v[best] : 1.0f;
+    if (best_out) best_out[o] = best;
   }
 }
 
@@ -437,16 +488,45 @@ hipError_t launch_clip_search(const uint16_t* W, const float* s, const uint16_t*
                               int n_ratio, float* clip_out, int32_t* best_out, float* errors,
                               hipStream_t stream) {
   if (M <= 0 || K <= 0) return hipSuccess;
-  if (n_ratio < 1 || n_ratio > kClipPairs / 2) return hipErrorInvalidValue;
-  const int rows_per_pass = kClipPairs / n_ratio;
-  // about 96 rows per block (the Gram matrix is staged once per block), fewer when the
-  // layer is small, so that the grid still fills the chip
+  if (n_ratio < 1 || n_ratio > kMaxClip) return hipErrorInvalidValue;
+  const void* fn;
+  switch (group_size) {
+    case 32: fn = (const void*)k_clip_mfma<32>; break;
+    case 64: fn = (const void*)k_clip_mfma<64>; break;
+    case 128: fn = (const void*)k_clip_mfma<128>; break;
+    default: return hipErrorInvalidValue;
+  }
+  // rows per block: the fewest rounds of resident blocks times the work of one block
+  // (its slices per wave plus about two slices' worth of staging)
+  // (resident blocks per device, queried once per group size: one kind of device assumed)
+  static std::atomic<int64_t> cap_cache[3];
+  const int gi = group_size == 32 ? 0 : group_size == 64 ? 1 : 2;
+  int64_t cap = cap_cache[gi].load(std::memory_order_relaxed);
+  if (cap <= 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t st = hipGetDevice(&dev);
+    if (st == hipSuccess)
+      st = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (st == hipSuccess)
+      st = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kClipThreads, 0);
+    if (st != hipSuccess) return st;
+    cap = (int64_t)max(1, cus) * max(1, per_cu);
+    cap_cache[gi].store(cap, std::memory_order_relaxed);
+  }
   const int ngroups = K / group_size;
-  int passes = (96 + rows_per_pass - 1) / rows_per_pass;
-  while (passes > 1 && (int64_t)ngroups * ((M + passes * rows_per_pass - 1) /
-                                           (passes * rows_per_pass)) < 1024)
-    --passes;
-  const int rows = passes * rows_per_pass;
+  int rows = 1;
+  int64_t best_cost = -1;
+  for (int r = 1; r <= kClipMaxRows; ++r) {
+    const int64_t blocks = (int64_t)ngroups * ((M + r - 1) / r);
+    const int64_t rounds = (blocks + cap - 1) / cap;
+    const int64_t per_wave = ((int64_t)min(r, M) * n_ratio + 16 * kClipWaves - 1) /
+                             (16 * kClipWaves);
+    const int64_t cost = rounds * (per_wave + 2);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      rows = r;
+    }
+  }
   dim3 grid(ngroups, (M + rows - 1) / rows);
 #define AWQ_CLIP(GS)                                                                        \
   hipLaunchKernelGGL(k_clip_mfma<GS>, grid, dim3(kClipThreads), 0, stream, W, s, Ghi, Glo,   \
@@ -455,8 +535,7 @@ hipError_t launch_clip_search(const uint16_t* W, const float* s, const uint16_t*
   switch (group_size) {
     case 32: AWQ_CLIP(32); break;
     case 64: AWQ_CLIP(64); break;
-    case 128: AWQ_CLIP(128); break;
-    default: return hipErrorInvalidValue;
+    default: AWQ_CLIP(128); break;
   }
 #undef AWQ_CLIP
   return hipGetLastError();
