@@ -233,10 +233,23 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
   const int m_begin = blockIdx.y * rows_per_block;
   const int R = min(M - m_begin, rows_per_block);
   const size_t gbase = (size_t)j * GS * GS;
+  // G' in LDS: G's 16 x 16 blocks above the diagonal doubled (exact), those below zero, so
+  // that d^T G d = sum over row tiles rt of d_rt^T (G' d)_rt and a row tile only needs the
+  // k-steps from its own diagonal block on
   for (int i = tid; i < GS * GS / 8; i += kClipThreads) {
     const int r = i / (GS / 8), c8 = (i - r * (GS / 8)) * 8;
-    const u32x4 a = *(const u32x4*)(Ghi + gbase + (size_t)r * GS + c8);
-    const u32x4 b = *(const u32x4*)(Glo + gbase + (size_t)r * GS + c8);
+    u32x4 a = *(const u32x4*)(Ghi + gbase + (size_t)r * GS + c8);
+    u32x4 b = *(const u32x4*)(Glo + gbase + (size_t)r * GS + c8);
+    if (c8 / 16 < r / 16) {
+      a = u32x4{0u, 0u, 0u, 0u};
+      b = a;
+    } else if (c8 / 16 > r / 16) {
+      half8 ah = __builtin_bit_cast(half8, a), bh = __builtin_bit_cast(half8, b);
+      ah = ah + ah;
+      bh = bh + bh;
+      a = __builtin_bit_cast(u32x4, ah);
+      b = __builtin_bit_cast(u32x4, bh);
+    }
     *(uint2*)(gh + r * GP + c8) = make_uint2(a[0], a[1]);
     *(uint2*)(gh + r * GP + c8 + 4) = make_uint2(a[2], a[3]);
     *(uint2*)(gl + r * GP + c8) = make_uint2(b[0], b[1]);
@@ -395,7 +408,7 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
       const uint16_t* rh = gh + (16 * rt + pl) * GP + 4 * q4;
       const uint16_t* rl = gl + (16 * rt + pl) * GP + 4 * q4;
 #pragma unroll
-      for (int sk = 0; sk < KS; ++sk) {
+      for (int sk = rt / 2; sk < KS; ++sk) {
         // k-slots e < 4: channel 32 sk + 4 q + e (block 2 sk); e >= 4: 32 sk + 16 + 4 q + e - 4
         const uint2 h0 = *(const uint2*)(rh + 32 * sk), h1 = *(const uint2*)(rh + 32 * sk + 16);
         const uint2 l0 = *(const uint2*)(rl + 32 * sk), l1 = *(const uint2*)(rl + 32 * sk + 16);
