@@ -186,6 +186,10 @@ __global__ __launch_bounds__(256) void k_gram_split(const double* __restrict__ G
 constexpr int kClipThreads = 256;
 constexpr int kClipWaves = kClipThreads / 64;
 constexpr int kClipMaxRows = 160;  // rows of one block (its per-row LDS tables)
+#ifndef AWQ_CLIP_SLICES
+#define AWQ_CLIP_SLICES 2
+#endif
+constexpr int kClipSlices = AWQ_CLIP_SLICES;  // 16-pair slices sharing one read of G's tiles
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -208,7 +212,7 @@ __device__ __forceinline__ unsigned long long clip_key(float e, int k) {
 // step s is channel 32 s + 16 (e div 4) + 4 q + (e mod 4) in both operands, and the C rows
 // of G's 16-row tile rt are channels 16 rt + 4 q + e -- this lane's own channels, so the
 // epilogue is local.
-template <int GS>
+template <int GS, int NS>
 __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
     const uint16_t* __restrict__ W, const float* __restrict__ s_in,
     const uint16_t* __restrict__ Ghi, const uint16_t* __restrict__ Glo,
@@ -295,116 +299,137 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
   const bool zp = zero_point != 0;
   const int P = R * n_ratio;
   const int slices = (P + 15) / 16;
-  // the lane's raw weights, channels 16 b + 4 q + i of its pair's row (a dead lane past the
-  // last pair reads the last pair's row)
-  uint2 raw[NB];
-  auto load_raw = [&](int sl) {
-    const int rr = min(16 * sl + pl, P - 1) / n_ratio;
-    const uint16_t* wr = W + (size_t)(m_begin + rr) * K + (size_t)j * GS + 4 * q4;
+  const int sgroups = (slices + NS - 1) / NS;  // a wave takes NS consecutive slices at once
+  // the lane's raw weights, channels 16 b + 4 q + i of the row of each of its NS pairs (a
+  // dead lane past the last pair reads the last pair's row)
+  uint2 raw[NS][NB];
+  auto load_raw = [&](int sg) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) raw[b] = *(const uint2*)(wr + 16 * b);
+    for (int u = 0; u < NS; ++u) {
+      const int rr = min(16 * (sg * NS + u) + pl, P - 1) / n_ratio;
+      const uint16_t* wr = W + (size_t)(m_begin + rr) * K + (size_t)j * GS + 4 * q4;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) raw[u][b] = *(const uint2*)(wr + 16 * b);
+    }
   };
-  if (wave < slices) load_raw(wave);
+  if (wave < sgroups) load_raw(wave);
   // -1 held in a register, so that d - hi stays one mixed-precision fused multiply-add
   float neg_one;
   asm volatile("s_mov_b32 %0, -1.0" : "=s"(neg_one));
 
-  for (int sl = wave; sl < slices; sl += kClipWaves) {
-    const int pair = 16 * sl + pl;
-    const bool live = pair < P;
-    const int pc = live ? pair : P - 1;
-    const int r = pc / n_ratio;
-    const int k = pc - r * n_ratio;
-    const float rho = ratios.v[k];
-    const float hi = rng_hi[r], lo = rng_lo[r];
-    const float vmax = fmaxf(fabsf(hi), fabsf(lo));
-    // the group's step and zero with the range shrunk by rho, as in the pack; the code
-    // relative to the zero, c - z, is clamped to [clo, chi]
-    float st, clo, chi;
-    if (zp) {
-      const float top = (float)((1 << w_bit) - 1);
-      const float hr = fmaxf(hi, 0.0f) * rho, lr = fminf(lo, 0.0f) * rho;
-      st = (hr - lr) / top;
-      if (st == 0.0f) st = 1.0f;
-      const float z = fminf(fmaxf(rintf(-lr / st), 0.0f), top);
-      clo = -z;
-      chi = top - z;
-    } else {
-      const float qmax = (float)((1 << (w_bit - 1)) - 1);
-      st = vmax * rho / qmax;
-      if (st == 0.0f) st = 1.0f;
-      clo = -qmax;
-      chi = qmax;
-    }
-    // |d| = |v - Q(v)| / s <= 2 max|v| max(1/s) = bound: scale by 2^kd so that the bound is
-    // below 2^14 (no fp16 overflow; values far below it only lose precision in terms that
-    // contribute little to e), then split d 2^kd into fp16 hi + lo (the B operand).
-    const float bound = 2.0f * vmax * rs_max;
-    int kd = 0;
-    if (bound > 0.0f && bound < INFINITY) {
-      int e2;
-      frexpf(bound, &e2);  // bound = f 2^e2, f in [0.5, 1)
-      kd = 14 - e2;
-    }
-    // rint(v / st) as rint(v * (1/st)), except for a lane with an element whose product lies
-    // within 2^-17 of a half-integer (or is not finite): that lane redoes its elements with
-    // the correctly rounded division.  The two agree for |v / st| <= 16, and beyond that the
-    // clamp gives the same code either way (the argument of the pack's quantiser).  Adding
-    // the integer zero after rounding keeps the pack's tie rule.
-    const float inv = __builtin_amdgcn_rcpf(st);
-    // block b's 4 channels as two dwords of fp16 pairs: hi = d 2^kd rounded toward zero
-    // (two per instruction), lo = the exact remainder rounded toward zero, so that
-    // |hi + lo - d 2^kd| <= 2^-20 |d 2^kd| above the fp16 subnormal range
-    uint32_t bhi[NB][2], blo[NB][2];
-    auto quant_block = [&](int b, bool exact) {
-      const float4 sv = *(const float4*)&ss[16 * b + 4 * q4];
-      const float4 rv = *(const float4*)&rs[16 * b + 4 * q4];
-      const float s4[4] = {sv.x, sv.y, sv.z, sv.w};
-      const float r4[4] = {rv.x, rv.y, rv.z, rv.w};
-      const uint32_t wp[2] = {raw[b].x, raw[b].y};
-      float dd[4];
-      bool near = false;
+  for (int sg = wave; sg < sgroups; sg += kClipWaves) {
+    // B operands of the NS pairs: block b's 4 channels as two dwords of fp16 pairs,
+    // hi = d 2^kd rounded toward zero (two per instruction) and lo = the exact remainder
+    // rounded toward zero, so that |hi + lo - d 2^kd| <= 2^-20 |d 2^kd| above the fp16
+    // subnormal range
+    uint32_t bhi[NS][NB][2], blo[NS][NB][2];
+    int kdv[NS], rv_[NS], kv[NS];
+    bool livev[NS];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const _Float16 wh = __builtin_bit_cast(_Float16, (uint16_t)(wp[i >> 1] >> (16 * (i & 1))));
-        const float v = fmaf((float)wh, s4[i], 0.0f);  // = w s (a zero's sign is immaterial)
-        const float t = v * inv;
-        float q = rintf(t);
-        const bool nr = !(fabsf(t - q) < 0.5f - kTieBand);
-        if (exact) {
-          if (nr) q = rintf(v / st);
-        } else {
-          near |= nr;
+    for (int u = 0; u < NS; ++u) {
+      const int pair = 16 * (sg * NS + u) + pl;
+      const bool live = pair < P;
+      const int pc = live ? pair : P - 1;
+      const int r = pc / n_ratio;
+      const int k = pc - r * n_ratio;
+      const float rho = ratios.v[k];
+      const float hi = rng_hi[r], lo = rng_lo[r];
+      const float vmax = fmaxf(fabsf(hi), fabsf(lo));
+      // the group's step and zero with the range shrunk by rho, as in the pack; the code
+      // relative to the zero, c - z, is clamped to [clo, chi]
+      float st, clo, chi;
+      if (zp) {
+        const float top = (float)((1 << w_bit) - 1);
+        const float hr = fmaxf(hi, 0.0f) * rho, lr = fminf(lo, 0.0f) * rho;
+        st = (hr - lr) / top;
+        if (st == 0.0f) st = 1.0f;
+        const float z = fminf(fmaxf(rintf(-lr / st), 0.0f), top);
+        clo = -z;
+        chi = top - z;
+      } else {
+        const float qmax = (float)((1 << (w_bit - 1)) - 1);
+        st = vmax * rho / qmax;
+        if (st == 0.0f) st = 1.0f;
+        clo = -qmax;
+        chi = qmax;
+      }
+      // |d| = |v - Q(v)| / s <= 2 max|v| max(1/s) = bound: scale by 2^kd so that the bound
+      // is below 2^14 (no fp16 overflow; values far below it only lose precision in terms
+      // that contribute little to e), then split d 2^kd into fp16 hi + lo
+      const float bound = 2.0f * vmax * rs_max;
+      int kd = 0;
+      if (bound > 0.0f && bound < INFINITY) {
+        int e2;
+        frexpf(bound, &e2);  // bound = f 2^e2, f in [0.5, 1)
+        kd = 14 - e2;
+      }
+      // rint(v / st) as rint(v * (1/st)), except for a lane with an element whose product
+      // lies within 2^-17 of a half-integer (or is not finite): that lane redoes its
+      // elements with the correctly rounded division.  The two agree for |v / st| <= 16, and
+      // beyond that the clamp gives the same code either way (the argument of the pack's
+      // quantiser).  Adding the integer zero after rounding keeps the pack's tie rule.
+      const float inv = __builtin_amdgcn_rcpf(st);
+      auto quant_block = [&](int b, bool exact) {
+        const float4 sv = *(const float4*)&ss[16 * b + 4 * q4];
+        const float4 rv = *(const float4*)&rs[16 * b + 4 * q4];
+        const float s4[4] = {sv.x, sv.y, sv.z, sv.w};
+        const float r4[4] = {rv.x, rv.y, rv.z, rv.w};
+        const uint32_t wp[2] = {raw[u][b].x, raw[u][b].y};
+        float dd[4];
+        bool near = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const _Float16 wh =
+              __builtin_bit_cast(_Float16, (uint16_t)(wp[i >> 1] >> (16 * (i & 1))));
+          const float v = fmaf((float)wh, s4[i], 0.0f);  // = w s (a zero's sign is immaterial)
+          const float t = v * inv;
+          float q = rintf(t);
+          const bool nr = !(fabsf(t - q) < 0.5f - kTieBand);
+          if (exact) {
+            if (nr) q = rintf(v / st);
+          } else {
+            near |= nr;
+          }
+          const float cz = __builtin_amdgcn_fmed3f(q, clo, chi);
+          dd[i] = ldexpf(fmaf(-cz, st, v) * r4[i], kd);
         }
-        const float cz = __builtin_amdgcn_fmed3f(q, clo, chi);
-        dd[i] = ldexpf(fmaf(-cz, st, v) * r4[i], kd);
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const uint32_t ph =
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(dd[i], dd[i + 1]));
+          const _Float16 h0 = __builtin_bit_cast(_Float16, (uint16_t)(ph & 0xffffu));
+          const _Float16 h1 = __builtin_bit_cast(_Float16, (uint16_t)(ph >> 16));
+          const float l0 = fmaf((float)h0, neg_one, dd[i]);
+          const float l1 = fmaf((float)h1, neg_one, dd[i + 1]);
+          bhi[u][b][i >> 1] = ph;
+          blo[u][b][i >> 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(l0, l1));
+        }
+        return near;
+      };
+      bool need = false;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) need |= quant_block(b, false);
+      if (need && live) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) quant_block(b, true);
       }
-#pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const uint32_t ph = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(dd[i], dd[i + 1]));
-        const _Float16 h0 = __builtin_bit_cast(_Float16, (uint16_t)(ph & 0xffffu));
-        const _Float16 h1 = __builtin_bit_cast(_Float16, (uint16_t)(ph >> 16));
-        const float l0 = fmaf((float)h0, neg_one, dd[i]), l1 = fmaf((float)h1, neg_one, dd[i + 1]);
-        bhi[b][i >> 1] = ph;
-        blo[b][i >> 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(l0, l1));
-      }
-      return near;
-    };
-    bool need = false;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) need |= quant_block(b, false);
-    if (need && live) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) quant_block(b, true);
+      kdv[u] = kd;
+      rv_[u] = r;
+      kv[u] = k;
+      livev[u] = live;
     }
-    // the next slice's weights load during this slice's matrix phase
-    if (sl + kClipWaves < slices) load_raw(sl + kClipWaves);
+    // the next slices' weights load during this group's matrix phase
+    if (sg + kClipWaves < sgroups) load_raw(sg + kClipWaves);
     __builtin_amdgcn_sched_barrier(0);
-    // ---- U^T = G D^T per 16-row tile of G, and e = sum_c U^T[c] d[c] ---------------------
-    float e_lane = 0.0f;
+    // ---- U^T = G' D^T per 16-row tile of G', and e = sum_c U^T[c] d[c] -------------------
+    float e_lane[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) e_lane[u] = 0.0f;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      floatx4 c = {};
+      floatx4 c[NS];
+#pragma unroll
+      for (int u = 0; u < NS; ++u) c[u] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
       const uint16_t* rh = gh + (16 * rt + pl) * GP + 4 * q4;
       const uint16_t* rl = gl + (16 * rt + pl) * GP + 4 * q4;
 #pragma unroll
@@ -414,29 +439,41 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
         const uint2 l0 = *(const uint2*)(rl + 32 * sk), l1 = *(const uint2*)(rl + 32 * sk + 16);
         const u32x4 hv = {h0.x, h0.y, h1.x, h1.y}, lv = {l0.x, l0.y, l1.x, l1.y};
         const half8 ahi = __builtin_bit_cast(half8, hv), alo = __builtin_bit_cast(half8, lv);
-        const u32x4 bh = {bhi[2 * sk][0], bhi[2 * sk][1], bhi[2 * sk + 1][0], bhi[2 * sk + 1][1]};
-        const u32x4 bl = {blo[2 * sk][0], blo[2 * sk][1], blo[2 * sk + 1][0], blo[2 * sk + 1][1]};
-        const half8 bhv = __builtin_bit_cast(half8, bh), blv = __builtin_bit_cast(half8, bl);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhv, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blv, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhv, c, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          const u32x4 bh = {bhi[u][2 * sk][0], bhi[u][2 * sk][1], bhi[u][2 * sk + 1][0],
+                            bhi[u][2 * sk + 1][1]};
+          const u32x4 bl = {blo[u][2 * sk][0], blo[u][2 * sk][1], blo[u][2 * sk + 1][0],
+                            blo[u][2 * sk + 1][1]};
+          const half8 bhv = __builtin_bit_cast(half8, bh), blv = __builtin_bit_cast(half8, bl);
+          c[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhv, c[u], 0, 0, 0);
+          c[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blv, c[u], 0, 0, 0);
+          c[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhv, c[u], 0, 0, 0);
+        }
       }
       // C element e: row 16 rt + 4 q + e = channel of block rt, i = e of this lane
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t ph = bhi[rt][e >> 1], pq = blo[rt][e >> 1];
-        const int sh = (e & 1) * 16;
-        const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(ph >> sh));
-        const _Float16 dl = __builtin_bit_cast(_Float16, (uint16_t)(pq >> sh));
-        e_lane = fmaf(c[e], (float)dl, fmaf(c[e], (float)dh, e_lane));
+      for (int u = 0; u < NS; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t ph = bhi[u][rt][e >> 1], pq = blo[u][rt][e >> 1];
+          const int sh = (e & 1) * 16;
+          const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(ph >> sh));
+          const _Float16 dl = __builtin_bit_cast(_Float16, (uint16_t)(pq >> sh));
+          e_lane[u] = fmaf(c[u][e], (float)dl, fmaf(c[u][e], (float)dh, e_lane[u]));
+        }
       }
     }
-    e_lane += __shfl_xor(e_lane, 16);
-    e_lane += __shfl_xor(e_lane, 32);
-    const float e = ldexpf(e_lane, ex - 2 * kd) + 0.0f;  // (+0 turns a -0 into +0)
-    if (live && q4 == 0) {
-      if (errors) errors[((size_t)k * M + m_begin + r) * G + j] = e;
-      if (fabsf(e) < INFINITY) atomicMin(&best_key[r], clip_key(e, k));
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      float el = e_lane[u];
+      el += __shfl_xor(el, 16);
+      el += __shfl_xor(el, 32);
+      const float e = ldexpf(el, ex - 2 * kdv[u]) + 0.0f;  // (+0 turns a -0 into +0)
+      if (livev[u] && q4 == 0) {
+        if (errors) errors[((size_t)kv[u] * M + m_begin + rv_[u]) * G + j] = e;
+        if (fabsf(e) < INFINITY) atomicMin(&best_key[rv_[u]], clip_key(e, kv[u]));
+      }
     }
   }
   __syncthreads();
@@ -504,9 +541,9 @@ hipError_t launch_clip_search(const uint16_t* W, const float* s, const uint16_t*
   if (n_ratio < 1 || n_ratio > kMaxClip) return hipErrorInvalidValue;
   const void* fn;
   switch (group_size) {
-    case 32: fn = (const void*)k_clip_mfma<32>; break;
-    case 64: fn = (const void*)k_clip_mfma<64>; break;
-    case 128: fn = (const void*)k_clip_mfma<128>; break;
+    case 32: fn = (const void*)k_clip_mfma<32, kClipSlices>; break;
+    case 64: fn = (const void*)k_clip_mfma<64, kClipSlices>; break;
+    case 128: fn = (const void*)k_clip_mfma<128, kClipSlices>; break;
     default: return hipErrorInvalidValue;
   }
   // rows per block: the fewest rounds of resident blocks times the work of one block
@@ -533,7 +570,7 @@ hipError_t launch_clip_search(const uint16_t* W, const float* s, const uint16_t*
     const int64_t blocks = (int64_t)ngroups * ((M + r - 1) / r);
     const int64_t rounds = (blocks + cap - 1) / cap;
     const int64_t per_wave = ((int64_t)min(r, M) * n_ratio + 16 * kClipWaves - 1) /
-                             (16 * kClipWaves);
+                             (16 * kClipWaves);  // slices per wave
     const int64_t cost = rounds * (per_wave + 2);
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
@@ -542,7 +579,7 @@ hipError_t launch_clip_search(const uint16_t* W, const float* s, const uint16_t*
   }
   dim3 grid(ngroups, (M + rows - 1) / rows);
 #define AWQ_CLIP(GS)                                                                        \
-  hipLaunchKernelGGL(k_clip_mfma<GS>, grid, dim3(kClipThreads), 0, stream, W, s, Ghi, Glo,   \
+  hipLaunchKernelGGL((k_clip_mfma<GS, kClipSlices>), grid, dim3(kClipThreads), 0, stream, W, s, Ghi, Glo,   \
                      gexp, M, K, w_bit, zero_point, ratios, n_ratio, rows, clip_out,          \
                      best_out, errors)
   switch (group_size) {
