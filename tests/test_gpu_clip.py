@@ -1,8 +1,9 @@
 """Clip search and the clipped pack on the GPU (through the C ABI) against the oracle.
 
-Group errors: the GPU takes e = d^T (X_j^T X_j) d with fp64 Gram sums stored in fp32 and
-an fp32 quadratic form over an fp32 d; the oracle takes the group's partial product
-directly in fp64.  Bar: |e_gpu - e| <= 1e-3 e + 2^-14 || |X_j| (|d| + 2^-18 |W_j|) ||^2
+Group errors: the GPU takes e = d^T (X_j^T X_j) d, the Gram sums on the matrix cores in
+fp32 over at most 256 tokens (within 2^-16 of the sum of |products|) and added in fp64, then
+an fp32 quadratic form over fp16 hi + lo splits of G and of d; the oracle takes the group's
+partial product directly in fp64.  Bar: |e_gpu - e| <= 1e-3 e + 2^-14 || |X_j| (|d| + 2^-18 |W_j|) ||^2
 (fp32 rounding of d and of the sums, bounded through |X_j|), and the same ratio wherever
 the oracle's best and runner-up differ by more than 1e-3 relative; elsewhere the GPU's
 choice must be within that tolerance of the best.  The clipped pack is bit-exact.
@@ -70,6 +71,7 @@ CASES = [
     (70, 320, 50, 3, 32, 1),
     (17, 128, 1, 4, 128, 1),      # one token
     (128, 1024, 700, 4, 128, 0),
+    (8, 128, 20000, 4, 128, 1),   # 64 token splits of 320: several fp32 sums per split
 ]
 
 

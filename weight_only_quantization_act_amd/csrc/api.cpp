@@ -388,7 +388,7 @@ size_t awq_clip_workspace_bytes(int64_t out_features, int64_t in_features, int64
   const size_t ng = (size_t)(in_features / cfg->group_size);
   return 2 * round_up(kg * sizeof(uint16_t), kAlign) + round_up(ng * sizeof(int32_t), kAlign) +
          round_up(ng * awq::gram_chunks(cfg->group_size) * sizeof(double), kAlign) +
-         round_up((size_t)splits * kg * sizeof(double), kAlign);
+         round_up(kg * sizeof(double), kAlign) + round_up((size_t)splits * kg * sizeof(float), kAlign);
 }
 
 int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_features,
@@ -433,11 +433,12 @@ int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_fe
   off += round_up(ng * sizeof(int32_t), kAlign);
   double* cmax = (double*)(ws + off);
   off += round_up(ng * awq::gram_chunks(cfg->group_size) * sizeof(double), kAlign);
-  double* partials = (double*)(ws + off);
-  const int splits = awq::gram_splits(N, K, cfg->group_size);
+  double* G64 = (double*)(ws + off);
+  off += round_up(kg * sizeof(double), kAlign);
+  float* partials = (float*)(ws + off);
   if ((st = hip_status(awq::launch_group_gram((const uint16_t*)X, (int)N, (int)K,
-                                              cfg->group_size, splits, partials, cmax, Ghi,
-                                              Glo, gexp, (hipStream_t)stream))))
+                                              cfg->group_size, partials, G64, cmax, Ghi, Glo,
+                                              gexp, (hipStream_t)stream))))
     return st;
   return hip_status(awq::launch_clip_search((const uint16_t*)W, s, Ghi, Glo, gexp, (int)M,
                                             (int)K, cfg->w_bit, cfg->group_size,

@@ -12,25 +12,27 @@
 // form per (row, group, ratio) (M K g n_ratio) costs g / N of the direct products, and all
 // ratios share the Gram matrix.
 //
-//   k_group_gram   fp64 sums of fp16 products (exact products, fp64 accumulation) over
-//                  token splits, one 64 x 64 (or g x g) tile of one group per block, a
-//                  4 x 4 (2 x 2) register tile per thread.
-//   k_gram_sum     adds the splits in order (over split 0) and takes per-chunk maxima;
+//   k_gram_mfma    the Gram sums on the matrix cores: fp16 products (exact in fp32) summed
+//                  in fp32 over at most 256 tokens, added in fp64, one 128-channel span and
+//                  token split per block (the stage transposed into LDS on the way in);
+//   k_gram_sum     adds the split partials in fp64 in split order and takes per-chunk
+//                  maxima;
 //   k_gram_split   scales the group's matrix by a power of two into [2^13, 2^14) and
 //                  splits it into fp16 hi + lo (G ~ hi + lo to about 2^-22 relative), with
 //                  the exponent kept per group.
-//   k_clip_mfma    the quadratic forms on the matrix cores.  A lane pair (l, l ^ 32) owns one
-//                  (row, ratio) pair: it quantises the row's group with its ratio in fp32
-//                  exactly as the pack does, forms d = (v - Q(v)) / s, scales d by a power
-//                  of two into [2^9, 2^10) and splits it into fp16 hi + lo.  Then
-//                  U^T = G D^T comes from v_mfma_f32_32x32x16_f16 in three passes
-//                  (G_hi D_hi + G_hi D_lo + G_lo D_hi; every product is exact in fp32),
-//                  G's 32-row tiles as the A operand (from LDS) and 32 pairs as the B
-//                  operand.  The k-slots of each 16-channel step are permuted so that lane
-//                  half h supplies the channels whose bit 2 is h -- exactly the rows of U^T
-//                  it receives in C -- so e = sum_c U^T[c] d[c] is a lane-local sum plus one
-//                  exchange with the partner lane.  The power-of-two scales are undone
-//                  exactly; the first smallest error per row is picked through LDS.
+//   k_clip_mfma    the quadratic forms on the matrix cores.  Four lanes own one (row, ratio)
+//                  pair: they quantise the row's group with its ratio in fp32 exactly as
+//                  the pack does, form d = (v - Q(v)) / s, scale d by a power of two below
+//                  2^14 and split it into fp16 hi + lo.  Then U^T = G' D^T comes from
+//                  v_mfma_f32_16x16x32_f16 in three passes (G_hi D_hi + G_hi D_lo +
+//                  G_lo D_hi; every product is exact in fp32), G' (G with its upper 16 x 16
+//                  blocks doubled and lower ones dropped, so only 20 of 32 tiles are needed)
+//                  as the A operand from LDS and 16 pairs as the B operand, two such slices
+//                  per wave sharing each read of G'.  The k-slots of each 32-channel step
+//                  are permuted so that each lane supplies the channels whose rows of U^T it
+//                  receives in C, so e = sum_c U^T[c] d[c] is a lane-local sum plus two
+//                  exchanges.  The power-of-two scales are undone exactly; the first smallest
+//                  error per row is kept through an LDS atomic minimum.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -46,77 +48,119 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGramThreads = 256;
-constexpr int kGramTT = 32;  // tokens per LDS stage
-constexpr int kGramTargetBlocks = 1024;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-// partials[sp][j][a][b] = sum over the split's tokens of X[t][j g + a] X[t][j g + b].
-template <int TS>
-__global__ __launch_bounds__(kGramThreads) void k_group_gram(const uint16_t* __restrict__ X,
-                                                             int N, int K, int g, int splits,
-                                                             int tokens_per_split,
-                                                             double* __restrict__ partials) {
-  constexpr int R = TS / 16;  // outputs per thread along each side
-  __shared__ float As[kGramTT][TS];
-  __shared__ float Bs[kGramTT][TS];
-  const int tiles_side = g / TS;
-  const int tiles = tiles_side * tiles_side;
-  const int j = blockIdx.x / tiles;
-  const int tile = blockIdx.x - j * tiles;
-  const int ta = tile / tiles_side, tb = tile - (tile / tiles_side) * tiles_side;
-  const int ca = j * g + ta * TS, cb = j * g + tb * TS;
+constexpr int kGramThreads = 512;
+constexpr int kGramSpan = 128;   // channels of one block (128 / g groups)
+constexpr int kGramStage = 64;   // tokens per LDS stage (two 32-token k-steps)
+constexpr int kGramFlush = 256;  // tokens summed in fp32 before adding into fp64
+constexpr int kGramXtp = 68;     // LDS row of the transposed tile (fp16, 8-byte aligned)
+constexpr int kGramTargetBlocks = 512;
+
+// partials[sp][j][a][b] = sum over split sp's tokens of X[t][j g + a] X[t][j g + b], the
+// products of fp16 values exact in fp32, summed on the matrix cores (v_mfma_f32_16x16x32_f16)
+// in fp32 over at most 256 tokens (error at most 2^-16 of the sum of |products|), those
+// sums added in fp64 and the split's total rounded to fp32.
+//
+// Block: channels [c0, c0 + 128) of the layer and split sp.  A stage of 64 tokens is stored
+// transposed in LDS, xt[channel][token]: lane l of wave w loads the channel pair
+// (2 l, 2 l + 1) of tokens 8 w .. 8 w + 7 (coalesced 256-byte token rows) and interleaves
+// the halves with v_perm.  The MFMA fragment of channel block b (16 channels) and k-step ks
+// is then lane (p, q)'s 16 bytes xt[16 b + p][32 ks + 8 q ..], the A operand of tile row b
+// and the B operand of tile column b alike.  Wave w owns tile row w and the g / 16 tile
+// columns of its group.
+template <int GS>
+__global__ __launch_bounds__(kGramThreads) void k_gram_mfma(const uint16_t* __restrict__ X,
+                                                            int N, int K, int tokens_per_split,
+                                                            float* __restrict__ partials) {
+  constexpr int TC = GS / 16;  // tile columns of a group
+  __shared__ __attribute__((aligned(16))) uint16_t xt[kGramSpan * kGramXtp];
+  const int c0 = blockIdx.x * kGramSpan;
   const int sp = blockIdx.y;
   const int t_begin = sp * tokens_per_split;
   const int t_end = min(N, t_begin + tokens_per_split);
-  const int tid = threadIdx.x;
-  const int ty = tid / 16, tx = tid - (tid / 16) * 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, pl = lane & 15;
+  const int ngroups = K / GS;
+  const int grp = (c0 + 16 * wave) / GS;  // the group of the wave's tile row
+  const int tc0 = (grp * GS - c0) / 16;   // the group's first tile column (span blocks)
+  const bool active = grp < ngroups;
+  const bool pair_ok = c0 + 2 * lane < K;
 
-  double acc[R][R];
+  floatx4 acc[TC];
+  double acc64[TC][4];
 #pragma unroll
-  for (int a = 0; a < R; ++a)
+  for (int tc = 0; tc < TC; ++tc) {
+    acc[tc] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int b = 0; b < R; ++b) acc[a][b] = 0.0;
-
-  constexpr int kChunksPerRow = TS / 8;                // 16-byte loads per token row
-  constexpr int kLoaders = kGramTT * kChunksPerRow;    // threads that load one tile
-  for (int t0 = t_begin; t0 < t_end; t0 += kGramTT) {
-    if (tid < kLoaders) {
-      const int r = tid / kChunksPerRow, c = (tid - r * kChunksPerRow) * 8;
-      const int t = t0 + r;
-      u32x4 ra = {0u, 0u, 0u, 0u}, rb = {0u, 0u, 0u, 0u};
-      if (t < t_end) {
-        ra = *(const u32x4*)(X + (size_t)t * K + ca + c);
-        rb = *(const u32x4*)(X + (size_t)t * K + cb + c);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        As[r][c + 2 * e] = h2f((uint16_t)(ra[e] & 0xffffu));
-        As[r][c + 2 * e + 1] = h2f((uint16_t)(ra[e] >> 16));
-        Bs[r][c + 2 * e] = h2f((uint16_t)(rb[e] & 0xffffu));
-        Bs[r][c + 2 * e + 1] = h2f((uint16_t)(rb[e] >> 16));
-      }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int t = 0; t < kGramTT; ++t) {
-      double av[R], bv[R];
-#pragma unroll
-      for (int a = 0; a < R; ++a) av[a] = (double)As[t][ty * R + a];
-#pragma unroll
-      for (int b = 0; b < R; ++b) bv[b] = (double)Bs[t][tx * R + b];
-#pragma unroll
-      for (int a = 0; a < R; ++a)
-#pragma unroll
-        for (int b = 0; b < R; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
-    }
-    __syncthreads();
+    for (int e = 0; e < 4; ++e) acc64[tc][e] = 0.0;
   }
-  double* out = partials + ((size_t)sp * (K / g) + j) * (size_t)g * g;
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kGramStage) {
+    {
+      uint32_t d[8];
 #pragma unroll
-  for (int a = 0; a < R; ++a)
+      for (int e = 0; e < 8; ++e) {
+        const int t = t0 + 8 * wave + e;
+        d[e] = (pair_ok && t < t_end) ? *(const uint32_t*)(X + (size_t)t * K + c0 + 2 * lane)
+                                      : 0u;
+      }
+      uint2 lo0, lo1, hi0, hi1;  // channel 2 l (low halves) and 2 l + 1 (high halves)
+      lo0.x = __builtin_amdgcn_perm(d[1], d[0], 0x05040100u);
+      lo0.y = __builtin_amdgcn_perm(d[3], d[2], 0x05040100u);
+      lo1.x = __builtin_amdgcn_perm(d[5], d[4], 0x05040100u);
+      lo1.y = __builtin_amdgcn_perm(d[7], d[6], 0x05040100u);
+      hi0.x = __builtin_amdgcn_perm(d[1], d[0], 0x07060302u);
+      hi0.y = __builtin_amdgcn_perm(d[3], d[2], 0x07060302u);
+      hi1.x = __builtin_amdgcn_perm(d[5], d[4], 0x07060302u);
+      hi1.y = __builtin_amdgcn_perm(d[7], d[6], 0x07060302u);
+      uint16_t* r0 = xt + (2 * lane) * kGramXtp + 8 * wave;
+      *(uint2*)r0 = lo0;
+      *(uint2*)(r0 + 4) = lo1;
+      *(uint2*)(r0 + kGramXtp) = hi0;
+      *(uint2*)(r0 + kGramXtp + 4) = hi1;
+    }
+    __syncthreads();
+    if (active) {
+      auto frag = [&](int blk, int ks) {
+        const uint16_t* src = xt + (16 * blk + pl) * kGramXtp + 32 * ks + 8 * q4;
+        const uint2 u0 = *(const uint2*)src, u1 = *(const uint2*)(src + 4);
+        const u32x4 v = {u0.x, u0.y, u1.x, u1.y};
+        return __builtin_bit_cast(half8, v);
+      };
 #pragma unroll
-    for (int b = 0; b < R; ++b)
-      out[(size_t)(ta * TS + ty * R + a) * g + tb * TS + tx * R + b] = acc[a][b];
+      for (int ks = 0; ks < kGramStage / 32; ++ks) {
+        const half8 fa = frag(wave, ks);
+#pragma unroll
+        for (int tc = 0; tc < TC; ++tc)
+          acc[tc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, frag(tc0 + tc, ks), acc[tc], 0,
+                                                           0, 0);
+      }
+    }
+    __syncthreads();
+    if ((t0 + kGramStage - t_begin) % kGramFlush == 0 || t0 + kGramStage >= t_end) {
+#pragma unroll
+      for (int tc = 0; tc < TC; ++tc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc64[tc][e] += (double)acc[tc][e];
+        acc[tc] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+  }
+  if (!active) return;
+  // C element e of tile (wave, tc0 + tc): G row 16 wave + 4 q + e, column
+  // 16 (tc0 + tc) + (l mod 16), both relative to the span; minus the group's offset
+  float* out = partials + ((size_t)sp * ngroups + grp) * (size_t)GS * GS;
+  const int goff = grp * GS - c0;
+#pragma unroll
+  for (int tc = 0; tc < TC; ++tc)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int a = 16 * wave + 4 * q4 + e - goff;
+      const int b = 16 * (tc0 + tc) + pl - goff;
+      out[(size_t)a * GS + b] = (float)acc64[tc][e];
+    }
 }
 
 constexpr int kGramChunk = 1024;  // Gram entries per block of the two passes below
@@ -125,10 +169,11 @@ __device__ __forceinline__ double nan_max64(double m, double a) {
   return (a > m || a != a) ? a : m;
 }
 
-// Pass 1, block (group j, chunk c): G = sum of the split partials in order, written over
-// split 0, and the chunk's largest magnitude (NaN if any entry is NaN).
-__global__ __launch_bounds__(256) void k_gram_sum(double* __restrict__ partials, int g,
+// Pass 1, block (group j, chunk c): G = the split partials added in fp64 in split order,
+// and the chunk's largest magnitude (NaN if any entry is NaN).
+__global__ __launch_bounds__(256) void k_gram_sum(const float* __restrict__ partials, int g,
                                                   int ngroups, int splits,
+                                                  double* __restrict__ G64,
                                                   double* __restrict__ cmax) {
   __shared__ double mx[256];
   const int j = blockIdx.x, c = blockIdx.y, nc = gridDim.y;
@@ -139,9 +184,9 @@ __global__ __launch_bounds__(256) void k_gram_sum(double* __restrict__ partials,
   const int n = (int)min((size_t)kGramChunk, gg - (size_t)c * kGramChunk);
   double m = 0.0;
   for (int i = tid; i < n; i += 256) {
-    double v = partials[base + i];
-    for (int sp = 1; sp < splits; ++sp) v += partials[sp * stride + base + i];
-    partials[base + i] = v;
+    double v = (double)partials[base + i];
+    for (int sp = 1; sp < splits; ++sp) v += (double)partials[sp * stride + base + i];
+    G64[base + i] = v;
     m = nan_max64(m, fabs(v));
   }
   mx[tid] = m;
@@ -191,8 +236,6 @@ constexpr int kClipMaxRows = 160;  // rows of one block (its per-row LDS tables)
 #endif
 constexpr int kClipSlices = AWQ_CLIP_SLICES;  // 16-pair slices sharing one read of G's tiles
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // Order-preserving key of a finite error and its ratio index: the smallest key is the
 // smallest error, and among equal errors the first ratio.
@@ -488,47 +531,64 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
 
 }  // namespace
 
-int gram_splits(int64_t N, int64_t K, int group_size) {
-  const int ts = group_size < 64 ? group_size : 64;
-  const int64_t blocks = (K / group_size) * (int64_t)(group_size / ts) * (group_size / ts);
-  int64_t sp = blocks > 0 ? (kGramTargetBlocks + blocks - 1) / blocks : 1;
-  const int64_t by_tokens = (N + 255) / 256;  // at least 256 tokens per split
+int gram_tokens_per_split(int64_t N, int64_t K) {
+  // enough splits to give the chip about kGramTargetBlocks blocks, each at least 256 tokens
+  // (a whole number of stages), and at most 64 splits
+  const int64_t spans = (K + kGramSpan - 1) / kGramSpan;
+  int64_t sp = spans > 0 ? (kGramTargetBlocks + spans - 1) / spans : 1;
+  const int64_t by_tokens = (N + kGramFlush - 1) / kGramFlush;
   if (sp > by_tokens) sp = by_tokens;
-  if (sp < 1) sp = 1;
   if (sp > 64) sp = 64;
-  return (int)sp;
+  if (sp < 1) sp = 1;
+  int64_t tps = (N + sp - 1) / sp;
+  tps = (tps + kGramStage - 1) / kGramStage * kGramStage;
+  return (int)(tps > kGramStage ? tps : kGramStage);
+}
+
+int gram_splits(int64_t N, int64_t K, int group_size) {
+  (void)group_size;
+  const int64_t tps = gram_tokens_per_split(N, K);
+  const int64_t sp = (N + tps - 1) / tps;
+  return (int)(sp > 1 ? sp : 1);
 }
 
 int gram_chunks(int group_size) {
   return (group_size * group_size + kGramChunk - 1) / kGramChunk;
 }
 
-hipError_t launch_group_gram(const uint16_t* X, int N, int K, int group_size, int splits,
-                             double* partials, double* cmax, uint16_t* Ghi, uint16_t* Glo,
+hipError_t launch_group_gram(const uint16_t* X, int N, int K, int group_size, float* partials,
+                             double* G64, double* cmax, uint16_t* Ghi, uint16_t* Glo,
                              int32_t* gexp, hipStream_t stream) {
   if (K <= 0) return hipSuccess;
-  const int ts = group_size < 64 ? group_size : 64;
-  const int tiles = (group_size / ts) * (group_size / ts);
-  const int tps = (N + splits - 1) / splits;
-  dim3 grid((K / group_size) * tiles, splits);
-  if (ts == 64)
-    hipLaunchKernelGGL(k_group_gram<64>, grid, dim3(kGramThreads), 0, stream, X, N, K,
-                       group_size, splits, tps, partials);
-  else if (ts == 32)
-    hipLaunchKernelGGL(k_group_gram<32>, grid, dim3(kGramThreads), 0, stream, X, N, K,
-                       group_size, splits, tps, partials);
-  else
-    return hipErrorInvalidValue;
+  const int tps = gram_tokens_per_split(N, K);
+  const int splits = gram_splits(N, K, group_size);
+  dim3 grid((K + kGramSpan - 1) / kGramSpan, splits);
+  switch (group_size) {
+    case 32:
+      hipLaunchKernelGGL(k_gram_mfma<32>, grid, dim3(kGramThreads), 0, stream, X, N, K, tps,
+                         partials);
+      break;
+    case 64:
+      hipLaunchKernelGGL(k_gram_mfma<64>, grid, dim3(kGramThreads), 0, stream, X, N, K, tps,
+                         partials);
+      break;
+    case 128:
+      hipLaunchKernelGGL(k_gram_mfma<128>, grid, dim3(kGramThreads), 0, stream, X, N, K, tps,
+                         partials);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nc = gram_chunks(group_size);
   dim3 g2(K / group_size, nc);
   hipLaunchKernelGGL(k_gram_sum, g2, dim3(256), 0, stream, partials, group_size,
-                     K / group_size, splits, cmax);
+                     K / group_size, splits, G64, cmax);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gram_split, g2, dim3(256), 0, stream, partials, group_size, cmax, Ghi,
-                     Glo, gexp);
+  hipLaunchKernelGGL(k_gram_split, g2, dim3(256), 0, stream, G64, group_size, cmax, Ghi, Glo,
+                     gexp);
   return hipGetLastError();
 }
 
