@@ -90,6 +90,22 @@ def test_clip_search_parity(M, K, N, w_bit, g, zp):
     say(f"  decided by a clear margin: {clear} of {total}")
 
 
+def test_clip_wide_dynamic_range():
+    """Rows whose magnitudes span 2^-12 .. 2^4 in one block and scales spanning four decades:
+    the power of two shared by a block's rows and the scaled Gram matrix keep every group
+    error within the same bound."""
+    M, K, N, g = 48, 256, 400, 128
+    L = make_layer(small_spec("w", M, K, N, outlier_count=3, seed=11))
+    rng = np.random.default_rng(12)
+    W = (L.W.astype(F64) * np.exp2(rng.uniform(-12, 4, M))[:, None]).astype(F16)
+    s = np.exp(rng.uniform(np.log(1e-2), np.log(1e2), K)).astype(F32)
+    cfg = awq.qconfig(4, g, 1)
+    res = awq.awq_clip_search(dev(W), dev(L.X), dev(s), RATIOS, cfg, want_errors=True)
+    torch.cuda.synchronize()
+    clear, total = _check_clip(res, W, L.X, s, ocfg(cfg), RATIOS, np.arange(M), "wide range")
+    say(f"  decided by a clear margin: {clear} of {total}")
+
+
 def test_clip_degenerate():
     cfg = awq.qconfig(4, 128, 1)
     L = make_layer(small_spec("z", 8, 256, 64))

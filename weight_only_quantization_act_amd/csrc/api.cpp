@@ -436,7 +436,7 @@ int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_fe
   double* G64 = (double*)(ws + off);
   off += round_up(kg * sizeof(double), kAlign);
   float* partials = (float*)(ws + off);
-  if ((st = hip_status(awq::launch_group_gram((const uint16_t*)X, (int)N, (int)K,
+  if ((st = hip_status(awq::launch_group_gram((const uint16_t*)X, s, (int)N, (int)K,
                                               cfg->group_size, partials, G64, cmax, Ghi, Glo,
                                               gexp, (hipStream_t)stream))))
     return st;

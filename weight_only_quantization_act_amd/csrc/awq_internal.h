@@ -57,16 +57,16 @@ constexpr int kMaxClip = 64;
 struct ClipList {
   float v[kMaxClip];
 };
-// Gram matrices of the activation groups: G[j] = X_j^T X_j (fp32 matrix-core sums over at
-// most 256 tokens, added in fp64 within a token split; split partials fp32
-// [splits][K/g][g][g] added in fp64 into G64 [K/g][g][g]), stored as
-// G[j] 2^-gexp[j] = Ghi + Glo with Ghi, Glo fp16 [K/g][g][g] and gexp int32 [K/g].
-// cmax: fp64 [K/g][gram_chunks(g)] per-chunk maxima of |G|.
+// Scaled Gram matrices of the activation groups: G~[j] = S_j^-1 X_j^T X_j S_j^-1 with
+// S_j = diag(s) over the group's channels (X_j^T X_j as fp32 matrix-core sums over at most
+// 256 tokens, added in fp64 within a token split; split partials fp32 [splits][K/g][g][g]
+// added in fp64 into G64 [K/g][g][g]), stored as G~[j] 2^-gexp[j] = Ghi + Glo with Ghi, Glo
+// fp16 [K/g][g][g] and gexp int32 [K/g].  cmax: fp64 [K/g][gram_chunks(g)] per-chunk maxima.
 int gram_splits(int64_t N, int64_t K, int group_size);
 int gram_chunks(int group_size);
-hipError_t launch_group_gram(const uint16_t* X, int N, int K, int group_size, float* partials,
-                             double* G64, double* cmax, uint16_t* Ghi, uint16_t* Glo,
-                             int32_t* gexp, hipStream_t stream);
+hipError_t launch_group_gram(const uint16_t* X, const float* s, int N, int K, int group_size,
+                             float* partials, double* G64, double* cmax, uint16_t* Ghi,
+                             uint16_t* Glo, int32_t* gexp, hipStream_t stream);
 // Per (row, group): the group's own output error d^T G_j d for every ratio, the first
 // smallest, its ratio (1 when none is finite); errors (nullable) fp32 [n][M][K/g].
 // n_ratio <= 64.

@@ -169,10 +169,13 @@ __device__ __forceinline__ double nan_max64(double m, double a) {
   return (a > m || a != a) ? a : m;
 }
 
-// Pass 1, block (group j, chunk c): G = the split partials added in fp64 in split order,
-// and the chunk's largest magnitude (NaN if any entry is NaN).
+// Pass 1, block (group j, chunk c): G~ = S^-1 G S^-1, G the split partials added in fp64
+// in split order and S = diag(s), and the chunk's largest magnitude (NaN if any entry is
+// NaN).  With it the group error of the scaled weight error d~ = v - Q(v) = d s is
+// d~^T G~ d~ = d^T G d.
 __global__ __launch_bounds__(256) void k_gram_sum(const float* __restrict__ partials, int g,
                                                   int ngroups, int splits,
+                                                  const float* __restrict__ s,
                                                   double* __restrict__ G64,
                                                   double* __restrict__ cmax) {
   __shared__ double mx[256];
@@ -186,6 +189,9 @@ __global__ __launch_bounds__(256) void k_gram_sum(const float* __restrict__ part
   for (int i = tid; i < n; i += 256) {
     double v = (double)partials[base + i];
     for (int sp = 1; sp < splits; ++sp) v += (double)partials[sp * stride + base + i];
+    const int e = c * kGramChunk + i;  // entry (a, b) of the group's matrix
+    const int a = e / g, b = e - (e / g) * g;
+    v = v / (double)s[j * g + a] / (double)s[j * g + b];
     G64[base + i] = v;
     m = nan_max64(m, fabs(v));
   }
@@ -268,11 +274,10 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
   constexpr int NB = GS / 16;  // 16-channel blocks; a lane owns 4 channels of each
   __shared__ __attribute__((aligned(16))) uint16_t gh[GS * GP];
   __shared__ __attribute__((aligned(16))) uint16_t gl[GS * GP];
-  __shared__ __attribute__((aligned(16))) float ss[GS];
-  __shared__ __attribute__((aligned(16))) float rs[GS];
+  __shared__ __attribute__((aligned(16))) float ss[GS];  // s, then s 2^kd
   __shared__ float rng_hi[kClipMaxRows], rng_lo[kClipMaxRows];  // range of v = w s per row
   __shared__ unsigned long long best_key[kClipMaxRows];
-  __shared__ float rs_max_sh;
+  __shared__ uint32_t vmax_bits, smax_bits;  // block maxima of max|v| (finite) and of |s|
   const int j = blockIdx.x;
   const int G = K / GS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -302,10 +307,10 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
     *(uint2*)(gl + r * GP + c8) = make_uint2(b[0], b[1]);
     *(uint2*)(gl + r * GP + c8 + 4) = make_uint2(b[2], b[3]);
   }
-  for (int i = tid; i < GS; i += kClipThreads) {
-    const float sv = s_in[j * GS + i];
-    ss[i] = sv;
-    rs[i] = 1.0f / sv;
+  for (int i = tid; i < GS; i += kClipThreads) ss[i] = s_in[j * GS + i];
+  if (tid == 0) {
+    vmax_bits = 0u;
+    smax_bits = 0u;
   }
   __syncthreads();
   // range of the scaled weights v = w s of every row of the block (shared by its ratios),
@@ -328,16 +333,32 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
     rng_hi[r] = hi;
     rng_lo[r] = lo;
     best_key[r] = ~0ull;
+    const float vm = fmaxf(fabsf(hi), fabsf(lo));
+    if (vm < INFINITY) atomicMax(&vmax_bits, __float_as_uint(vm));
   }
-  if (wave == 0) {
-    float mx = 0.0f;
-    for (int c = lane; c < GS; c += 64) mx = fmaxf(mx, fabsf(rs[c]));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if (lane == 0) rs_max_sh = mx;
+  for (int i = tid; i < GS; i += kClipThreads) {
+    const float a = fabsf(ss[i]);
+    if (a < INFINITY) atomicMax(&smax_bits, __float_as_uint(a));
   }
   __syncthreads();
-  const float rs_max = rs_max_sh;
+  // One power of two 2^kd for the block: |v - Q(v)| <= |v| + |Q(v)| <= 2.07 max|v|, so with
+  // 2 max|v| below 2^14 the scaled errors d~ 2^kd stay far inside fp16 (65504); kd is also
+  // capped so that every s 2^kd stays finite.  Scaling s by 2^kd scales v, the step and the
+  // errors exactly (the quotient v / step is unchanged).
+  int kd = 0;
+  {
+    const float bound = 2.0f * __uint_as_float(vmax_bits);
+    if (bound > 0.0f) {
+      int e2, es;
+      frexpf(bound, &e2);  // bound = f 2^e2, f in [0.5, 1)
+      kd = 14 - e2;
+      frexpf(__uint_as_float(smax_bits), &es);
+      kd = min(kd, 127 - es);
+    }
+  }
+  __syncthreads();  // every thread has read the maxima; ss is rescaled next
+  for (int i = tid; i < GS; i += kClipThreads) ss[i] = ldexpf(ss[i], kd);
+  __syncthreads();
   const int ex = gexp[j];
   const bool zp = zero_point != 0;
   const int P = R * n_ratio;
@@ -362,11 +383,11 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
 
   for (int sg = wave; sg < sgroups; sg += kClipWaves) {
     // B operands of the NS pairs: block b's 4 channels as two dwords of fp16 pairs,
-    // hi = d 2^kd rounded toward zero (two per instruction) and lo = the exact remainder
-    // rounded toward zero, so that |hi + lo - d 2^kd| <= 2^-20 |d 2^kd| above the fp16
+    // hi = d~ 2^kd rounded toward zero (two per instruction) and lo = the exact remainder
+    // rounded toward zero, so that |hi + lo - d~ 2^kd| <= 2^-20 |d~ 2^kd| above the fp16
     // subnormal range
     uint32_t bhi[NS][NB][2], blo[NS][NB][2];
-    int kdv[NS], rv_[NS], kv[NS];
+    int rv_[NS], kv[NS];
     bool livev[NS];
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -396,16 +417,7 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
         clo = -qmax;
         chi = qmax;
       }
-      // |d| = |v - Q(v)| / s <= 2 max|v| max(1/s) = bound: scale by 2^kd so that the bound
-      // is below 2^14 (no fp16 overflow; values far below it only lose precision in terms
-      // that contribute little to e), then split d 2^kd into fp16 hi + lo
-      const float bound = 2.0f * vmax * rs_max;
-      int kd = 0;
-      if (bound > 0.0f && bound < INFINITY) {
-        int e2;
-        frexpf(bound, &e2);  // bound = f 2^e2, f in [0.5, 1)
-        kd = 14 - e2;
-      }
+      st = ldexpf(st, kd);  // the step in the block's scaled units
       // rint(v / st) as rint(v * (1/st)), except for a lane with an element whose product
       // lies within 2^-17 of a half-integer (or is not finite): that lane redoes its
       // elements with the correctly rounded division.  The two agree for |v / st| <= 16, and
@@ -414,9 +426,7 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
       const float inv = __builtin_amdgcn_rcpf(st);
       auto quant_block = [&](int b, bool exact) {
         const float4 sv = *(const float4*)&ss[16 * b + 4 * q4];
-        const float4 rv = *(const float4*)&rs[16 * b + 4 * q4];
         const float s4[4] = {sv.x, sv.y, sv.z, sv.w};
-        const float r4[4] = {rv.x, rv.y, rv.z, rv.w};
         const uint32_t wp[2] = {raw[u][b].x, raw[u][b].y};
         float dd[4];
         bool near = false;
@@ -424,7 +434,8 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
         for (int i = 0; i < 4; ++i) {
           const _Float16 wh =
               __builtin_bit_cast(_Float16, (uint16_t)(wp[i >> 1] >> (16 * (i & 1))));
-          const float v = fmaf((float)wh, s4[i], 0.0f);  // = w s (a zero's sign is immaterial)
+          // v = w s 2^kd (a zero's sign is immaterial)
+          const float v = fmaf((float)wh, s4[i], 0.0f);
           const float t = v * inv;
           float q = rintf(t);
           const bool nr = !(fabsf(t - q) < 0.5f - kTieBand);
@@ -434,7 +445,7 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
             near |= nr;
           }
           const float cz = __builtin_amdgcn_fmed3f(q, clo, chi);
-          dd[i] = ldexpf(fmaf(-cz, st, v) * r4[i], kd);
+          dd[i] = fmaf(-cz, st, v);  // d~ 2^kd = (v - Q(v)) 2^kd
         }
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
@@ -456,7 +467,6 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
 #pragma unroll
         for (int b = 0; b < NB; ++b) quant_block(b, true);
       }
-      kdv[u] = kd;
       rv_[u] = r;
       kv[u] = k;
       livev[u] = live;
@@ -512,7 +522,7 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
       float el = e_lane[u];
       el += __shfl_xor(el, 16);
       el += __shfl_xor(el, 32);
-      const float e = ldexpf(el, ex - 2 * kdv[u]) + 0.0f;  // (+0 turns a -0 into +0)
+      const float e = ldexpf(el, ex - 2 * kd) + 0.0f;  // (+0 turns a -0 into +0)
       if (livev[u] && q4 == 0) {
         if (errors) errors[((size_t)kv[u] * M + m_begin + rv_[u]) * G + j] = e;
         if (fabsf(e) < INFINITY) atomicMin(&best_key[rv_[u]], clip_key(e, kv[u]));
@@ -556,9 +566,9 @@ int gram_chunks(int group_size) {
   return (group_size * group_size + kGramChunk - 1) / kGramChunk;
 }
 
-hipError_t launch_group_gram(const uint16_t* X, int N, int K, int group_size, float* partials,
-                             double* G64, double* cmax, uint16_t* Ghi, uint16_t* Glo,
-                             int32_t* gexp, hipStream_t stream) {
+hipError_t launch_group_gram(const uint16_t* X, const float* s, int N, int K, int group_size,
+                             float* partials, double* G64, double* cmax, uint16_t* Ghi,
+                             uint16_t* Glo, int32_t* gexp, hipStream_t stream) {
   if (K <= 0) return hipSuccess;
   const int tps = gram_tokens_per_split(N, K);
   const int splits = gram_splits(N, K, group_size);
@@ -584,7 +594,7 @@ hipError_t launch_group_gram(const uint16_t* X, int N, int K, int group_size, fl
   const int nc = gram_chunks(group_size);
   dim3 g2(K / group_size, nc);
   hipLaunchKernelGGL(k_gram_sum, g2, dim3(256), 0, stream, partials, group_size,
-                     K / group_size, splits, G64, cmax);
+                     K / group_size, splits, s, G64, cmax);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_gram_split, g2, dim3(256), 0, stream, G64, group_size, cmax, Ghi, Glo,
