@@ -97,15 +97,20 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_mfma(const uint16_t* __re
     for (int e = 0; e < 4; ++e) acc64[tc][e] = 0.0;
   }
 
+  // the lane's 8 token values of its channel pair for a stage; the next stage's load is
+  // in flight during this stage's matrix work
+  uint32_t d[8];
+  auto load_stage = [&](int t0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = t0 + 8 * wave + e;
+      d[e] = (pair_ok && t < t_end) ? *(const uint32_t*)(X + (size_t)t * K + c0 + 2 * lane)
+                                    : 0u;
+    }
+  };
+  if (t_begin < t_end) load_stage(t_begin);
   for (int t0 = t_begin; t0 < t_end; t0 += kGramStage) {
     {
-      uint32_t d[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = t0 + 8 * wave + e;
-        d[e] = (pair_ok && t < t_end) ? *(const uint32_t*)(X + (size_t)t * K + c0 + 2 * lane)
-                                      : 0u;
-      }
       uint2 lo0, lo1, hi0, hi1;  // channel 2 l (low halves) and 2 l + 1 (high halves)
       lo0.x = __builtin_amdgcn_perm(d[1], d[0], 0x05040100u);
       lo0.y = __builtin_amdgcn_perm(d[3], d[2], 0x05040100u);
@@ -122,6 +127,7 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_mfma(const uint16_t* __re
       *(uint2*)(r0 + kGramXtp + 4) = hi1;
     }
     __syncthreads();
+    if (t0 + kGramStage < t_end) load_stage(t0 + kGramStage);
     if (active) {
       auto frag = [&](int blk, int ks) {
         const uint16_t* src = xt + (16 * blk + pl) * kGramXtp + 32 * ks + 8 * q4;
@@ -163,7 +169,7 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_mfma(const uint16_t* __re
     }
 }
 
-constexpr int kGramChunk = 1024;  // Gram entries per block of the two passes below
+constexpr int kGramChunk = 256;  // Gram entries per block of the two passes below (one a thread)
 
 __device__ __forceinline__ double nan_max64(double m, double a) {
   return (a > m || a != a) ? a : m;
@@ -187,11 +193,20 @@ __global__ __launch_bounds__(256) void k_gram_sum(const float* __restrict__ part
   const int n = (int)min((size_t)kGramChunk, gg - (size_t)c * kGramChunk);
   double m = 0.0;
   for (int i = tid; i < n; i += 256) {
-    double v = (double)partials[base + i];
-    for (int sp = 1; sp < splits; ++sp) v += (double)partials[sp * stride + base + i];
+    // sixteen independent loads at a time, added in split order
+    double v = 0.0;
+    for (int sp0 = 0; sp0 < splits; sp0 += 16) {
+      float p[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        p[u] = sp0 + u < splits ? partials[(size_t)(sp0 + u) * stride + base + i] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (sp0 + u < splits) v += (double)p[u];
+    }
     const int e = c * kGramChunk + i;  // entry (a, b) of the group's matrix
     const int a = e / g, b = e - (e / g) * g;
-    v = v / (double)s[j * g + a] / (double)s[j * g + b];
+    v = v / ((double)s[j * g + a] * (double)s[j * g + b]);  // (the fp32 product is exact)
     G64[base + i] = v;
     m = nan_max64(m, fabs(v));
   }
@@ -212,10 +227,15 @@ __global__ __launch_bounds__(256) void k_gram_split(const double* __restrict__ G
                                                     uint16_t* __restrict__ Ghi,
                                                     uint16_t* __restrict__ Glo,
                                                     int32_t* __restrict__ gexp) {
-  const int j = blockIdx.x, c = blockIdx.y, nc = gridDim.y;
+  __shared__ double red[4];
+  const int j = blockIdx.x, c = blockIdx.y, nc = gridDim.y;  // nc = g * g / 256 <= 64
   const int tid = threadIdx.x;
-  double top = 0.0;
-  for (int q = 0; q < nc; ++q) top = nan_max64(top, cmax[(size_t)j * nc + q]);
+  double top = tid < nc ? cmax[(size_t)j * nc + tid] : 0.0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) top = nan_max64(top, __shfl_xor(top, o));
+  if ((tid & 63) == 0) red[tid >> 6] = top;
+  __syncthreads();
+  top = nan_max64(nan_max64(red[0], red[1]), nan_max64(red[2], red[3]));
   int ex = 0;
   if (top > 0.0 && top < INFINITY) {
     int e2;
