@@ -31,6 +31,11 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source additions.  The clip-search kernels keep their small MFMA accumulators in
+# VGPRs (no accumulator-register moves in the epilogue); the large-tile GEMMs need AGPRs.
+HIP_FILE_FLAGS = {
+    "clip_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
               f"-I{ROCM}/include"]
 
@@ -58,7 +63,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         src = os.path.join(CSRC, f)
         obj = os.path.join(BUILD, f + ".o")
         if f.endswith(".hip"):
-            jobs_list.append([hipcc, *HIP_FLAGS, *incs, "-c", src, "-o", obj])
+            jobs_list.append([hipcc, *HIP_FLAGS, *HIP_FILE_FLAGS.get(f, []), *incs, "-c", src,
+                              "-o", obj])
         elif f.endswith(".cpp"):
             jobs_list.append([clangxx, *HOST_FLAGS, *incs, "-c", src, "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
