@@ -25,6 +25,7 @@ constexpr int kRowsFQ = 8;    // rows per block, fake quantisation
 constexpr int kRowsPack = 8;  // rows per block, packing
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void unpack8(const u32x4& r, float (&w)[8]) {
 #pragma unroll
@@ -54,56 +55,154 @@ __global__ __launch_bounds__(kThreads) void k_make_scales(const float* __restric
   s_table[(size_t)k * K + i] = s;
 }
 
-template <int LANES>
+// Cross-lane max / min over aligned groups of L lanes (2, 4 or 8) with DPP moves: a
+// half-row mirror (i <-> 7 - i) leaves every group member's value in each quad, then quad
+// swaps finish the reduction.
+template <int L>
+__device__ __forceinline__ float gmax_lanes(float x) {
+  static_assert(L == 2 || L == 4 || L == 8, "group of 2, 4 or 8 lanes");
+  if constexpr (L == 8) x = fmaxf(x, dpp_mov<kDppRowHalfMirror>(x));
+  if constexpr (L >= 4) x = fmaxf(x, dpp_mov<kDppQuadXor2>(x));
+  return fmaxf(x, dpp_mov<kDppQuadXor1>(x));
+}
+template <int L>
+__device__ __forceinline__ float gmin_lanes(float x) {
+  static_assert(L == 2 || L == 4 || L == 8, "group of 2, 4 or 8 lanes");
+  if constexpr (L == 8) x = fminf(x, dpp_mov<kDppRowHalfMirror>(x));
+  if constexpr (L >= 4) x = fminf(x, dpp_mov<kDppQuadXor2>(x));
+  return fminf(x, dpp_mov<kDppQuadXor1>(x));
+}
+
+// dW_k = (v - Q(v)) / s for every grid point k, v = w s_k.  A lane owns 16 consecutive
+// input channels (a group is g / 16 lanes) of kRowsFQ rows, keeps the rows' weights as
+// fp16 pairs in registers and reuses them for every k; the next grid point's scales load
+// during the current one.  The quantiser is the pack's (quantize8) in a leaner form: the
+// code relative to the zero, c - z = clamp(rint(v / step), -z, top - z) (or
+// +-qmax), comes from one med3; v / step is v * rcp(step) unless a quotient of the row (or
+// -lo / step) lies within 2^-17 of a half-integer or is not finite, in which case the
+// lane redoes the row with the correctly rounded divisions -- the same integers either way.
+// The error v - (c - z) step is one fused multiply-add, multiplied by rcp(s) (the error
+// only enters the fp16 loss product) and rounded once to fp16.
+template <int LANES, bool ZP>
 __global__ __launch_bounds__(kThreads) void k_fake_quant_delta(
     const uint16_t* __restrict__ W, const float* __restrict__ s_table, int M, int K, int nb,
-    int w_bit, int zero_point, uint16_t* __restrict__ dW) {
+    int w_bit, uint16_t* __restrict__ dW) {
   const int chunk = blockIdx.x * kThreads + threadIdx.x;
-  const int col0 = chunk * 8;
+  const int col0 = chunk * 16;
   const bool col_ok = col0 < K;
   const int row0 = blockIdx.y * kRowsFQ;
   const int nrows = min(kRowsFQ, M - row0);
-  const bool zp = zero_point != 0;
 
-  float w[kRowsFQ][8];
+  uint32_t w[kRowsFQ][8];  // fp16 pairs (channel 2 i low, 2 i + 1 high)
 #pragma unroll
   for (int r = 0; r < kRowsFQ; ++r) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (col_ok && r < nrows) raw = *(const u32x4*)(W + (size_t)(row0 + r) * K + col0);
-    unpack8(raw, w[r]);
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (col_ok && r < nrows) {
+      const u32x4* src = (const u32x4*)(W + (size_t)(row0 + r) * K + col0);
+      a = src[0];
+      b = src[1];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[r][q] = a[q];
+      w[r][4 + q] = b[q];
+    }
   }
+  const float top = (float)((1 << w_bit) - 1);
+  const float qmax = (float)((1 << (w_bit - 1)) - 1);
+  float4 sn[4];
+  auto load_s = [&](int k) {
+    const float4* sp = (const float4*)(s_table + (size_t)k * K + col0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sn[q] = col_ok ? sp[q] : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+  };
+  load_s(0);
 
   for (int k = 0; k < nb; ++k) {
-    float s[8], inv[8];
-    if (col_ok) {
-      const float4* sp = (const float4*)(s_table + (size_t)k * K + col0);
-      const float4 s0 = sp[0], s1 = sp[1];
-      s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w;
-      s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
-    } else {
+    float s[16], is[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s[i] = 1.0f;
+    for (int q = 0; q < 4; ++q) {
+      s[4 * q] = sn[q].x;
+      s[4 * q + 1] = sn[q].y;
+      s[4 * q + 2] = sn[q].z;
+      s[4 * q + 3] = sn[q].w;
     }
-    // 1/s only enters the weight error fed to the fp16 loss product (not the codes), so
-    // the hardware reciprocal (1 ulp) is accurate enough.
+    if (k + 1 < nb) load_s(k + 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) inv[i] = __builtin_amdgcn_rcpf(s[i]);
+    for (int i = 0; i < 16; ++i) is[i] = __builtin_amdgcn_rcpf(s[i]);
 
     uint16_t* out = dW + (size_t)k * M * K;
 #pragma unroll
     for (int r = 0; r < kRowsFQ; ++r) {
       if (r >= nrows) break;  // uniform across the block
-      float v[8], code[8], st, z;
+      float v[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = w[r][i] * s[i];
-      quantize8<LANES>(v, w_bit, zp, code, st, z);
-      float e[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float d = (code[i] - z) * st;   // quantised scaled weight
-        e[i] = (v[i] - d) * inv[i];           // weight error, W - Q(W s)/s = (v - d)/s
+      for (int i = 0; i < 16; ++i) {
+        const _Float16 wh =
+            __builtin_bit_cast(_Float16, (uint16_t)(w[r][i >> 1] >> (16 * (i & 1))));
+        v[i] = fmaf((float)wh, s[i], 0.0f);  // = w s (a zero's sign is immaterial)
       }
-      if (col_ok) *(u32x4*)(out + (size_t)(row0 + r) * K + col0) = pack8(e);
+      float hi = v[0], lo = v[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) {
+        hi = fmaxf(hi, v[i]);
+        lo = fminf(lo, v[i]);
+      }
+      hi = gmax_lanes<LANES>(hi);
+      lo = gmin_lanes<LANES>(lo);
+      float st, clo, chi, lr = 0.0f;
+      bool need;
+      if constexpr (ZP) {
+        const float hr = fmaxf(hi, 0.0f);
+        lr = fminf(lo, 0.0f);
+        st = (hr - lr) / top;
+        if (st == 0.0f) st = 1.0f;
+        const float tz = -lr * __builtin_amdgcn_rcpf(st);
+        const float z = rintf(tz);
+        need = !(fabsf(tz - z) < 0.5f - kTieBand);
+        const float zc = __builtin_amdgcn_fmed3f(z, 0.0f, top);
+        clo = -zc;
+        chi = top - zc;
+      } else {
+        st = fmaxf(fabsf(hi), fabsf(lo)) / qmax;
+        if (st == 0.0f) st = 1.0f;
+        clo = -qmax;
+        chi = qmax;
+        need = false;
+      }
+      const float inv = __builtin_amdgcn_rcpf(st);
+      float cz[16];
+      float dist = 0.0f;  // the largest |t - rint t| of the row (a NaN one leaves the errors NaN)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float t0 = v[i] * inv, t1 = v[i + 1] * inv;
+        const float q0 = rintf(t0), q1 = rintf(t1);
+        dist = fmaxf(dist, fmaxf(fabsf(t0 - q0), fabsf(t1 - q1)));
+        cz[i] = __builtin_amdgcn_fmed3f(q0, clo, chi);
+        cz[i + 1] = __builtin_amdgcn_fmed3f(q1, clo, chi);
+      }
+      need |= !(dist < 0.5f - kTieBand);
+      if (need) {  // rare: the correctly rounded divisions
+        if constexpr (ZP) {
+          const float zc = __builtin_amdgcn_fmed3f(rintf(-lr / st), 0.0f, top);
+          clo = -zc;
+          chi = top - zc;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cz[i] = __builtin_amdgcn_fmed3f(rintf(v[i] / st), clo, chi);
+      }
+      if (col_ok) {
+        uint32_t e[8];
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const half2_t ep = {(_Float16)(fmaf(-cz[i], st, v[i]) * is[i]),
+                              (_Float16)(fmaf(-cz[i + 1], st, v[i + 1]) * is[i + 1])};
+          e[i >> 1] = __builtin_bit_cast(uint32_t, ep);
+        }
+        u32x4* dst = (u32x4*)(out + (size_t)(row0 + r) * K + col0);
+        dst[0] = u32x4{e[0], e[1], e[2], e[3]};
+        dst[1] = u32x4{e[4], e[5], e[6], e[7]};
+      }
     }
   }
 }
@@ -173,24 +272,22 @@ hipError_t launch_fake_quant_delta(const uint16_t* W, const float* s_table, int 
                                    int nb, int w_bit, int group_size, int zero_point,
                                    uint16_t* dW, hipStream_t stream) {
   if (M <= 0 || K <= 0 || nb <= 0) return hipSuccess;
-  const int chunks = K / 8;
+  const int chunks = K / 16;
   dim3 grid((chunks + kThreads - 1) / kThreads, (M + kRowsFQ - 1) / kRowsFQ);
+#define AWQ_FQ(L)                                                                         \
+  if (zero_point)                                                                         \
+    hipLaunchKernelGGL((k_fake_quant_delta<L, true>), grid, dim3(kThreads), 0, stream, W,  \
+                       s_table, M, K, nb, w_bit, dW);                                     \
+  else                                                                                    \
+    hipLaunchKernelGGL((k_fake_quant_delta<L, false>), grid, dim3(kThreads), 0, stream, W, \
+                       s_table, M, K, nb, w_bit, dW)
   switch (group_size) {
-    case 32:
-      hipLaunchKernelGGL(k_fake_quant_delta<4>, grid, dim3(kThreads), 0, stream, W, s_table,
-                         M, K, nb, w_bit, zero_point, dW);
-      break;
-    case 64:
-      hipLaunchKernelGGL(k_fake_quant_delta<8>, grid, dim3(kThreads), 0, stream, W, s_table,
-                         M, K, nb, w_bit, zero_point, dW);
-      break;
-    case 128:
-      hipLaunchKernelGGL(k_fake_quant_delta<16>, grid, dim3(kThreads), 0, stream, W, s_table,
-                         M, K, nb, w_bit, zero_point, dW);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 32: AWQ_FQ(2); break;
+    case 64: AWQ_FQ(4); break;
+    case 128: AWQ_FQ(8); break;
+    default: return hipErrorInvalidValue;
   }
+#undef AWQ_FQ
   return hipGetLastError();
 }
 
