@@ -4,11 +4,12 @@
 // weight, divide back); "AWQ量化" tutorial 缩放保护 (W_hat = Q(s W) / s); kwkr.cn AWQ
 // 技术解析 §1.2, §2.1, §4.2 (int4 codes with fp16 scales, two codes per byte).
 //
-// Layout of work: a block of 256 threads owns a stripe of 256 column chunks (8 input
-// channels each, 2048 channels) and ROWS consecutive output rows.  Each thread keeps its
-// 8 scales (and their reciprocals) in registers and reuses them for all ROWS rows, so
-// the per-element traffic is the fp16 weight read and the fp16 result write, both as
-// 16-byte coalesced accesses.  Groups of g channels are g/8 consecutive lanes.
+// Layout of work: a block of 256 threads owns a stripe of column chunks and a few output
+// rows.  The fake quantisation gives each lane 16 input channels of 8 rows (weights kept
+// in registers and reused for every grid point); the pack gives each lane 8 channels
+// (quantize8).  Either way a lane keeps its scales in registers, the per-element traffic
+// is the fp16 weight read and the fp16 (or 4-bit) write as 16-byte coalesced accesses,
+// and a group of g channels is g/16 (g/8) consecutive lanes.
 #include <hip/hip_runtime.h>
 
 #include "awq_internal.h"
