@@ -52,7 +52,8 @@ def _check_clip(res, W16, X16, s32, cfg, ratios, rows, where):
     bg = host(res["best"])[rows]
     bo = orc["best"]
     srt = np.sort(eo, axis=0)
-    gap = (srt[1] - srt[0]) / np.maximum(srt[0], 1e-300) if len(ratios) > 1 else np.inf
+    gap = ((srt[1] - srt[0]) / np.maximum(srt[0], 1e-300) if len(ratios) > 1
+           else np.full(eo.shape[1:], np.inf))
     clear = gap > 1e-3
     assert np.array_equal(bg[clear], bo[clear]), (where, int((bg[clear] != bo[clear]).sum()))
     mm, jj = np.nonzero(~clear)
@@ -88,6 +89,22 @@ def test_clip_search_parity(M, K, N, w_bit, g, zp):
     clear, total = _check_clip(res, L.W, L.X, s, ocfg(cfg), RATIOS, np.arange(M),
                                f"{M}x{K}x{N}")
     say(f"  decided by a clear margin: {clear} of {total}")
+
+
+@pytest.mark.parametrize("n_ratio,M,K,N,g", [(1, 37, 256, 90, 128), (64, 23, 192, 140, 64),
+                                              (7, 161, 96, 70, 32)])
+def test_clip_ratio_counts(n_ratio, M, K, N, g):
+    """One ratio, the largest grid (64), and a grid that leaves a partial 16-pair slice,
+    on layers whose 128-channel Gram spans run past in_features (K = 192 and 96)."""
+    say(f"clip n_ratio={n_ratio} M={M} K={K} N={N} g={g}")
+    L = make_layer(small_spec("r", M, K, N, group_size=g, outlier_count=2, seed=n_ratio + M))
+    rng = np.random.default_rng(n_ratio)
+    s = np.exp(rng.uniform(-1.0, 1.0, K)).astype(F32)
+    ratios = (1.0 - np.arange(n_ratio) * (0.6 / max(1, n_ratio - 1))).astype(F32)
+    cfg = awq.qconfig(4, g, 1)
+    res = awq.awq_clip_search(dev(L.W), dev(L.X), dev(s), ratios, cfg, want_errors=True)
+    torch.cuda.synchronize()
+    _check_clip(res, L.W, L.X, s, ocfg(cfg), ratios, np.arange(M), f"n={n_ratio}")
 
 
 def test_clip_wide_dynamic_range():
