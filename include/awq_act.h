@@ -217,12 +217,23 @@ int awq_quantize_pack_clipped(const void* W, const float* s, const float* clip,
  *            awq_quantize_pack (zeros must hold integers in [0, 15]); codes 16-byte aligned
  *   cfg      only group_size is read (codes occupy 4-bit slots for every w_bit)
  *   y        fp16 [n_tokens][out], device (written)
+ *   workspace  device, 16-byte aligned, or NULL; with s given and n_tokens >= 2, a
+ *            workspace of at least awq_w4a16_workspace_bytes(n_tokens, in) bytes makes the
+ *            call write xt there first (one elementwise pass) and multiply with the
+ *            matrix-core kernel; NULL or 0 bytes keeps the vector kernel, which forms xt in
+ *            registers.  Both give the same xt; the sums may differ in rounding order.
+ *            Nonzero but smaller than needed: AWQ_E_WORKSPACE.  Owned by the caller; its
+ *            contents after the call are unspecified.
  * fp32 accumulation in a fixed order (bitwise repeatable), rounded to fp16 once.
  * in_features <= 32768; n_tokens >= 0 (0 enqueues nothing); in_features = 0 gives y = 0.
  * ---------------------------------------------------------------------------------- */
 int awq_w4a16_matmul(const void* x, const float* s, int64_t n_tokens, const void* codes,
                      const void* scales, const void* zeros, int64_t out_features,
-                     int64_t in_features, const awq_qconfig* cfg, void* y, void* stream);
+                     int64_t in_features, const awq_qconfig* cfg, void* y, void* workspace,
+                     size_t workspace_bytes, void* stream);
+/* Bytes of workspace for awq_w4a16_matmul's fold of x / s: 2 n_tokens in_features rounded
+ * up to 256, or 0 when the fold is never taken (n_tokens < 2, or shapes out of range). */
+size_t awq_w4a16_workspace_bytes(int64_t n_tokens, int64_t in_features);
 
 /* ------------------------------------------------------------------------------------
  * A3 alone: dW = W - Q(W diag(s)) diag(s)^-1 rounded to fp16, the operand the search's

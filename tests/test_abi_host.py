@@ -36,7 +36,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in awq_act.h but not exported"
     assert set(names) == set(_lib._SIGNATURES)
@@ -203,8 +203,10 @@ def test_table_threshold_hadamard_validation(L):
 def test_w4a16_validation(L):
     f = L.awq_w4a16_matmul
 
-    def call(x=P, s=None, T=2, c=P, sc=P, z=P, M=64, K=256, cfg=None, y=P):
-        return f(x, s, T, c, sc, z, M, K, cfg if cfg is not None else _cfg(), y, None)
+    def call(x=P, s=None, T=2, c=P, sc=P, z=P, M=64, K=256, cfg=None, y=P, ws=None,
+             ws_bytes=0):
+        return f(x, s, T, c, sc, z, M, K, cfg if cfg is not None else _cfg(), y, ws, ws_bytes,
+                 None)
 
     assert call(x=None) == E["NULL"] and call(c=None) == E["NULL"] and call(y=None) == E["NULL"]
     assert call(cfg=_cfg(4, 48)) == E["CONFIG"]
@@ -216,6 +218,15 @@ def test_w4a16_validation(L):
     assert call(s=ctypes.c_void_p(0x10004)) == E["ALIGN"]
     assert call(y=ctypes.c_void_p(0x10001)) == E["ALIGN"]
     assert call(T=0) == E["OK"] and call(M=0) == E["OK"]
+    # the fold workspace: 2 T K bytes rounded to 256, none below two tokens
+    need = awq.awq_w4a16_workspace_bytes(3, 256)
+    assert need == 1536 and awq.awq_w4a16_workspace_bytes(1, 256) == 0
+    assert awq.awq_w4a16_workspace_bytes(2, 32768 + 32) == 0
+    assert call(s=P, T=3, ws=P, ws_bytes=need - 1, M=0) == E["WORKSPACE"]
+    assert call(s=P, T=3, ws=ctypes.c_void_p(0x10008), ws_bytes=need) == E["ALIGN"]
+    assert call(s=P, T=3, ws=P, ws_bytes=need, M=0) == E["OK"]
+    assert call(s=None, T=3, ws=P, ws_bytes=1, M=0) == E["OK"]    # no s: the workspace is unused
+    assert call(s=P, T=1, ws=P, ws_bytes=1, M=0) == E["OK"]       # one token: never folded
 
 
 def test_clip_validation(L):

@@ -64,6 +64,8 @@ CASES = [
     (40, 1024, 9, 64, True),        # three passes
     (9, 32768, 2, 128, False),      # the largest K: 1024 threads
     (33, 32, 1, 32, True),          # a single chunk
+    (70, 4096, 4, 128, True),       # s given, several tokens: the fold, then the matrix cores
+    (48, 1024, 21, 64, True),       # the same over two token passes
     # folded activations, several tokens: the matrix-core kernel
     (100, 1024, 16, 32, False),
     (50, 2048, 16, 64, False),
@@ -86,6 +88,17 @@ def test_w4a16_random_codes(M, K, T, g, with_s):
                              s=dev(s) if with_s else None)
     r = _check(host(y), packed, scales, zeros, X, g, s, f"{M}x{K}x{T}")
     say(f"  max err / bound {r:.3f}")
+    if with_s and T >= 2:
+        # the default call folds x / s into a workspace and takes the matrix-core kernel;
+        # an empty workspace keeps the vector kernel, which must meet the same bound
+        y2 = awq.awq_w4a16_matmul(dev(X), dev(packed), dev(scales), dev(zeros), cfg, s=dev(s),
+                                  workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+        _check(host(y2), packed, scales, zeros, X, g, s, f"{M}x{K}x{T} vector kernel")
+        # the fold is the oracle's x~ bit for bit: the same kernel on the oracle's x~ gives
+        # the same bits
+        y3 = awq.awq_w4a16_matmul(dev(O.fold_inverse_scales(X, s)), dev(packed), dev(scales),
+                                  dev(zeros), cfg)
+        assert np.array_equal(host(y).view(np.uint16), host(y3).view(np.uint16))
 
 
 def test_w4a16_degenerate():

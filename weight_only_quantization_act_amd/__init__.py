@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     awq_search_scale_table,
     awq_threshold_scales,
     awq_w4a16_matmul,
+    awq_w4a16_workspace_bytes,
     awq_fake_quant_delta,
     awq_quantize_pack,
     awq_search_scales,

@@ -57,7 +57,8 @@ _SIGNATURES = {
                                             _vp]),
     "awq_hadamard_rotate": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
     "awq_w4a16_matmul": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _cfgp, _vp,
-                                        _vp]),
+                                        _vp, _sz, _vp]),
+    "awq_w4a16_workspace_bytes": (_sz, [_i64, _i64]),
     "awq_clip_workspace_bytes": (_sz, [_i64, _i64, _i64, _cfgp]),
     "awq_clip_search": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _cfgp, _vp, _i32, _vp,
                                        _vp, _vp, _vp, _sz, _vp]),
@@ -317,10 +318,18 @@ def awq_hadamard_rotate(A: torch.Tensor, block: int, out: Optional[torch.Tensor]
     return out
 
 
+def awq_w4a16_workspace_bytes(n_tokens: int, in_features: int) -> int:
+    return int(lib().awq_w4a16_workspace_bytes(n_tokens, in_features))
+
+
 def awq_w4a16_matmul(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
                      zeros: torch.Tensor, cfg: awq_qconfig, s: Optional[torch.Tensor] = None,
-                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """y [T, M] fp16 = x~ [T, K] times the dequantised packed weights (x~ = x / s if s)."""
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """y [T, M] fp16 = x~ [T, K] times the dequantised packed weights (x~ = x / s if s).
+
+    With s given and two or more tokens a workspace for the fold of x / s is allocated
+    unless one is passed; an empty workspace keeps the vector kernel."""
     _dev(x, torch.float16, "x")
     if x.dim() != 2:
         raise ValueError("x must be 2-D [n_tokens, in_features]")
@@ -340,8 +349,15 @@ def awq_w4a16_matmul(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
     pc = _ptr(codes) if K else _ptr(dummy)
     ps = _ptr(scales) if K else _ptr(dummy)
     pz = _ptr(zeros) if K else _ptr(dummy)
+    if workspace is None and s is not None:
+        need = awq_w4a16_workspace_bytes(T, K)
+        workspace = _buf(need, x.device) if need else None
+    pw, nw = None, 0
+    if workspace is not None and workspace.numel() > 0:
+        _dev(workspace, torch.uint8, "workspace")
+        pw, nw = _ptr(workspace), workspace.numel()
     st = lib().awq_w4a16_matmul(px, _ptr(s) if (s is not None and K) else None, T, pc, ps, pz,
-                                M, K, ctypes.byref(cfg), _ptr(y), _stream_ptr(stream))
+                                M, K, ctypes.byref(cfg), _ptr(y), pw, nw, _stream_ptr(stream))
     _check(st, "awq_w4a16_matmul")
     return y
 

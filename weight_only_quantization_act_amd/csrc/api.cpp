@@ -298,9 +298,17 @@ int awq_hadamard_rotate(const void* A, int64_t rows, int64_t in_features, int32_
                                          (uint16_t*)out, (hipStream_t)stream));
 }
 
+size_t awq_w4a16_workspace_bytes(int64_t n_tokens, int64_t in_features) {
+  if (n_tokens < awq::kW4a16MfmaMinT || in_features <= 0 || in_features > awq::kGemvMaxK ||
+      n_tokens >= kMaxElems / in_features)
+    return 0;
+  return round_up((size_t)n_tokens * (size_t)in_features * sizeof(uint16_t), kAlign);
+}
+
 int awq_w4a16_matmul(const void* x, const float* s, int64_t n_tokens, const void* codes,
                      const void* scales, const void* zeros, int64_t out_features,
-                     int64_t in_features, const awq_qconfig* cfg, void* y, void* stream) {
+                     int64_t in_features, const awq_qconfig* cfg, void* y, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   const int64_t T = n_tokens, M = out_features, K = in_features;
   if (!x || !codes || !scales || !zeros || !cfg || !y) return AWQ_E_NULL;
   if (!cfg_valid(cfg)) return AWQ_E_CONFIG;
@@ -311,13 +319,27 @@ int awq_w4a16_matmul(const void* x, const float* s, int64_t n_tokens, const void
     return AWQ_E_SHAPE;
   if (K > awq::kGemvMaxK) return AWQ_E_SHAPE;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2) ||
-      !aligned(y, 2) || (s && !aligned(s, 16)))
+      !aligned(y, 2) || (s && !aligned(s, 16)) || !aligned(workspace, 16))
     return AWQ_E_ALIGN;
+  // the fold into the workspace is taken only when it helps: s given, several tokens
+  const bool fold = s && workspace && workspace_bytes > 0 && T >= awq::kW4a16MfmaMinT && K > 0;
+  if (fold && workspace_bytes < awq_w4a16_workspace_bytes(T, K)) return AWQ_E_WORKSPACE;
   if (T == 0 || M == 0) return AWQ_OK;
   if ((st = device_ptr(x)) || (st = device_ptr(codes)) || (st = device_ptr(scales)) ||
       (st = device_ptr(zeros)) || (st = device_ptr(y)))
     return st;
   if (s && (st = device_ptr(s))) return st;
+  if (fold) {
+    if ((st = device_ptr(workspace))) return st;
+    uint16_t* xt = (uint16_t*)workspace;
+    if ((st = hip_status(awq::launch_fold_inverse_scales((const uint16_t*)x, s, (int)T, (int)K,
+                                                         xt, (hipStream_t)stream))))
+      return st;
+    return hip_status(awq::launch_w4a16_gemv((const uint8_t*)codes, (const uint16_t*)scales,
+                                             (const uint16_t*)zeros, xt, nullptr, (int)T,
+                                             (int)M, (int)K, cfg->group_size, (uint16_t*)y,
+                                             (hipStream_t)stream));
+  }
   return hip_status(awq::launch_w4a16_gemv((const uint8_t*)codes, (const uint16_t*)scales,
                                            (const uint16_t*)zeros, (const uint16_t*)x, s,
                                            (int)T, (int)M, (int)K, cfg->group_size,

@@ -94,6 +94,9 @@ int w4a16_mfma_waves(int64_t M, int64_t K, int group_size);
 hipError_t launch_w4a16_gemv(const uint8_t* codes, const uint16_t* scales,
                              const uint16_t* zeros, const uint16_t* x, const float* s, int T,
                              int M, int K, int group_size, uint16_t* y, hipStream_t stream);
+// x~ [T][K] fp16 = fp16(fp32(x) / s) per element (K a multiple of 8).
+hipError_t launch_fold_inverse_scales(const uint16_t* x, const float* s, int T, int K,
+                                      uint16_t* out, hipStream_t stream);
 
 // ---- loss product and selection ------------------------------------------------------
 // partials[k * tiles + tm * tiles_n + tn] = sum over the tile of (dW_k X^T)^2.

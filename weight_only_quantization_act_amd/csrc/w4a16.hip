@@ -442,6 +442,29 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void k_w4a16_mfma(
   }
 }
 
+// x~[t][c] = fp16(fp32(x[t][c]) / s[c]): one correctly rounded fp32 division, then one
+// rounding to fp16 -- the fold the product applies when s is given.  Eight channels a
+// thread (in_features is a multiple of 32).
+__global__ __launch_bounds__(256) void k_fold_inverse_scales(const uint16_t* __restrict__ x,
+                                                             const float* __restrict__ s,
+                                                             int64_t n8, int K,
+                                                             uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 8-channel chunk
+  if (i >= n8) return;
+  const int c0 = (int)((i * 8) % K);
+  const u32x4 r = *(const u32x4*)(x + i * 8);
+  const f32x4 s0 = *(const f32x4*)(s + c0), s1 = *(const f32x4*)(s + c0 + 4);
+  const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint16_t lo = f2h(h2f((uint16_t)(r[j] & 0xffffu)) / sv[2 * j]);
+    const uint16_t hi = f2h(h2f((uint16_t)(r[j] >> 16)) / sv[2 * j + 1]);
+    o[j] = (uint32_t)lo | ((uint32_t)hi << 16);
+  }
+  *(u32x4*)(out + i * 8) = o;
+}
+
 }  // namespace
 
 GemvPlan w4a16_gemv_plan(int64_t M, int64_t K) {
@@ -524,6 +547,20 @@ hipError_t launch_w4a16_gemv(const uint8_t* codes, const uint16_t* scales,
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace awq
+
+namespace awq {
+
+hipError_t launch_fold_inverse_scales(const uint16_t* x, const float* s, int T, int K,
+                                      uint16_t* out, hipStream_t stream) {
+  const int64_t n8 = (int64_t)T * K / 8;
+  if (n8 <= 0) return hipSuccess;
+  if (K % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_fold_inverse_scales, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                     stream, x, s, n8, K, out);
+  return hipGetLastError();
 }
 
 }  // namespace awq
