@@ -145,6 +145,10 @@ SEARCH_CASES = [
     (520, 512, 1, 4, 64, 0),        # one token
     (64, 1024, 515, 2, 128, 0),
     (1024, 640, 300, 3, 64, 1),
+    # many more tokens than channels: the loss through G = X^T X
+    (300, 256, 3000, 4, 128, 1),
+    (130, 320, 5000, 3, 32, 0),     # 128-channel Gram spans cut at in_features
+    (64, 1024, 8192, 4, 128, 1),
 ]
 
 

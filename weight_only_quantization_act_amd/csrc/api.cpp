@@ -52,19 +52,39 @@ int device_ptr(const void* p) {
   return AWQ_E_DEVICE;
 }
 
+// Workspace of the search: s table | loss partials | (Gram form: fp32 G, G_hi, G_lo, tile
+// maxima, exponent) | dW batch.
 struct SearchLayout {
   size_t s_off, p_off, dw_off;
+  size_t g32_off, ghi_off, glo_off, tmax_off, gexp_off;
   size_t dw_bytes_per_alpha;
   int64_t tiles;
+  bool gram;
 };
 
 SearchLayout search_layout(int64_t M, int64_t K, int64_t N, int32_t n_alpha) {
   SearchLayout L;
   const bool work = (M > 0 && K > 0);
-  L.tiles = work ? awq::loss_tiles_m(M) * awq::loss_tiles_n(N) : 0;
+  L.gram = work && awq::loss_use_gram(M, K, N, n_alpha);
+  L.tiles = work ? awq::loss_tiles_m(M) * awq::loss_tiles_n(L.gram ? K : N) : 0;
   L.s_off = 0;
   L.p_off = round_up((size_t)n_alpha * (size_t)K * sizeof(float), kAlign);
-  L.dw_off = L.p_off + round_up((size_t)n_alpha * (size_t)L.tiles * sizeof(double), kAlign);
+  size_t off = L.p_off + round_up((size_t)n_alpha * (size_t)L.tiles * sizeof(double), kAlign);
+  L.g32_off = L.ghi_off = L.glo_off = L.tmax_off = L.gexp_off = off;
+  if (L.gram) {
+    const size_t kk = (size_t)K * (size_t)K;
+    L.g32_off = off;
+    off += round_up(kk * sizeof(float), kAlign);
+    L.ghi_off = off;
+    off += round_up(kk * sizeof(uint16_t), kAlign);
+    L.glo_off = off;
+    off += round_up(kk * sizeof(uint16_t), kAlign);
+    L.tmax_off = off;
+    off += round_up((size_t)awq::gram_full_tiles(K) * sizeof(float), kAlign);
+    L.gexp_off = off;
+    off += kAlign;
+  }
+  L.dw_off = off;
   L.dw_bytes_per_alpha = work ? (size_t)M * (size_t)K * 2 : 0;
   return L;
 }
@@ -106,6 +126,16 @@ int run_search(const void* W, const void* X, const float* s_table, int64_t M, in
   }
   int st;
   if (L.tiles > 0) {
+    uint16_t* Ghi = (uint16_t*)(ws + L.ghi_off);
+    uint16_t* Glo = (uint16_t*)(ws + L.glo_off);
+    int32_t* gexp = (int32_t*)(ws + L.gexp_off);
+    if (L.gram) {  // G = X^T X once, for every grid point
+      if ((st = record(hook.gemm_start, sm))) return st;
+      st = hip_status(awq::launch_gram_full((const uint16_t*)X, (int)N, (int)K,
+                                            (float*)(ws + L.g32_off),
+                                            (float*)(ws + L.tmax_off), Ghi, Glo, gexp, sm));
+      if (st) return st;
+    }
     for (int k0 = 0; k0 < nc; k0 += batch) {
       const int nb = nc - k0 < batch ? nc - k0 : batch;
       const bool first = (k0 == 0);
@@ -115,9 +145,13 @@ int run_search(const void* W, const void* X, const float* s_table, int64_t M, in
                                                    cfg->group_size, cfg->zero_point, dW, sm));
       if (st) return st;
       if (first && (st = record(hook.fq_stop, sm))) return st;
-      if (first && (st = record(hook.gemm_start, sm))) return st;
-      st = hip_status(awq::launch_loss_gemm(dW, (const uint16_t*)X, (int)M, (int)N, (int)K, nb,
-                                            partials + (size_t)k0 * L.tiles, sm));
+      if (first && !L.gram && (st = record(hook.gemm_start, sm))) return st;
+      if (L.gram)
+        st = hip_status(awq::launch_loss_gemm_gram(dW, Ghi, Glo, gexp, (int)M, (int)K, nb,
+                                                   partials + (size_t)k0 * L.tiles, sm));
+      else
+        st = hip_status(awq::launch_loss_gemm(dW, (const uint16_t*)X, (int)M, (int)N, (int)K,
+                                              nb, partials + (size_t)k0 * L.tiles, sm));
       if (st) return st;
     }
     if ((st = record(hook.gemm_stop, sm))) return st;

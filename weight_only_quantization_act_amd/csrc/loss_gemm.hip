@@ -137,10 +137,16 @@ struct Stage {
   }
 };
 
-template <class S>
+// GRAM = false: C = dW_k X^T (X fp16 [N][K]) and the tile's sum of squares.
+// GRAM = true:  C = dW_k (G_hi + G_lo) with G 2^-gexp = G_hi + G_lo fp16 [K][K] (B0, B1;
+// N = K, symmetric, so rows serve as the K-contiguous operand): the K loop runs twice,
+// first over G_hi then over G_lo with the same dW_k, and the tile's sum of C * dW_k at the
+// same positions, times 2^gexp, is the tile's share of sum_r dW_r G dW_r^T.
+template <class S, bool GRAM>
 __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
-    const uint16_t* __restrict__ dW, const uint16_t* __restrict__ X, int M, int N, int K,
-    int tiles_m, int tiles_n, int nb, double* __restrict__ partials) {
+    const uint16_t* __restrict__ dW, const uint16_t* __restrict__ X,
+    const uint16_t* __restrict__ B1, int M, int N, int K, int tiles_m, int tiles_n, int nb,
+    const int32_t* __restrict__ gexp, double* __restrict__ partials) {
   // One LDS array per pipeline stage: distinct objects let the compiler see that a DMA
   // into one stage never aliases fragment reads from another, so it does not drain the
   // DMA queue before every LDS read.
@@ -193,7 +199,9 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   const int dma_lchunk_even = (lane % S::CPR) ^ S::swz(dma_row_in);
   const int dma_lchunk_odd = (lane % S::CPR) ^ S::swz(dma_row_in + (S::ROWS_PER_DMA == 8 ? 8 : 0));
   const int32x4 rsrc_a = make_rsrc(A, (unsigned)rows_a * (unsigned)K * 2u);
-  const int32x4 rsrc_b = make_rsrc(B, (unsigned)rows_b * (unsigned)K * 2u);
+  const int32x4 rsrc_b0 = make_rsrc(B, (unsigned)rows_b * (unsigned)K * 2u);
+  int32x4 rsrc_b1 = rsrc_b0;
+  if constexpr (GRAM) rsrc_b1 = make_rsrc(B1 + (size_t)tn * BN * K, (unsigned)rows_b * (unsigned)K * 2u);
   static_assert(S::DMA_A % 2 == 0 && S::DMA_B % 2 == 0, "block parity follows j");
   const unsigned row_a = (unsigned)(wave * S::DMA_A * S::ROWS_PER_DMA + dma_row_in);
   const unsigned row_b = (unsigned)(wave * S::DMA_B * S::ROWS_PER_DMA + dma_row_in);
@@ -215,8 +223,17 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   // LDS byte addresses of the stage buffers (uniform, computed once).
   const unsigned lds_stage[4] = {lds_addr(sm0), lds_addr(sm1), lds_addr(sm2), lds_addr(sm3)};
 
-  auto dma_stage = [&](auto st, int k0) {
+  // k-tiles rounded up to a multiple of NS: the padding tiles lie past in_features, read
+  // as zeros and add nothing, and the NS-unrolled loop below then has a single exit.  In
+  // GRAM mode the loop covers 2 nk tiles: tile kt reads channels (kt mod nk) BK of dW and
+  // of G_hi (kt < nk) or G_lo; tiles past the end read zeros.
+  const int nk = ((K + S::BK * S::NS - 1) / (S::BK * S::NS)) * S::NS;
+  const int nkt = GRAM ? 2 * nk : nk;
+
+  auto dma_stage = [&](auto st, int kt) {
     constexpr int ST = decltype(st)::value;
+    const int k0 = (kt < nkt ? (GRAM ? kt % nk : kt) : nk) * S::BK;
+    const int32x4 rsrc_b = (GRAM && kt >= nk) ? rsrc_b1 : rsrc_b0;
     const unsigned la = lds_stage[ST] + (unsigned)(wave * S::DMA_A) * 1024u;
     const unsigned lb = lds_stage[ST] + (unsigned)S::A_BYTES + (unsigned)(wave * S::DMA_B) * 1024u;
     const bool k_ok0 = k0 + dma_lchunk_even * 8 < K;
@@ -283,10 +300,6 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
   };
 
-  // k-tiles rounded up to a multiple of NS: the padding tiles lie past in_features, read
-  // as zeros and add nothing, and the NS-unrolled loop below then has a single exit.
-  const int nk = ((K + S::BK * S::NS - 1) / (S::BK * S::NS)) * S::NS;
-
   // ---- pipeline: NS stages in flight; a stage buffer is refilled right after the
   //      barrier that follows the last fragment read from it.  DMAs are issued for
   //      every stage slot (past the end of K they read zeros into a slot nobody reads),
@@ -297,9 +310,9 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   using I2 = std::integral_constant<int, 2 % S::NS>;
   using I3 = std::integral_constant<int, 3 % S::NS>;
   dma_stage(I0{}, 0);
-  if constexpr (S::NS > 1) dma_stage(I1{}, 1 * S::BK);
-  if constexpr (S::NS > 2) dma_stage(I2{}, 2 * S::BK);
-  if constexpr (S::NS > 3) dma_stage(I3{}, 3 * S::BK);
+  if constexpr (S::NS > 1) dma_stage(I1{}, 1);
+  if constexpr (S::NS > 2) dma_stage(I2{}, 2);
+  if constexpr (S::NS > 3) dma_stage(I3{}, 3);
   __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 1) * S::PER_STAGE>::value);
   __builtin_amdgcn_s_barrier();
 
@@ -329,12 +342,12 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     // stage kt+1 has landed (own DMAs) and this wave's reads of stage kt are done
     __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 2) * S::PER_STAGE>::value);
     __builtin_amdgcn_s_barrier();
-    dma_stage(st, (kt + S::NS) * S::BK);
+    dma_stage(st, kt + S::NS);
     load_frag(NEXT{}, 0, f0);  // after the last k-tile this reads a slot nobody uses
     mma(f1);
   };
 
-  for (int kt = 0; kt < nk; kt += S::NS) {
+  for (int kt = 0; kt < nkt; kt += S::NS) {
     step(I0{}, kt);
     if constexpr (S::NS > 1) step(I1{}, kt + 1);
     if constexpr (S::NS > 2) step(I2{}, kt + 2);
@@ -342,15 +355,31 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   }
   __builtin_amdgcn_s_waitcnt(WaitVmLgkm<0>::value);  // no LDS write may outlive the block
 
-  // ---- epilogue: sum of squares of the 256 x 256 output tile -------------------------
+  // ---- epilogue: sum of squares of the 256 x 256 output tile (GRAM: sum of C * dW at
+  //      the output positions; element e of a 32x32 block is row 8 (e / 4) + 4 (l / 32) +
+  //      (e mod 4), column l mod 32) ---------------------------------------------------
   double ssum = 0.0;
 #pragma unroll
   for (int mi = 0; mi < S::MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < S::NI; ++ni) {
       float t = 0.0f;
+      if constexpr (GRAM) {
+        const int col = tn * BN + wn * S::NI * 32 + ni * 32 + (lane & 31);
+        const int r0 = wm * S::MI * 32 + mi * 32 + 4 * (lane >> 5);
+        uint16_t dv[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) t += acc[mi][ni][e] * acc[mi][ni][e];
+        for (int e = 0; e < 16; ++e) {
+          const int r = r0 + 8 * (e >> 2) + (e & 3);
+          dv[e] = (r < rows_a && col < N) ? A[(size_t)r * K + col] : (uint16_t)0;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          t += acc[mi][ni][e] * (float)__builtin_bit_cast(_Float16, dv[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) t += acc[mi][ni][e] * acc[mi][ni][e];
+      }
       ssum += (double)t;
       __builtin_amdgcn_sched_barrier(0);  // one 32x32 block at a time: low VGPR pressure
     }
@@ -362,6 +391,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     double t = red[0];
 #pragma unroll
     for (int w = 1; w < S::WAVES; ++w) t += red[w];
+    if constexpr (GRAM) t = ldexp(t, gexp[0]);
     partials[(size_t)kk_alpha * per_alpha + (size_t)tm * tiles_n + tn] = t;
   }
 }
@@ -420,9 +450,22 @@ hipError_t launch_loss_gemm(const uint16_t* dW, const uint16_t* X, int M, int N,
   const int tm = (int)loss_tiles_m(M), tn = (int)loss_tiles_n(N);
   const long long blocks = (long long)nb * tm * tn;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_loss_gemm<LossStage>, dim3((unsigned)blocks), dim3(LossStage::THREADS), 0,
-                     stream, dW,
-                     X, M, N, K, tm, tn, nb, partials);
+  hipLaunchKernelGGL((k_loss_gemm<LossStage, false>), dim3((unsigned)blocks),
+                     dim3(LossStage::THREADS), 0, stream, dW, X, nullptr, M, N, K, tm, tn, nb,
+                     nullptr, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_gemm_gram(const uint16_t* dW, const uint16_t* Ghi, const uint16_t* Glo,
+                                 const int32_t* gexp, int M, int K, int nb, double* partials,
+                                 hipStream_t stream) {
+  if (M <= 0 || K <= 0 || nb <= 0) return hipSuccess;
+  const int tm = (int)loss_tiles_m(M), tn = (int)loss_tiles_n(K);
+  const long long blocks = (long long)nb * tm * tn;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_loss_gemm<LossStage, true>), dim3((unsigned)blocks),
+                     dim3(LossStage::THREADS), 0, stream, dW, Ghi, Glo, M, K, K, tm, tn, nb, gexp,
+                     partials);
   return hipGetLastError();
 }
 
