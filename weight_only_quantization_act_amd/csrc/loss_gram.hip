@@ -33,9 +33,14 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGfThreads = 512;  // 8 waves, one 16-row tile row each
 constexpr int kGfSpan = 128;     // channels of a tile side
-constexpr int kGfStage = 64;     // tokens per LDS stage (two 32-token k-steps)
-constexpr int kGfFlush = 256;    // tokens summed in fp32 before adding into fp64
-constexpr int kGfXtp = 68;       // LDS row of a transposed stage (fp16, 8-byte aligned)
+#ifndef AWQ_GF_STAGE
+#define AWQ_GF_STAGE 128
+#endif
+constexpr int kGfStage = AWQ_GF_STAGE;  // tokens per LDS stage (32-token k-steps)
+constexpr int kGfOct = kGfStage / 64;   // 8-token octets a wave stages per stage
+constexpr int kGfFlush = 256;           // tokens summed in fp32 before adding into fp64
+constexpr int kGfXtp = kGfStage + 4;    // LDS row of a transposed stage (fp16, 8-byte aligned)
+static_assert(kGfStage == 64 || kGfStage == 128, "64 or 128 tokens a stage");
 constexpr int kGfSplitChunk = 4096;  // entries per block of the split pass
 
 __device__ __forceinline__ float nan_maxf(float m, float a) {
@@ -43,9 +48,9 @@ __device__ __forceinline__ float nan_maxf(float m, float a) {
 }
 
 // Block b: the b-th pair (sa <= sb) of 128-channel spans in row-major order of the upper
-// triangle.  A stage of 64 tokens of both spans is stored transposed in LDS (xa, xb
-// [channel][token]): lane l of wave w loads the channel pair (2 l, 2 l + 1) of tokens
-// 8 w .. 8 w + 7 of each span and interleaves the halves with v_perm.  The MFMA fragment
+// triangle.  A stage of kGfStage tokens of both spans is stored transposed in LDS (xa, xb
+// [channel][token]): lane l of wave w loads the channel pair (2 l, 2 l + 1) of the 8-token
+// octets w (and w + 8) of each span and interleaves the halves with v_perm.  The MFMA fragment
 // (16x16x32 f16) of a 16-channel block and a 32-token k-step is then lane (p, q)'s 16 bytes
 // at row 16 block + p, token 32 ks + 8 q; wave w multiplies its tile row w of span a (A)
 // with the 8 tile columns of span b (B).  C element e of a tile is row 4 q + e, column p.
@@ -77,17 +82,20 @@ __global__ __launch_bounds__(kGfThreads) void k_gram_full(const uint16_t* __rest
     for (int e = 0; e < 4; ++e) acc64[tc][e] = 0.0;
   }
 
-  uint32_t da[8], db[8];  // the next stage's token values, in flight during the MFMAs
+  // the next stage's token values (octets wave, wave + 8), in flight during the MFMAs
+  uint32_t da[kGfOct][8], db[kGfOct][8];
   auto load_stage = [&](int t0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = t0 + 8 * wave + e;
-      const size_t row = (size_t)t * K;
-      da[e] = (pa_ok && t < N) ? *(const uint32_t*)(X + row + ca + 2 * lane) : 0u;
-      db[e] = (pb_ok && t < N) ? *(const uint32_t*)(X + row + cb + 2 * lane) : 0u;
-    }
+    for (int o = 0; o < kGfOct; ++o)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = t0 + 8 * (wave + 8 * o) + e;
+        const size_t row = (size_t)t * K;
+        da[o][e] = (pa_ok && t < N) ? *(const uint32_t*)(X + row + ca + 2 * lane) : 0u;
+        db[o][e] = (pb_ok && t < N) ? *(const uint32_t*)(X + row + cb + 2 * lane) : 0u;
+      }
   };
-  auto put = [&](uint16_t* xt, const uint32_t (&d)[8]) {
+  auto put = [&](uint16_t* xt, const uint32_t (&d)[8], int oct) {
     uint2 lo0, lo1, hi0, hi1;  // channel 2 l (low halves) and 2 l + 1 (high halves)
     lo0.x = __builtin_amdgcn_perm(d[1], d[0], 0x05040100u);
     lo0.y = __builtin_amdgcn_perm(d[3], d[2], 0x05040100u);
@@ -97,7 +105,7 @@ __global__ __launch_bounds__(kGfThreads) void k_gram_full(const uint16_t* __rest
     hi0.y = __builtin_amdgcn_perm(d[3], d[2], 0x07060302u);
     hi1.x = __builtin_amdgcn_perm(d[5], d[4], 0x07060302u);
     hi1.y = __builtin_amdgcn_perm(d[7], d[6], 0x07060302u);
-    uint16_t* r0 = xt + (2 * lane) * kGfXtp + 8 * wave;
+    uint16_t* r0 = xt + (2 * lane) * kGfXtp + 8 * oct;
     *(uint2*)r0 = lo0;
     *(uint2*)(r0 + 4) = lo1;
     *(uint2*)(r0 + kGfXtp) = hi0;
@@ -112,8 +120,11 @@ __global__ __launch_bounds__(kGfThreads) void k_gram_full(const uint16_t* __rest
 
   if (N > 0) load_stage(0);
   for (int t0 = 0; t0 < N; t0 += kGfStage) {
-    put(xa, da);
-    put(xb, db);
+#pragma unroll
+    for (int o = 0; o < kGfOct; ++o) {
+      put(xa, da[o], wave + 8 * o);
+      put(xb, db[o], wave + 8 * o);
+    }
     __syncthreads();
     if (t0 + kGfStage < N) load_stage(t0 + kGfStage);
 #pragma unroll
