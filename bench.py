@@ -293,6 +293,7 @@ def main():
     if not args.no_variants:
         line["variants"] = time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N)
         line["w4a16"] = time_w4a16(awq, torch, out, res["s"], Xd, cfg, sptr, M, K)
+        line["large_layers"] = time_large_layers(awq, torch, alphas, sptr)
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib * (1 << 20) // 2, dtype=torch.float16, device="cuda")
         dst = torch.empty_like(src)
@@ -374,6 +375,42 @@ def w4a16_bytes(M, K, g, T, with_s):
     """HBM bytes one W4A16 product must move: codes, fp16 step and zero per group, the
     activations, s if given, and the fp16 output."""
     return M * K / 2 + 4.0 * M * K / g + 2.0 * T * K + (4.0 * K if with_s else 0.0) + 2.0 * T * M
+
+
+def time_large_layers(awq, torch, alphas, sptr, reps=2):
+    """The whole 20-alpha search (statistics excluded) on the three large layer shapes, with
+    seeded device-side weights and activations (1% of the channels scaled by 20).  With
+    many more tokens than channels the library takes the loss through X^T X; the
+    direct-equivalent rate divides the direct form's 2 M K N per alpha by the time."""
+    shapes = [("c3 up", 11008, 4096, 16384, 4, 128, 1), ("c5", 13824, 5120, 32768, 3, 64, 1),
+              ("c4", 28672, 8192, 65536, 4, 128, 1)]
+    out = {}
+    gen = torch.Generator(device="cuda")
+    for name, M, K, N, b, g, zp in shapes:
+        gen.manual_seed(20260 + M)
+        W = (torch.randn((M, K), device="cuda", generator=gen) * 0.02).half()
+        X = torch.randn((N, K), device="cuda", generator=gen)
+        X[:, ::100] *= 20.0
+        X = X.half()
+        cfg = awq.qconfig(b, g, zp)
+        a = awq.awq_act_stats(X)
+        ws = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, len(alphas), 0),
+                         dtype=torch.uint8, device="cuda")
+        awq.awq_search_scales(W, X, a, alphas, cfg, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(sptr)
+        for _ in range(reps):
+            awq.awq_search_scales(W, X, a, alphas, cfg, workspace=ws)
+        e1.record(sptr)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_ms(e1) / reps
+        direct = 2.0 * M * K * N * len(alphas)
+        out[name] = {"M": M, "K": K, "N": N, "w_bit": b, "group_size": g, "search_ms": ms,
+                     "direct_equivalent_TFLOP/s": direct / (ms * 1e-3) / 1e12}
+        del W, X, a, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, reps=50):
