@@ -138,7 +138,8 @@ def test_threshold_scales_from_gpu_statistic():
 @pytest.mark.parametrize("M,K,N,w_bit,g,zp", [(256, 256, 256, 4, 128, 1),
                                               (300, 384, 700, 4, 128, 1),
                                               (77, 160, 33, 3, 32, 1),
-                                              (520, 512, 1, 4, 64, 0)])
+                                              (520, 512, 1, 4, 64, 0),
+                                              (200, 256, 4000, 4, 128, 1)])  # loss via X^T X
 def test_search_scale_table(M, K, N, w_bit, g, zp):
     say(f"table search M={M} K={K} N={N}")
     L = make_layer(small_spec("q", M, K, N, w_bit=w_bit, group_size=g, zero_point=zp,
