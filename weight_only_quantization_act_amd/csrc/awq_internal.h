@@ -15,16 +15,17 @@ constexpr int kLossBN = 256;  // tokens per tile
 inline int64_t loss_tiles_m(int64_t M) { return (M + kLossBM - 1) / kLossBM; }
 inline int64_t loss_tiles_n(int64_t N) { return (N + kLossBN - 1) / kLossBN; }
 // The loss through G = X^T X (launch_gram_full + launch_loss_gemm_gram) instead of the
-// direct product when its matrix-core work -- N K^2 for G's upper triangle plus
-// 4 M K^2 per grid point (two passes, G_hi and G_lo) -- is below 0.7 of the direct
-// 2 M K N per grid point, for in_features up to 32768.
+// direct product when its matrix-core work -- N K^2 for G's upper triangle plus, per grid
+// point, two passes (G_hi and G_lo) over the block upper triangle of G, 2 M K^2 (1 + BN/K)
+// -- is below 0.7 of the direct 2 M K N per grid point, for in_features up to 32768.
 #ifndef AWQ_LOSS_GRAM_RATIO
 #define AWQ_LOSS_GRAM_RATIO 0.7
 #endif
 inline bool loss_use_gram(int64_t M, int64_t K, int64_t N, int64_t n_alpha) {
   if (M <= 0 || K <= 0 || N <= 0 || K > 32768) return false;
   const double k2 = (double)K * (double)K;
-  const double gram = (double)N * k2 + 4.0 * (double)M * k2 * (double)n_alpha;
+  const double gram = (double)N * k2 + 2.0 * (double)M * k2 * (double)n_alpha *
+                                           (1.0 + (double)kLossBN / (double)K);
   const double direct = 2.0 * (double)M * (double)K * (double)N * (double)n_alpha;
   return gram < AWQ_LOSS_GRAM_RATIO * direct;
 }

@@ -138,10 +138,11 @@ struct Stage {
 };
 
 // GRAM = false: C = dW_k X^T (X fp16 [N][K]) and the tile's sum of squares.
-// GRAM = true:  C = dW_k (G_hi + G_lo) with G 2^-gexp = G_hi + G_lo fp16 [K][K] (B0, B1;
-// N = K, symmetric, so rows serve as the K-contiguous operand): the K loop runs twice,
-// first over G_hi then over G_lo with the same dW_k, and the tile's sum of C * dW_k at the
-// same positions, times 2^gexp, is the tile's share of sum_r dW_r G dW_r^T.
+// GRAM = true:  C = dW_k G'^T with G' 2^-gexp = G_hi + G_lo fp16 [K][K] (B0, B1; N = K):
+// G' is G with its BN x BN blocks above the diagonal doubled and those below it zero, so
+// column tile tn needs k from tn BN on only.  The K loop runs twice over that range, first
+// over G_hi then over G_lo with the same dW_k, and the tile's sum of C * dW_k at the same
+// positions, times 2^gexp, is the tile's share of sum_r dW_r G dW_r^T.
 template <class S, bool GRAM>
 __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     const uint16_t* __restrict__ dW, const uint16_t* __restrict__ X,
@@ -228,12 +229,17 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   // GRAM mode the loop covers 2 nk tiles: tile kt reads channels (kt mod nk) BK of dW and
   // of G_hi (kt < nk) or G_lo; tiles past the end read zeros.
   const int nk = ((K + S::BK * S::NS - 1) / (S::BK * S::NS)) * S::NS;
-  const int nkt = GRAM ? 2 * nk : nk;
+  // GRAM: k-tiles kt0 .. nk - 1 in each pass (kt0 a multiple of NS since BN / BK is)
+  static_assert(!GRAM || (BN / S::BK) % S::NS == 0, "the diagonal block starts on a whole pipeline step");
+  const int kt0 = GRAM ? min(tn * (BN / S::BK), nk) : 0;
+  const int npass = nk - kt0;
+  const int nkt = GRAM ? 2 * npass : nk;
 
-  auto dma_stage = [&](auto st, int kt) {
+  // loop tile i -> k-tile (kt0 + i mod npass) of pass i / npass; past the end: zeros
+  auto dma_stage = [&](auto st, int i) {
     constexpr int ST = decltype(st)::value;
-    const int k0 = (kt < nkt ? (GRAM ? kt % nk : kt) : nk) * S::BK;
-    const int32x4 rsrc_b = (GRAM && kt >= nk) ? rsrc_b1 : rsrc_b0;
+    const int k0 = (i < nkt ? (GRAM ? kt0 + (i >= npass ? i - npass : i) : i) : nk) * S::BK;
+    const int32x4 rsrc_b = (GRAM && i >= npass) ? rsrc_b1 : rsrc_b0;
     const unsigned la = lds_stage[ST] + (unsigned)(wave * S::DMA_A) * 1024u;
     const unsigned lb = lds_stage[ST] + (unsigned)S::A_BYTES + (unsigned)(wave * S::DMA_B) * 1024u;
     const bool k_ok0 = k0 + dma_lchunk_even * 8 < K;

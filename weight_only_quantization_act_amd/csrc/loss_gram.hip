@@ -14,8 +14,12 @@
 //                      at most 256 tokens, those sums added in fp64, the total rounded to
 //                      fp32 and written at (a, b) and (b, a); each tile's largest |G|.
 //   k_gram_full_split  one power of two 2^-ex for the whole matrix (its largest magnitude
-//                      into [2^13, 2^14)) and G 2^-ex = hi + lo in fp16 (about 2^-22
-//                      relative), the two operands of the per-grid-point product.
+//                      into [2^13, 2^14)) and G' 2^-ex = hi + lo in fp16 (about 2^-22
+//                      relative), the two operands of the per-grid-point product.  G' is G
+//                      with its blocks of kLossBN x kLossBN above the diagonal doubled
+//                      (exact) and those below it zero: with d the rows of dW,
+//                      sum_r d_r G d_r^T = sum over column blocks a of d_a . (G' d)_a, and
+//                      the product for column block a only runs over k from block a on.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(kGfThreads) void k_gram_full(const uint16_t* __rest
 // Block c: entries [c chunk, (c + 1) chunk) of G (K x K).  Every block derives the same
 // exponent from all tile maxima (NaN if any entry is NaN: then ex = 0 and the NaN reaches
 // the losses); block 0 publishes it.
-__global__ __launch_bounds__(256) void k_gram_full_split(const float* __restrict__ G,
+__global__ __launch_bounds__(256) void k_gram_full_split(const float* __restrict__ G, int K,
                                                          int64_t KK,
                                                          const float* __restrict__ tmax,
                                                          int ntiles, uint16_t* __restrict__ Ghi,
@@ -206,7 +210,10 @@ __global__ __launch_bounds__(256) void k_gram_full_split(const float* __restrict
   for (int i = tid; i < kGfSplitChunk; i += 256) {
     const int64_t j = base + i;
     if (j >= KK) break;
-    const float vs = ldexpf(G[j], -ex);
+    const int64_t row = j / K, col = j - (j / K) * K;
+    const int64_t ra = row / kLossBN, cb = col / kLossBN;
+    const float g = cb < ra ? 0.0f : (cb > ra ? 2.0f * G[j] : G[j]);
+    const float vs = ldexpf(g, -ex);
     const uint16_t hi = f2h(vs);
     Ghi[j] = hi;
     Glo[j] = f2h(vs - h2f(hi));
@@ -232,7 +239,7 @@ hipError_t launch_gram_full(const uint16_t* X, int N, int K, float* G, float* tm
   if (e != hipSuccess) return e;
   const int64_t KK = (int64_t)K * K;
   const int64_t blocks = (KK + kGfSplitChunk - 1) / kGfSplitChunk;
-  hipLaunchKernelGGL(k_gram_full_split, dim3((unsigned)blocks), dim3(256), 0, stream, G, KK,
+  hipLaunchKernelGGL(k_gram_full_split, dim3((unsigned)blocks), dim3(256), 0, stream, G, K, KK,
                      tmax, ntiles, Ghi, Glo, gexp);
   return hipGetLastError();
 }
