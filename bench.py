@@ -9,7 +9,9 @@ zero-point, group 128, 20 alphas).
 
 Prints one JSON line.  The loss product's live duration comes from HIP events that the
 library records on its own stream around that launch (one launch per step, the whole
-alpha grid in one pass).  The CPU baseline is the oracle, timed on a bounded row subset
+alpha grid in one pass).  On this layer the library takes the loss through G = X^T X
+(formed once per step, also bracketed by events): the loss product is then dW_k G'^T
+over the block upper triangle of G, and its flops are counted as executed.  The CPU baseline is the oracle, timed on a bounded row subset
 of the same layer (the loss is a sum over rows) and scaled to the full layer.
 """
 from __future__ import annotations
@@ -202,7 +204,8 @@ def main():
         a = awq.awq_act_stats(Xd, workspace=ws_stats)
         if ev is not None:
             ev["st1"].record(sptr)
-            awq.awq_set_profile_events(ev["g0"], ev["g1"], ev["f0"], ev["f1"])
+            awq.awq_set_profile_events(ev["g0"], ev["g1"], ev["f0"], ev["f1"], ev["r0"],
+                                       ev["r1"])
         res = awq.awq_search_scales(Wd, Xd, a, alphas, cfg, workspace=ws_search)
         if ev is not None:
             ev["p0"].record(sptr)
@@ -227,7 +230,7 @@ def main():
     total_ms = t_start.elapsed_ms(t_end)
     ms_per_step = total_ms / args.steps
 
-    names = ("st0", "st1", "g0", "g1", "f0", "f1", "p0", "p1")
+    names = ("st0", "st1", "g0", "g1", "f0", "f1", "r0", "r1", "p0", "p1")
     evs = [{n: HipEvent() for n in names} for _ in range(args.steps)]
     for i in range(args.steps):
         res, out = step(evs[i])
@@ -236,11 +239,19 @@ def main():
     def avg(a, b):
         return float(np.mean([e[a].elapsed_ms(e[b]) for e in evs]))
 
+    gram = awq.awq_loss_form(M, K, N, nA) == awq.AWQ_LOSS_GRAM
     gemm_ms, fq_ms = avg("g0", "g1"), avg("f0", "f1")
     stats_ms, pack_ms = avg("st0", "st1"), avg("p0", "p1")
+    gram_ms = avg("r0", "r1") if gram else 0.0
 
     status = int(res["status"].cpu()[0])
-    gemm_flops = 2.0 * M * N * K * nA                       # one launch = all alphas
+    direct_flops = 2.0 * M * N * K * nA                     # the direct product dW_k X^T
+    if gram:
+        # one launch = all alphas; column tile j of 256 channels runs over k >= 256 j
+        gemm_flops = nA * sum(2.0 * M * min(256, K - c0) * (K - c0) for c0 in range(0, K, 256))
+        gram_flops = sum(2.0 * N * min(128, K - c0) * (K - c0) for c0 in range(0, K, 128))
+    else:
+        gemm_flops, gram_flops = direct_flops, 0.0
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
     g = spec.group_size
     stats_bytes = 2.0 * N * K + 4.0 * K
@@ -282,15 +293,21 @@ def main():
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": gemm_tflops / MFMA_F16_PEAK_TFLOPS,
                      "traffic": traffic,
-                     "kernel": "k_loss_gemm", "flops_per_launch": gemm_flops,
-                     "avg_launch_ms": gemm_ms},
+                     "kernel": "k_loss_gemm" + ("<G form>" if gram else ""),
+                     "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms},
         "kernels": {
             "act_stats": {"ms": stats_ms, "GB/s": stats_bytes / (stats_ms * 1e-3) / 1e9,
                           "frac_hbm": stats_bytes / (stats_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
             "fake_quant": {"ms": fq_ms, "GB/s": fq_bytes / (fq_ms * 1e-3) / 1e9,
                            "frac_hbm": fq_bytes / (fq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
             "loss_gemm": {"ms": gemm_ms, "TFLOP/s": gemm_tflops,
-                          "frac_mfma": gemm_tflops / MFMA_F16_PEAK_TFLOPS},
+                          "frac_mfma": gemm_tflops / MFMA_F16_PEAK_TFLOPS,
+                          "form": "gram" if gram else "direct",
+                          "direct_equivalent_TFLOP/s":
+                              direct_flops / ((gemm_ms + gram_ms) * 1e-3) / 1e12},
+            **({"gram": {"ms": gram_ms, "TFLOP/s": gram_flops / (gram_ms * 1e-3) / 1e12,
+                         "frac_mfma": gram_flops / (gram_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                         "kernels": "k_gram_full + k_gram_full_split"}} if gram else {}),
             "quant_pack": {"ms": pack_ms, "GB/s": pack_bytes / (pack_ms * 1e-3) / 1e9,
                            "frac_hbm": pack_bytes / (pack_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         },
@@ -350,8 +367,10 @@ def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, reps=20):
                      device="cuda")
     ms = timed(lambda: awq.awq_search_scale_table(Wd, Xd, table, cfg, workspace=ws))
     tf = 2.0 * M * N * K * table.shape[0] / (ms * 1e-3) / 1e12
-    out["search_scale_table_20_threshold_rows"] = {"ms": ms, "TFLOP/s": tf,
-                                                   "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS}
+    form = awq.awq_loss_form(M, K, N, table.shape[0])
+    out["search_scale_table_20_threshold_rows"] = {
+        "ms": ms, "direct_equivalent_TFLOP/s": tf,
+        "form": "gram" if form == awq.AWQ_LOSS_GRAM else "direct"}
     ratios = [1.0 - 0.025 * k for k in range(20)]
     s_best = awq.awq_search_scales(Wd, Xd, a, [0.5], cfg)["s"]
     ws_clip = torch.empty(awq.awq_clip_workspace_bytes(M, K, N, cfg), dtype=torch.uint8,

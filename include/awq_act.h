@@ -121,7 +121,11 @@ int awq_act_stats_ex(const void* X, int64_t n_tokens, int64_t in_features, int32
  *   status_out  int32 [1], device (written: AWQ_OK or AWQ_W_NONFINITE); may be NULL
  *   workspace   device scratch; see awq_workspace_bytes.
  * Losses are computed with dW rounded to fp16 and an fp16 MFMA product with fp32
- * accumulation, reduced in fp64 in a fixed order (bitwise repeatable run to run).
+ * accumulation, reduced in fp64 in a fixed order (bitwise repeatable run to run).  When
+ * the estimated cost favours it (roughly n_tokens >= in_features), the same quantity is
+ * taken as sum_r dW_r G dW_r^T with G = X^T X [AWQ-notes §1.1]: G summed on the matrix
+ * cores (fp32 over at most 256 tokens, then fp64) and stored fp32; its off-diagonal
+ * entries enter an fp16 MFMA product, its diagonal enters in fp32.
  * out_features >= 0, in_features >= 0 (multiple of group_size), n_tokens >= 1.
  * ---------------------------------------------------------------------------------- */
 
@@ -131,6 +135,14 @@ int awq_act_stats_ex(const void* X, int64_t n_tokens, int64_t in_features, int32
  * runs as many grid points per pass as fit.  Returns 0 for invalid arguments. */
 size_t awq_workspace_bytes(int64_t out_features, int64_t in_features, int64_t n_tokens,
                            const awq_qconfig* cfg, int32_t n_alpha, int32_t alpha_batch);
+
+/* Which form the search takes for these sizes: AWQ_LOSS_DIRECT (the product dW X^T) or
+ * AWQ_LOSS_GRAM (sum_r dW_r G dW_r^T, G = X^T X formed once per call).  Both give the
+ * losses defined above; the choice depends on the sizes only.  Returns -1 for sizes that
+ * awq_workspace_bytes rejects (n_alpha outside 1 .. AWQ_MAX_ALPHA, negative sizes,
+ * n_tokens < 1); group size and bit width do not enter. */
+enum { AWQ_LOSS_DIRECT = 0, AWQ_LOSS_GRAM = 1 };
+int awq_loss_form(int64_t out_features, int64_t in_features, int64_t n_tokens, int32_t n_alpha);
 
 int awq_search_scales(const void* W, const void* X, const float* a,
                       int64_t out_features, int64_t in_features, int64_t n_tokens,
@@ -264,13 +276,15 @@ int awq_quantize_pack(const void* W, const float* s, int64_t out_features,
 /* ------------------------------------------------------------------------------------
  * Profiling hook (per calling thread, one-shot): the next awq_search_scales call on
  * this thread records `gemm_start`/`gemm_stop` (hipEvent_t) on its stream immediately
- * before its first and after its last loss-product launch, and `fq_start`/`fq_stop`
- * around its first fake-quantisation launch.  Any of them may be NULL.  With the whole
- * alpha grid in one pass (a workspace of awq_workspace_bytes(..., n_alpha, 0)), each
- * pair brackets exactly one kernel launch.  Returns AWQ_OK.
+ * before its first and after its last loss-product launch, `fq_start`/`fq_stop` around
+ * its first fake-quantisation launch, and `gram_start`/`gram_stop` around the two
+ * launches that form G = X^T X (only when the search takes the G form).  Any of them may
+ * be NULL.  With the whole alpha grid in one pass (a workspace of
+ * awq_workspace_bytes(..., n_alpha, 0)), the loss and fake-quantisation pairs each
+ * bracket exactly one kernel launch.  Returns AWQ_OK.
  * ---------------------------------------------------------------------------------- */
 int awq_set_profile_events(void* gemm_start, void* gemm_stop, void* fq_start,
-                           void* fq_stop);
+                           void* fq_stop, void* gram_start, void* gram_stop);
 
 #ifdef __cplusplus
 }

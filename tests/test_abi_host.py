@@ -36,7 +36,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in awq_act.h but not exported"
     assert set(names) == set(_lib._SIGNATURES)
@@ -93,7 +93,9 @@ def test_search_validation(L):
 
 def test_workspace_query(L):
     cfg = awq.qconfig(4, 128, 1)
-    M = K = N = 4096
+    M = K = 4096
+    N = 2048                                     # the direct form
+    assert awq.awq_loss_form(M, K, N, 20) == awq.AWQ_LOSS_DIRECT
     full = awq.awq_workspace_bytes(M, K, N, cfg, 20, 0)
     one = awq.awq_workspace_bytes(M, K, N, cfg, 20, 1)
     tiles = (M // 256) * (N // 256)
@@ -101,6 +103,14 @@ def test_workspace_query(L):
     assert one == fixed + M * K * 2
     assert full == fixed + 20 * M * K * 2
     assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 7) == fixed + 7 * M * K * 2
+    # the G form: tiles over K, then fp32 G, fp16 G', fp32 diagonal, the 528 tile maxima of
+    # G's upper triangle in 128-channel spans, and the exponent, each 256-byte aligned
+    N = 4096
+    assert awq.awq_loss_form(M, K, N, 20) == awq.AWQ_LOSS_GRAM
+    tiles = (M // 256) * (K // 256)
+    fixed = 20 * K * 4 + 20 * tiles * 8 + K * K * 4 + K * K * 2 + K * 4 + 2304 + 256
+    assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 1) == fixed + M * K * 2
+    assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 0) == fixed + 20 * M * K * 2
     assert awq.awq_workspace_bytes(M, K, N, cfg, 0, 0) == 0
     assert awq.awq_workspace_bytes(M, 100, N, cfg, 20, 0) == 0
     assert awq.awq_workspace_bytes(0, K, N, cfg, 3, 0) == ((3 * K * 4 + 255) // 256) * 256
@@ -140,8 +150,27 @@ def test_pack_and_fake_quant_validation(L):
     assert g(P, P, 8, 0, _cfg(), P, None) == E["OK"]
 
 
+def test_loss_form_choice():
+    q = awq.awq_loss_form
+    # few tokens: the direct product; as many tokens as channels or more: the G form
+    assert q(512, 512, 256, 20) == awq.AWQ_LOSS_DIRECT
+    assert q(4096, 4096, 1024, 20) == awq.AWQ_LOSS_DIRECT
+    assert q(4096, 4096, 4096, 20) == awq.AWQ_LOSS_GRAM
+    assert q(28672, 8192, 65536, 20) == awq.AWQ_LOSS_GRAM
+    assert q(4096, 11008, 16384, 20) == awq.AWQ_LOSS_GRAM
+    assert q(4096, 40960, 32768, 20) == awq.AWQ_LOSS_DIRECT   # G beyond 32768 channels
+    assert q(0, 4096, 4096, 20) == awq.AWQ_LOSS_DIRECT
+    for bad in [(-1, 64, 64, 20), (64, 64, 0, 20), (64, 64, 64, 0), (64, 64, 64, 65)]:
+        assert q(*bad) == -1
+    # the choice agrees with the workspace: the G form holds G (fp32 and fp16) besides dW
+    cfg = awq.qconfig(4, 128, 1)
+    direct = awq.awq_workspace_bytes(4096, 4096, 1024, cfg, 20, 0)
+    gram = awq.awq_workspace_bytes(4096, 4096, 4096, cfg, 20, 0)
+    assert gram - direct >= 4096 * 4096 * 6
+
+
 def test_profile_hook_set_and_clear(L):
-    assert L.awq_set_profile_events(None, None, None, None) == E["OK"]
+    assert L.awq_set_profile_events(None, None, None, None, None, None) == E["OK"]
 
 
 def test_stats_ex_validation(L):

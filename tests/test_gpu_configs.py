@@ -57,6 +57,10 @@ def test_full_size_layer(cfg_name, layer, rows):
 
     say(f"{spec.name}: additivity over row halves")
     h = (M // 2) // 256 * 256
+    # both halves take the same form of the loss as the whole layer, so the tile partials
+    # are the same numbers and only their fp64 summation order differs
+    assert (awq.awq_loss_form(h, K, N, len(alphas)) == awq.awq_loss_form(M - h, K, N, len(alphas))
+            == awq.awq_loss_form(M, K, N, len(alphas)))
     top = awq.awq_search_scales(Wd[:h].contiguous(), Xd, a, alphas, cfg)
     bot = awq.awq_search_scales(Wd[h:].contiguous(), Xd, a, alphas, cfg)
     assert np.allclose(lf, host(top["losses"]) + host(bot["losses"]), rtol=1e-12, atol=0)

@@ -145,16 +145,24 @@ SEARCH_CASES = [
     (520, 512, 1, 4, 64, 0),        # one token
     (64, 1024, 515, 2, 128, 0),
     (1024, 640, 300, 3, 64, 1),
-    # many more tokens than channels: the loss through G = X^T X
+    # about as many tokens as channels or more: the loss through G = X^T X
+    (300, 384, 700, 3, 64, 0),      # 384 channels: a partial 256-block of G'
     (300, 256, 3000, 4, 128, 1),
     (130, 320, 5000, 3, 32, 0),     # 128-channel Gram spans cut at in_features
     (64, 1024, 8192, 4, 128, 1),
 ]
 
 
+def test_search_forms_covered():
+    """The cases above exercise both forms of the loss."""
+    forms = {awq.awq_loss_form(M, K, N, 20) for M, K, N, *_ in SEARCH_CASES}
+    assert forms == {awq.AWQ_LOSS_DIRECT, awq.AWQ_LOSS_GRAM}
+
+
 @pytest.mark.parametrize("M,K,N,w_bit,g,zp", SEARCH_CASES)
 def test_search_parity(M, K, N, w_bit, g, zp):
-    say(f"search M={M} K={K} N={N} b={w_bit} g={g} zp={zp}")
+    form = "gram" if awq.awq_loss_form(M, K, N, 20) == awq.AWQ_LOSS_GRAM else "direct"
+    say(f"search M={M} K={K} N={N} b={w_bit} g={g} zp={zp} ({form} form)")
     L = make_layer(small_spec("q", M, K, N, w_bit=w_bit, group_size=g, zero_point=zp,
                               outlier_count=max(1, K // 100), seed=M + K))
     cfg = awq.qconfig(w_bit, g, zp)
@@ -221,9 +229,14 @@ def test_search_deterministic_and_batch_invariant():
         assert np.array_equal(ref.view(np.uint64), got.view(np.uint64)), batch
 
 
-def test_search_rows_additive():
-    """The loss is a sum over output rows, so row blocks add up to the whole layer."""
-    L = make_layer(small_spec("r", 1024, 512, 512, outlier_count=5))
+@pytest.mark.parametrize("K,N", [(512, 256), (256, 2048)])
+def test_search_rows_additive(K, N):
+    """The loss is a sum over output rows, so row blocks add up to the whole layer (in
+    either form of the loss, the same for the whole layer and its blocks here)."""
+    forms = {awq.awq_loss_form(m, K, N, 8) for m in (1024, 256)}
+    assert len(forms) == 1
+    say(f"rows additive K={K} N={N} form={forms}")
+    L = make_layer(small_spec("r", 1024, K, N, outlier_count=5))
     cfg = awq.qconfig(4, 128, 1)
     alphas = alpha_grid(8)
     Xd = dev(L.X)

@@ -43,11 +43,12 @@ _SIGNATURES = {
     "awq_act_stats_workspace_bytes": (_sz, [_i64, _i64]),
     "awq_act_stats": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "awq_workspace_bytes": (_sz, [_i64, _i64, _i64, _cfgp, _i32, _i32]),
+    "awq_loss_form": (ctypes.c_int, [_i64, _i64, _i64, _i32]),
     "awq_search_scales": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _cfgp, _vp, _i32,
                                          _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "awq_fake_quant_delta": (ctypes.c_int, [_vp, _vp, _i64, _i64, _cfgp, _vp, _vp]),
     "awq_quantize_pack": (ctypes.c_int, [_vp, _vp, _i64, _i64, _cfgp, _vp, _vp, _vp, _vp]),
-    "awq_set_profile_events": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
+    "awq_set_profile_events": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "awq_act_stats_ex_workspace_bytes": (_sz, [_i64, _i64, _i32, _i64]),
     "awq_act_stats_ex": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i64, ctypes.c_double, _vp, _vp,
                                         _sz, _vp]),
@@ -162,6 +163,14 @@ def awq_workspace_bytes(out_features: int, in_features: int, n_tokens: int, cfg:
                                          ctypes.byref(cfg), n_alpha, alpha_batch))
 
 
+AWQ_LOSS_DIRECT, AWQ_LOSS_GRAM = 0, 1
+
+
+def awq_loss_form(out_features: int, in_features: int, n_tokens: int, n_alpha: int) -> int:
+    """AWQ_LOSS_DIRECT or AWQ_LOSS_GRAM: the form awq_search_scales takes for these sizes."""
+    return int(lib().awq_loss_form(out_features, in_features, n_tokens, n_alpha))
+
+
 def awq_search_scales(W: torch.Tensor, X: torch.Tensor, a: torch.Tensor,
                       alphas: Sequence[float], cfg: awq_qconfig,
                       workspace: Optional[torch.Tensor] = None, alpha_batch: int = 0,
@@ -227,14 +236,16 @@ def awq_quantize_pack(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig, stream
     return codes, scales, zeros
 
 
-def awq_set_profile_events(gemm_start=None, gemm_stop=None, fq_start=None, fq_stop=None):
+def awq_set_profile_events(gemm_start=None, gemm_stop=None, fq_start=None, fq_stop=None,
+                           gram_start=None, gram_stop=None):
     """Arm the one-shot per-thread event hook of the next awq_search_scales call.
     Arguments are hipEvent_t handles (int), or objects exposing one as `.handle`."""
     def h(e):
         if e is None:
             return None
         return int(e) if isinstance(e, int) else int(e.handle)
-    _check(lib().awq_set_profile_events(h(gemm_start), h(gemm_stop), h(fq_start), h(fq_stop)),
+    _check(lib().awq_set_profile_events(h(gemm_start), h(gemm_stop), h(fq_start), h(fq_stop),
+                                        h(gram_start), h(gram_stop)),
            "awq_set_profile_events")
 
 

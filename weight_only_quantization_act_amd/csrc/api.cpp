@@ -52,11 +52,11 @@ int device_ptr(const void* p) {
   return AWQ_E_DEVICE;
 }
 
-// Workspace of the search: s table | loss partials | (Gram form: fp32 G, G_hi, G_lo, tile
-// maxima, exponent) | dW batch.
+// Workspace of the search: s table | loss partials | (Gram form: fp32 G, fp16 G', fp32
+// diagonal, tile maxima, exponent) | dW batch.
 struct SearchLayout {
   size_t s_off, p_off, dw_off;
-  size_t g32_off, ghi_off, glo_off, tmax_off, gexp_off;
+  size_t g32_off, gh_off, gdiag_off, tmax_off, gexp_off;
   size_t dw_bytes_per_alpha;
   int64_t tiles;
   bool gram;
@@ -70,15 +70,15 @@ SearchLayout search_layout(int64_t M, int64_t K, int64_t N, int32_t n_alpha) {
   L.s_off = 0;
   L.p_off = round_up((size_t)n_alpha * (size_t)K * sizeof(float), kAlign);
   size_t off = L.p_off + round_up((size_t)n_alpha * (size_t)L.tiles * sizeof(double), kAlign);
-  L.g32_off = L.ghi_off = L.glo_off = L.tmax_off = L.gexp_off = off;
+  L.g32_off = L.gh_off = L.gdiag_off = L.tmax_off = L.gexp_off = off;
   if (L.gram) {
     const size_t kk = (size_t)K * (size_t)K;
     L.g32_off = off;
     off += round_up(kk * sizeof(float), kAlign);
-    L.ghi_off = off;
+    L.gh_off = off;
     off += round_up(kk * sizeof(uint16_t), kAlign);
-    L.glo_off = off;
-    off += round_up(kk * sizeof(uint16_t), kAlign);
+    L.gdiag_off = off;
+    off += round_up((size_t)K * sizeof(float), kAlign);
     L.tmax_off = off;
     off += round_up((size_t)awq::gram_full_tiles(K) * sizeof(float), kAlign);
     L.gexp_off = off;
@@ -94,6 +94,8 @@ struct ProfileHook {
   void* gemm_stop = nullptr;
   void* fq_start = nullptr;
   void* fq_stop = nullptr;
+  void* gram_start = nullptr;
+  void* gram_stop = nullptr;
 };
 thread_local ProfileHook g_hook;
 
@@ -126,15 +128,16 @@ int run_search(const void* W, const void* X, const float* s_table, int64_t M, in
   }
   int st;
   if (L.tiles > 0) {
-    uint16_t* Ghi = (uint16_t*)(ws + L.ghi_off);
-    uint16_t* Glo = (uint16_t*)(ws + L.glo_off);
+    uint16_t* Gh = (uint16_t*)(ws + L.gh_off);
+    float* gdiag = (float*)(ws + L.gdiag_off);
     int32_t* gexp = (int32_t*)(ws + L.gexp_off);
     if (L.gram) {  // G = X^T X once, for every grid point
-      if ((st = record(hook.gemm_start, sm))) return st;
+      if ((st = record(hook.gram_start, sm))) return st;
       st = hip_status(awq::launch_gram_full((const uint16_t*)X, (int)N, (int)K,
                                             (float*)(ws + L.g32_off),
-                                            (float*)(ws + L.tmax_off), Ghi, Glo, gexp, sm));
+                                            (float*)(ws + L.tmax_off), Gh, gdiag, gexp, sm));
       if (st) return st;
+      if ((st = record(hook.gram_stop, sm))) return st;
     }
     for (int k0 = 0; k0 < nc; k0 += batch) {
       const int nb = nc - k0 < batch ? nc - k0 : batch;
@@ -145,9 +148,9 @@ int run_search(const void* W, const void* X, const float* s_table, int64_t M, in
                                                    cfg->group_size, cfg->zero_point, dW, sm));
       if (st) return st;
       if (first && (st = record(hook.fq_stop, sm))) return st;
-      if (first && !L.gram && (st = record(hook.gemm_start, sm))) return st;
+      if (first && (st = record(hook.gemm_start, sm))) return st;
       if (L.gram)
-        st = hip_status(awq::launch_loss_gemm_gram(dW, Ghi, Glo, gexp, (int)M, (int)K, nb,
+        st = hip_status(awq::launch_loss_gemm_gram(dW, Gh, gdiag, gexp, (int)M, (int)K, nb,
                                                    partials + (size_t)k0 * L.tiles, sm));
       else
         st = hip_status(awq::launch_loss_gemm(dW, (const uint16_t*)X, (int)M, (int)N, (int)K,
@@ -234,6 +237,13 @@ size_t awq_workspace_bytes(int64_t out_features, int64_t in_features, int64_t n_
   if (alpha_batch <= 0 || alpha_batch > n_alpha) alpha_batch = n_alpha;
   SearchLayout L = search_layout(out_features, in_features, n_tokens, n_alpha);
   return L.dw_off + (size_t)alpha_batch * L.dw_bytes_per_alpha;
+}
+
+int awq_loss_form(int64_t out_features, int64_t in_features, int64_t n_tokens, int32_t n_alpha) {
+  if (out_features < 0 || in_features < 0 || token_shape(n_tokens, in_features) != AWQ_OK) return -1;
+  if (n_alpha < 1 || n_alpha > AWQ_MAX_ALPHA) return -1;
+  return search_layout(out_features, in_features, n_tokens, n_alpha).gram ? AWQ_LOSS_GRAM
+                                                                           : AWQ_LOSS_DIRECT;
 }
 
 int awq_search_scales(const void* W, const void* X, const float* a, int64_t out_features,
@@ -502,11 +512,14 @@ int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_fe
                                             errors_out, (hipStream_t)stream));
 }
 
-int awq_set_profile_events(void* gemm_start, void* gemm_stop, void* fq_start, void* fq_stop) {
+int awq_set_profile_events(void* gemm_start, void* gemm_stop, void* fq_start, void* fq_stop,
+                           void* gram_start, void* gram_stop) {
   g_hook.gemm_start = gemm_start;
   g_hook.gemm_stop = gemm_stop;
   g_hook.fq_start = fq_start;
   g_hook.fq_stop = fq_stop;
+  g_hook.gram_start = gram_start;
+  g_hook.gram_stop = gram_stop;
   return AWQ_OK;
 }
 

@@ -15,17 +15,21 @@ constexpr int kLossBN = 256;  // tokens per tile
 inline int64_t loss_tiles_m(int64_t M) { return (M + kLossBM - 1) / kLossBM; }
 inline int64_t loss_tiles_n(int64_t N) { return (N + kLossBN - 1) / kLossBN; }
 // The loss through G = X^T X (launch_gram_full + launch_loss_gemm_gram) instead of the
-// direct product when its matrix-core work -- N K^2 for G's upper triangle plus, per grid
-// point, two passes (G_hi and G_lo) over the block upper triangle of G, 2 M K^2 (1 + BN/K)
-// -- is below 0.7 of the direct 2 M K N per grid point, for in_features up to 32768.
+// direct product when it is estimated to take less time, for in_features up to 32768.
+// Matrix-core work in flops: N K^2 for G's upper triangle, and per grid point
+// M K^2 (1 + BN/K) over the block upper triangle of G, against the direct 2 M K N.  The
+// Gram pass runs at about a third of the loss product's rate (its fp64 flushes and its
+// re-reads of X), hence the weight kGramPassWeight; the triangular product loses a little
+// to its uneven tiles, hence the ratio.
 #ifndef AWQ_LOSS_GRAM_RATIO
-#define AWQ_LOSS_GRAM_RATIO 0.7
+#define AWQ_LOSS_GRAM_RATIO 0.85
 #endif
+constexpr double kGramPassWeight = 3.0;
 inline bool loss_use_gram(int64_t M, int64_t K, int64_t N, int64_t n_alpha) {
   if (M <= 0 || K <= 0 || N <= 0 || K > 32768) return false;
   const double k2 = (double)K * (double)K;
-  const double gram = (double)N * k2 + 2.0 * (double)M * k2 * (double)n_alpha *
-                                           (1.0 + (double)kLossBN / (double)K);
+  const double gram = kGramPassWeight * (double)N * k2 +
+                      (double)M * k2 * (double)n_alpha * (1.0 + (double)kLossBN / (double)K);
   const double direct = 2.0 * (double)M * (double)K * (double)N * (double)n_alpha;
   return gram < AWQ_LOSS_GRAM_RATIO * direct;
 }
@@ -117,14 +121,16 @@ hipError_t launch_fold_inverse_scales(const uint16_t* x, const float* s, int T, 
 // partials[k * tiles + tm * tiles_n + tn] = sum over the tile of (dW_k X^T)^2.
 hipError_t launch_loss_gemm(const uint16_t* dW, const uint16_t* X, int M, int N, int K,
                             int nb, double* partials, hipStream_t stream);
-// G 2^-gexp = Ghi + Glo (fp16 [K][K]) from X fp16 [N][K] (K even): fp32 G [K][K] and
-// the per-tile maxima tmax [gram_full_tiles(K)] are scratch.
+// From X fp16 [N][K] (K even): Gh = G' 2^-gexp (fp16 [K][K]; G with the kLossBN blocks
+// above its diagonal doubled, those below and the diagonal zero) and gdiag = diag(G)
+// 2^-gexp (fp32 [K]); fp32 G [K][K] and the per-tile maxima tmax [gram_full_tiles(K)] are
+// scratch.
 int gram_full_tiles(int64_t K);
 hipError_t launch_gram_full(const uint16_t* X, int N, int K, float* G, float* tmax,
-                            uint16_t* Ghi, uint16_t* Glo, int32_t* gexp, hipStream_t stream);
+                            uint16_t* Gh, float* gdiag, int32_t* gexp, hipStream_t stream);
 // partials as launch_loss_gemm (loss_tiles_m(M) x loss_tiles_n(K) tiles per grid point),
 // each the tile's share of sum_r dW_r G dW_r^T.
-hipError_t launch_loss_gemm_gram(const uint16_t* dW, const uint16_t* Ghi, const uint16_t* Glo,
+hipError_t launch_loss_gemm_gram(const uint16_t* dW, const uint16_t* Gh, const float* gdiag,
                                  const int32_t* gexp, int M, int K, int nb, double* partials,
                                  hipStream_t stream);
 hipError_t launch_reduce_select(const double* partials, int n_alpha, int tiles,

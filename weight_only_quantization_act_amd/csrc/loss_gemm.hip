@@ -65,6 +65,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 typedef int int32x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // Raw buffer resource (gfx9 layout): 48-bit base, stride 0, byte range, 32-bit data
 // format.  Accesses at offsets >= num_bytes return zero.
@@ -138,15 +140,18 @@ struct Stage {
 };
 
 // GRAM = false: C = dW_k X^T (X fp16 [N][K]) and the tile's sum of squares.
-// GRAM = true:  C = dW_k G'^T with G' 2^-gexp = G_hi + G_lo fp16 [K][K] (B0, B1; N = K):
-// G' is G with its BN x BN blocks above the diagonal doubled and those below it zero, so
-// column tile tn needs k from tn BN on only.  The K loop runs twice over that range, first
-// over G_hi then over G_lo with the same dW_k, and the tile's sum of C * dW_k at the same
-// positions, times 2^gexp, is the tile's share of sum_r dW_r G dW_r^T.
+// GRAM = true:  C = G' dW_k^T with G' 2^-gexp fp16 [K][K] passed as X (N = K): the A side
+// of the tile is channels (rows of G'), the B side rows of dW_k.  G' is G with its BM x BM
+// blocks above the diagonal doubled, those below it zero and its diagonal zero, so tile
+// row tm needs k from tm BM on only.  The tile's sum over its positions (c, r) of
+// dW_k[r][c] (C[c][r] + dW_k[r][c] gdiag[c]), with gdiag = diag(G) 2^-gexp in fp32, times
+// 2^gexp, is the tile's share of sum_r dW_r G dW_r^T.  With channels on the A side, the
+// four consecutive C rows a lane holds are four consecutive channels of one dW row, so
+// the epilogue reads dW in 8-byte pieces.
 template <class S, bool GRAM>
 __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     const uint16_t* __restrict__ dW, const uint16_t* __restrict__ X,
-    const uint16_t* __restrict__ B1, int M, int N, int K, int tiles_m, int tiles_n, int nb,
+    const float* __restrict__ gdiag, int M, int N, int K, int tiles_m, int tiles_n, int nb,
     const int32_t* __restrict__ gexp, double* __restrict__ partials) {
   // One LDS array per pipeline stage: distinct objects let the compiler see that a DMA
   // into one stage never aliases fragment reads from another, so it does not drain the
@@ -166,7 +171,10 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   const int wn = wave % S::WN;
 
   // ---- block -> (grid point, tile row, tile column), XCD-contiguous ----------------
-  const int per_alpha = tiles_m * tiles_n;
+  // GRAM: tile row tm covers k from tm BM on, so a block takes the pair of tile rows tm
+  // and tiles_m - 1 - tm (tiles_m + 1 blocks of G' between them): equal work per block.
+  const int tm_count = GRAM ? (tiles_m + 1) / 2 : tiles_m;
+  const int per_alpha = tm_count * tiles_n;
   const int total = nb * per_alpha;
   const int b = blockIdx.x;
   const int xcd = b & 7;
@@ -177,15 +185,14 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   const int rem = logical - kk_alpha * per_alpha;
   const int band = rem / (kBandM * tiles_n);
   const int first_m = band * kBandM;
-  const int band_rows = min(kBandM, tiles_m - first_m);
+  const int band_rows = min(kBandM, tm_count - first_m);
   const int in_band = rem - band * kBandM * tiles_n;
   const int tm = first_m + in_band % band_rows;
   const int tn = in_band / band_rows;
 
-  const uint16_t* A = dW + (size_t)kk_alpha * M * K + (size_t)tm * BM * K;
-  const uint16_t* B = X + (size_t)tn * BN * K;
-  const int rows_a = min(BM, M - tm * BM);
-  const int rows_b = min(BN, N - tn * BN);
+  const uint16_t* B = GRAM ? dW + (size_t)kk_alpha * M * K + (size_t)tn * BN * K
+                           : X + (size_t)tn * BN * K;
+  const int rows_b = GRAM ? min(BN, M - tn * BN) : min(BN, N - tn * BN);
 
   // ---- DMA through buffer resources.  Lane l of a wave-level buffer_load ... lds fills
   //      LDS bytes [16 l, 16 l + 16) of a 1 KiB block: row l / CPR of the block,
@@ -199,10 +206,8 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   const int dma_row_in = lane / S::CPR;
   const int dma_lchunk_even = (lane % S::CPR) ^ S::swz(dma_row_in);
   const int dma_lchunk_odd = (lane % S::CPR) ^ S::swz(dma_row_in + (S::ROWS_PER_DMA == 8 ? 8 : 0));
-  const int32x4 rsrc_a = make_rsrc(A, (unsigned)rows_a * (unsigned)K * 2u);
-  const int32x4 rsrc_b0 = make_rsrc(B, (unsigned)rows_b * (unsigned)K * 2u);
-  int32x4 rsrc_b1 = rsrc_b0;
-  if constexpr (GRAM) rsrc_b1 = make_rsrc(B1 + (size_t)tn * BN * K, (unsigned)rows_b * (unsigned)K * 2u);
+  int32x4 rsrc_a;  // set per tile row (part) below
+  const int32x4 rsrc_b = make_rsrc(B, (unsigned)rows_b * (unsigned)K * 2u);
   static_assert(S::DMA_A % 2 == 0 && S::DMA_B % 2 == 0, "block parity follows j");
   const unsigned row_a = (unsigned)(wave * S::DMA_A * S::ROWS_PER_DMA + dma_row_in);
   const unsigned row_b = (unsigned)(wave * S::DMA_B * S::ROWS_PER_DMA + dma_row_in);
@@ -225,21 +230,16 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   const unsigned lds_stage[4] = {lds_addr(sm0), lds_addr(sm1), lds_addr(sm2), lds_addr(sm3)};
 
   // k-tiles rounded up to a multiple of NS: the padding tiles lie past in_features, read
-  // as zeros and add nothing, and the NS-unrolled loop below then has a single exit.  In
-  // GRAM mode the loop covers 2 nk tiles: tile kt reads channels (kt mod nk) BK of dW and
-  // of G_hi (kt < nk) or G_lo; tiles past the end read zeros.
+  // as zeros and add nothing, and the NS-unrolled loop below then has a single exit.
   const int nk = ((K + S::BK * S::NS - 1) / (S::BK * S::NS)) * S::NS;
-  // GRAM: k-tiles kt0 .. nk - 1 in each pass (kt0 a multiple of NS since BN / BK is)
-  static_assert(!GRAM || (BN / S::BK) % S::NS == 0, "the diagonal block starts on a whole pipeline step");
-  const int kt0 = GRAM ? min(tn * (BN / S::BK), nk) : 0;
-  const int npass = nk - kt0;
-  const int nkt = GRAM ? 2 * npass : nk;
+  // GRAM: k-tiles kt0 .. nk - 1 (kt0 a multiple of NS since BM / BK is); set per part
+  static_assert(!GRAM || (BM / S::BK) % S::NS == 0, "the diagonal block starts on a whole pipeline step");
+  int kt0 = 0, nkt = nk;
 
-  // loop tile i -> k-tile (kt0 + i mod npass) of pass i / npass; past the end: zeros
+  // loop tile i -> k-tile kt0 + i; past the end: zeros
   auto dma_stage = [&](auto st, int i) {
     constexpr int ST = decltype(st)::value;
-    const int k0 = (i < nkt ? (GRAM ? kt0 + (i >= npass ? i - npass : i) : i) : nk) * S::BK;
-    const int32x4 rsrc_b = (GRAM && i >= npass) ? rsrc_b1 : rsrc_b0;
+    const int k0 = (i < nkt ? kt0 + i : nk) * S::BK;
     const unsigned la = lds_stage[ST] + (unsigned)(wave * S::DMA_A) * 1024u;
     const unsigned lb = lds_stage[ST] + (unsigned)S::A_BYTES + (unsigned)(wave * S::DMA_B) * 1024u;
     const bool k_ok0 = k0 + dma_lchunk_even * 8 < K;
@@ -278,12 +278,6 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   };
 
   floatx16 acc[S::MI][S::NI];
-#pragma unroll
-  for (int i = 0; i < S::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < S::NI; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   // Interleave one k-step's MFMAs with the LDS reads of the next step's fragments so
   // that neither the matrix pipe nor the LDS sees a burst.
@@ -315,19 +309,8 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   using I1 = std::integral_constant<int, 1 % S::NS>;
   using I2 = std::integral_constant<int, 2 % S::NS>;
   using I3 = std::integral_constant<int, 3 % S::NS>;
-  dma_stage(I0{}, 0);
-  if constexpr (S::NS > 1) dma_stage(I1{}, 1);
-  if constexpr (S::NS > 2) dma_stage(I2{}, 2);
-  if constexpr (S::NS > 3) dma_stage(I3{}, 3);
-  __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 1) * S::PER_STAGE>::value);
-  __builtin_amdgcn_s_barrier();
-
-  // Fragments ping-pong between two register sets; KSTEPS is even, so a stage always
-  // starts with its first k-step in f0 and ends having loaded the next stage's first
-  // k-step into f0 as well.
   static_assert(S::KSTEPS % 2 == 0, "even number of 16-channel steps per stage");
   Frag f0, f1;
-  if (nk > 0) load_frag(I0{}, 0, f0);
 
   // one k-tile held in stage ST (k-tile index kt)
   auto step = [&](auto st, int kt) {
@@ -353,6 +336,44 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     mma(f1);
   };
 
+  double ssum = 0.0;
+  // One pass per tile row of the block (two for a GRAM pair).  Between passes no barrier
+  // is needed: every wave's DMAs of the next pass go to its own LDS blocks after its own
+  // vmcnt(0), and other waves have finished their fragment reads of the last real stage
+  // at the final barrier of the previous pass (the read after it only loads a register
+  // set nobody uses).
+  const int nparts = (GRAM && tiles_m - 1 - tm != tm) ? 2 : 1;
+  for (int part = 0; part < nparts; ++part) {
+  const int tmc = part == 0 ? tm : tiles_m - 1 - tm;
+  {
+    const uint16_t* A = GRAM ? X + (size_t)tmc * BM * K
+                             : dW + (size_t)kk_alpha * M * K + (size_t)tmc * BM * K;
+    const int rows_a = GRAM ? min(BM, N - tmc * BM) : min(BM, M - tmc * BM);
+    rsrc_a = make_rsrc(A, (unsigned)rows_a * (unsigned)K * 2u);
+    if constexpr (GRAM) {
+      kt0 = min(tmc * (BM / S::BK), nk);
+      nkt = nk - kt0;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  dma_stage(I0{}, 0);
+  if constexpr (S::NS > 1) dma_stage(I1{}, 1);
+  if constexpr (S::NS > 2) dma_stage(I2{}, 2);
+  if constexpr (S::NS > 3) dma_stage(I3{}, 3);
+  __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 1) * S::PER_STAGE>::value);
+  __builtin_amdgcn_s_barrier();
+
+  // Fragments ping-pong between two register sets; KSTEPS is even, so a stage always
+  // starts with its first k-step in f0 and ends having loaded the next stage's first
+  // k-step into f0 as well.
+  if (nk > 0) load_frag(I0{}, 0, f0);
+
   for (int kt = 0; kt < nkt; kt += S::NS) {
     step(I0{}, kt);
     if constexpr (S::NS > 1) step(I1{}, kt + 1);
@@ -361,34 +382,73 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   }
   __builtin_amdgcn_s_waitcnt(WaitVmLgkm<0>::value);  // no LDS write may outlive the block
 
-  // ---- epilogue: sum of squares of the 256 x 256 output tile (GRAM: sum of C * dW at
-  //      the output positions; element e of a 32x32 block is row 8 (e / 4) + 4 (l / 32) +
-  //      (e mod 4), column l mod 32) ---------------------------------------------------
-  double ssum = 0.0;
+  // ---- epilogue: sum of squares of the 256 x 256 output tile (GRAM: sum of
+  //      dW (C + dW gdiag) at the output positions); element e of a 32x32 block is row
+  //      8 (e / 4) + 4 (l / 32) + (e mod 4), column l mod 32 ---------------------------
+  if constexpr (GRAM) {
+    // dW_k and gdiag through buffer resources: a lane's piece outside the layer (row past
+    // out_features or channel past in_features) takes an offset past the resource's range
+    // and reads zeros.  M K < 2^31 and K is a multiple of 32, so dW_k's byte range ends
+    // below the out-of-range offset.
+    constexpr unsigned kOff = 0xfffffff0u;
+    const __amdgpu_buffer_rsrc_t rs_d = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(dW + (size_t)kk_alpha * M * K), (short)0, (int)((unsigned)M * (unsigned)K * 2u),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_g =
+        __builtin_amdgcn_make_buffer_rsrc((void*)gdiag, (short)0, N * 4, 0x00020000);
 #pragma unroll
-  for (int mi = 0; mi < S::MI; ++mi)
+    for (int mi = 0; mi < S::MI; ++mi) {
+      // channels c0 + 8 j + (0..3) of rows r_ni: one 8-byte piece of dW and one 16-byte
+      // piece of gdiag per j (c0 is a multiple of 4 and K of 32, so a piece is either
+      // wholly inside in_features or wholly past it)
+      const int c0 = tmc * BM + wm * S::MI * 32 + mi * 32 + 4 * (lane >> 5);
+      floatx4 gd[4];
+      u32x2 dv[S::NI][4];
 #pragma unroll
-    for (int ni = 0; ni < S::NI; ++ni) {
-      float t = 0.0f;
-      if constexpr (GRAM) {
-        const int col = tn * BN + wn * S::NI * 32 + ni * 32 + (lane & 31);
-        const int r0 = wm * S::MI * 32 + mi * 32 + 4 * (lane >> 5);
-        uint16_t dv[16];
+      for (int j = 0; j < 4; ++j)
+        gd[j] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rs_g, c0 + 8 * j < N ? (c0 + 8 * j) * 4u : kOff, 0, 0));
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = r0 + 8 * (e >> 2) + (e & 3);
-          dv[e] = (r < rows_a && col < N) ? A[(size_t)r * K + col] : (uint16_t)0;
+      for (int ni = 0; ni < S::NI; ++ni) {
+        const int r = tn * BN + wn * S::NI * 32 + ni * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const unsigned off = (r < M && c0 + 8 * j < N)
+                                   ? ((unsigned)r * (unsigned)K + (unsigned)(c0 + 8 * j)) * 2u
+                                   : kOff;
+          dv[ni][j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs_d, off, 0, 0));
         }
+      }
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          t += acc[mi][ni][e] * (float)__builtin_bit_cast(_Float16, dv[e]);
-      } else {
+      for (int ni = 0; ni < S::NI; ++ni) {
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const unsigned w = dv[ni][j][q >> 1];
+            const float d = (float)__builtin_bit_cast(
+                _Float16, (uint16_t)(q & 1 ? w >> 16 : w & 0xffffu));
+            t = fmaf(d, fmaf(d, gd[j][q], acc[mi][ni][4 * j + q]), t);
+          }
+        }
+        ssum += (double)t;
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one block row at a time: low VGPR pressure
+    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < S::MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < S::NI; ++ni) {
+        float t = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) t += acc[mi][ni][e] * acc[mi][ni][e];
+        ssum += (double)t;
+        __builtin_amdgcn_sched_barrier(0);  // one 32x32 block at a time: low VGPR pressure
       }
-      ssum += (double)t;
-      __builtin_amdgcn_sched_barrier(0);  // one 32x32 block at a time: low VGPR pressure
-    }
+  }
+  }  // part
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off);
   if (lane == 0) red[wave] = ssum;
@@ -398,7 +458,9 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
 #pragma unroll
     for (int w = 1; w < S::WAVES; ++w) t += red[w];
     if constexpr (GRAM) t = ldexp(t, gexp[0]);
-    partials[(size_t)kk_alpha * per_alpha + (size_t)tm * tiles_n + tn] = t;
+    double* part_k = partials + (size_t)kk_alpha * tiles_m * tiles_n;
+    part_k[(size_t)tm * tiles_n + tn] = t;
+    if (nparts == 2) part_k[(size_t)(tiles_m - 1 - tm) * tiles_n + tn] = 0.0;
   }
 }
 
@@ -462,15 +524,18 @@ hipError_t launch_loss_gemm(const uint16_t* dW, const uint16_t* X, int M, int N,
   return hipGetLastError();
 }
 
-hipError_t launch_loss_gemm_gram(const uint16_t* dW, const uint16_t* Ghi, const uint16_t* Glo,
+hipError_t launch_loss_gemm_gram(const uint16_t* dW, const uint16_t* Gh, const float* gdiag,
                                  const int32_t* gexp, int M, int K, int nb, double* partials,
                                  hipStream_t stream) {
+  static_assert(kLossBM == kLossBN, "the G form uses square tiles (G's blocks)");
   if (M <= 0 || K <= 0 || nb <= 0) return hipSuccess;
-  const int tm = (int)loss_tiles_m(M), tn = (int)loss_tiles_n(K);
-  const long long blocks = (long long)nb * tm * tn;
+  // tile rows over channels (rows of G'), tile columns over rows of dW; a block takes a
+  // pair of tile rows
+  const int tm = (int)loss_tiles_m(K), tn = (int)loss_tiles_n(M);
+  const long long blocks = (long long)nb * ((tm + 1) / 2) * tn;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_loss_gemm<LossStage, true>), dim3((unsigned)blocks),
-                     dim3(LossStage::THREADS), 0, stream, dW, Ghi, Glo, M, K, K, tm, tn, nb, gexp,
+                     dim3(LossStage::THREADS), 0, stream, dW, Gh, gdiag, M, K, K, tm, tn, nb, gexp,
                      partials);
   return hipGetLastError();
 }

@@ -6,20 +6,24 @@
 //
 // ||Delta W X^T||_F^2 = sum over rows r of Delta W_r G Delta W_r^T with G = X^T X (K x K).
 // Forming G costs N K^2 multiply-adds once (the upper triangle); each grid point then
-// costs M K^2 (twice, for the fp16 split of G below) instead of M K N, which pays when N
-// is several times K.
+// costs about M K^2 / 2 (the block upper triangle of G below) instead of M K N, which
+// pays once N is about as large as K.
 //
 //   k_gram_full        G's upper triangle in 128 x 128 tiles, every tile over all tokens:
 //                      fp16 products (exact in fp32) summed on the matrix cores in fp32 over
 //                      at most 256 tokens, those sums added in fp64, the total rounded to
 //                      fp32 and written at (a, b) and (b, a); each tile's largest |G|.
 //   k_gram_full_split  one power of two 2^-ex for the whole matrix (its largest magnitude
-//                      into [2^13, 2^14)) and G' 2^-ex = hi + lo in fp16 (about 2^-22
-//                      relative), the two operands of the per-grid-point product.  G' is G
-//                      with its blocks of kLossBN x kLossBN above the diagonal doubled
-//                      (exact) and those below it zero: with d the rows of dW,
-//                      sum_r d_r G d_r^T = sum over column blocks a of d_a . (G' d)_a, and
-//                      the product for column block a only runs over k from block a on.
+//                      into [2^13, 2^14)) and the operand of the per-grid-point product:
+//                      G' 2^-ex in fp16, where G' is G with its blocks of kLossBN x kLossBN
+//                      above the diagonal doubled (exact), those below it zero and its
+//                      diagonal zero.  With d the rows of dW,
+//                      sum_r d_r G d_r^T = sum over column blocks a of d_a . (G' d)_a
+//                                          + sum_c (sum_r d_rc^2) G_cc,
+//                      the product for column block a only runs over k from block a on,
+//                      and the diagonal term, which carries most of the sum, is taken in
+//                      fp32 from gdiag = diag(G) 2^-ex (fp32) in the product's epilogue,
+//                      so that only the off-diagonal entries are rounded to fp16.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -187,8 +191,8 @@ __global__ __launch_bounds__(kGfThreads) void k_gram_full(const uint16_t* __rest
 __global__ __launch_bounds__(256) void k_gram_full_split(const float* __restrict__ G, int K,
                                                          int64_t KK,
                                                          const float* __restrict__ tmax,
-                                                         int ntiles, uint16_t* __restrict__ Ghi,
-                                                         uint16_t* __restrict__ Glo,
+                                                         int ntiles, uint16_t* __restrict__ Gh,
+                                                         float* __restrict__ gdiag,
                                                          int32_t* __restrict__ gexp) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
@@ -212,11 +216,13 @@ __global__ __launch_bounds__(256) void k_gram_full_split(const float* __restrict
     if (j >= KK) break;
     const int64_t row = j / K, col = j - (j / K) * K;
     const int64_t ra = row / kLossBN, cb = col / kLossBN;
-    const float g = cb < ra ? 0.0f : (cb > ra ? 2.0f * G[j] : G[j]);
-    const float vs = ldexpf(g, -ex);
-    const uint16_t hi = f2h(vs);
-    Ghi[j] = hi;
-    Glo[j] = f2h(vs - h2f(hi));
+    if (row == col) {
+      gdiag[row] = ldexpf(G[j], -ex);
+      Gh[j] = 0;
+    } else {
+      const float g = cb < ra ? 0.0f : (cb > ra ? 2.0f * G[j] : G[j]);
+      Gh[j] = f2h(ldexpf(g, -ex));
+    }
   }
 }
 
@@ -228,7 +234,7 @@ int gram_full_tiles(int64_t K) {
 }
 
 hipError_t launch_gram_full(const uint16_t* X, int N, int K, float* G, float* tmax,
-                            uint16_t* Ghi, uint16_t* Glo, int32_t* gexp, hipStream_t stream) {
+                            uint16_t* Gh, float* gdiag, int32_t* gexp, hipStream_t stream) {
   if (K <= 0) return hipSuccess;
   if (K % 2 != 0) return hipErrorInvalidValue;
   const int nspan = (K + kGfSpan - 1) / kGfSpan;
@@ -240,7 +246,7 @@ hipError_t launch_gram_full(const uint16_t* X, int N, int K, float* G, float* tm
   const int64_t KK = (int64_t)K * K;
   const int64_t blocks = (KK + kGfSplitChunk - 1) / kGfSplitChunk;
   hipLaunchKernelGGL(k_gram_full_split, dim3((unsigned)blocks), dim3(256), 0, stream, G, K, KK,
-                     tmax, ntiles, Ghi, Glo, gexp);
+                     tmax, ntiles, Gh, gdiag, gexp);
   return hipGetLastError();
 }
 
