@@ -307,7 +307,7 @@ def main():
                               direct_flops / ((gemm_ms + gram_ms) * 1e-3) / 1e12},
             **({"gram": {"ms": gram_ms, "TFLOP/s": gram_flops / (gram_ms * 1e-3) / 1e12,
                          "frac_mfma": gram_flops / (gram_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                         "kernels": "k_gram_full + k_gram_full_split"}} if gram else {}),
+                         "kernels": "k_transpose_x + k_loss_gemm<G build> + k_gram_full_split"}} if gram else {}),
             "quant_pack": {"ms": pack_ms, "GB/s": pack_bytes / (pack_ms * 1e-3) / 1e9,
                            "frac_hbm": pack_bytes / (pack_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         },

@@ -126,7 +126,8 @@ int awq_act_stats_ex(const void* X, int64_t n_tokens, int64_t in_features, int32
  * taken as sum_r dW_r G dW_r^T with G = X^T X [AWQ-notes §1.1]: G summed on the matrix
  * cores (fp32 over at most 256 tokens, then fp64) and stored fp32; its off-diagonal
  * entries enter an fp16 MFMA product, its diagonal enters in fp32.
- * out_features >= 0, in_features >= 0 (multiple of group_size), n_tokens >= 1.
+ * out_features >= 0, in_features >= 0 (multiple of group_size, at most 4194304),
+ * n_tokens >= 1.
  * ---------------------------------------------------------------------------------- */
 
 /* Workspace bytes for a search that processes `alpha_batch` grid points per pass

@@ -103,14 +103,23 @@ def test_workspace_query(L):
     assert one == fixed + M * K * 2
     assert full == fixed + 20 * M * K * 2
     assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 7) == fixed + 7 * M * K * 2
-    # the G form: tiles over K, then fp32 G, fp16 G', fp32 diagonal, the 528 tile maxima of
-    # G's upper triangle in 128-channel spans, and the exponent, each 256-byte aligned
+    # the G form: tiles over K, then X^T (fp16 [K][N]; one token split, so no partials),
+    # fp32 G, fp16 G', fp32 diagonal, the maxima of the 136 tiles of G's upper block
+    # triangle, and the exponent, each 256-byte aligned
     N = 4096
     assert awq.awq_loss_form(M, K, N, 20) == awq.AWQ_LOSS_GRAM
     tiles = (M // 256) * (K // 256)
-    fixed = 20 * K * 4 + 20 * tiles * 8 + K * K * 4 + K * K * 2 + K * 4 + 2304 + 256
+    fixed = (20 * K * 4 + 20 * tiles * 8 + K * N * 2 + K * K * 4 + K * K * 2 + K * 4 + 768
+             + 256)
     assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 1) == fixed + M * K * 2
     assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 0) == fixed + 20 * M * K * 2
+    # more tokens than one split (8192) holds: fp32 partial tiles per split besides
+    N = 20000
+    ld = 20000                                    # already a multiple of 8
+    splits, pairs = 3, 136
+    fixed = (20 * K * 4 + 20 * tiles * 8 + K * ld * 2 + splits * pairs * 256 * 256 * 4
+             + K * K * 4 + K * K * 2 + K * 4 + ((4 * pairs * 4 + 255) // 256) * 256 + 256)
+    assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 1) == fixed + M * K * 2
     assert awq.awq_workspace_bytes(M, K, N, cfg, 0, 0) == 0
     assert awq.awq_workspace_bytes(M, 100, N, cfg, 20, 0) == 0
     assert awq.awq_workspace_bytes(0, K, N, cfg, 3, 0) == ((3 * K * 4 + 255) // 256) * 256
@@ -160,8 +169,11 @@ def test_loss_form_choice():
     assert q(4096, 11008, 16384, 20) == awq.AWQ_LOSS_GRAM
     assert q(4096, 40960, 32768, 20) == awq.AWQ_LOSS_DIRECT   # G beyond 32768 channels
     assert q(0, 4096, 4096, 20) == awq.AWQ_LOSS_DIRECT
-    for bad in [(-1, 64, 64, 20), (64, 64, 0, 20), (64, 64, 64, 0), (64, 64, 64, 65)]:
+    for bad in [(-1, 64, 64, 20), (64, 64, 0, 20), (64, 64, 64, 0), (64, 64, 64, 65),
+                (1, 1 << 23, 16, 20)]:
         assert q(*bad) == -1
+    # in_features beyond 2^22: the search rejects the shape
+    assert awq.awq_workspace_bytes(1, 1 << 23, 16, awq.qconfig(4, 128, 1), 20, 0) == 0
     # the choice agrees with the workspace: the G form holds G (fp32 and fp16) besides dW
     cfg = awq.qconfig(4, 128, 1)
     direct = awq.awq_workspace_bytes(4096, 4096, 1024, cfg, 20, 0)

@@ -150,6 +150,8 @@ SEARCH_CASES = [
     (300, 256, 3000, 4, 128, 1),
     (130, 320, 5000, 3, 32, 0),     # 128-channel Gram spans cut at in_features
     (64, 1024, 8192, 4, 128, 1),
+    (100, 96, 3000, 3, 32, 1),      # 96 channels: partial transpose and G tiles
+    (200, 256, 20003, 4, 64, 1),    # three token splits of G, the last one ragged
 ]
 
 

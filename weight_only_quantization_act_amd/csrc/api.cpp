@@ -33,6 +33,10 @@ int weight_shape(int64_t M, int64_t K, const awq_qconfig* cfg) {
   return AWQ_OK;
 }
 
+// The loss product addresses a 256-row panel of dW or X through 32-bit buffer offsets
+// (at most 2^31 bytes), which bounds in_features for the search.
+constexpr int64_t kMaxSearchK = (int64_t)1 << 22;
+
 int token_shape(int64_t N, int64_t K) {
   if (N < 1 || K < 0) return AWQ_E_SHAPE;
   if (N >= kMaxElems || (K > 0 && N >= kMaxElems / K)) return AWQ_E_SHAPE;
@@ -52,11 +56,11 @@ int device_ptr(const void* p) {
   return AWQ_E_DEVICE;
 }
 
-// Workspace of the search: s table | loss partials | (Gram form: fp32 G, fp16 G', fp32
-// diagonal, tile maxima, exponent) | dW batch.
+// Workspace of the search: s table | loss partials | (Gram form: X^T, split partials,
+// fp32 G, fp16 G', fp32 diagonal, tile maxima, exponent) | dW batch.
 struct SearchLayout {
   size_t s_off, p_off, dw_off;
-  size_t g32_off, gh_off, gdiag_off, tmax_off, gexp_off;
+  size_t xt_off, gpart_off, g32_off, gh_off, gdiag_off, tmax_off, gexp_off;
   size_t dw_bytes_per_alpha;
   int64_t tiles;
   bool gram;
@@ -70,9 +74,16 @@ SearchLayout search_layout(int64_t M, int64_t K, int64_t N, int32_t n_alpha) {
   L.s_off = 0;
   L.p_off = round_up((size_t)n_alpha * (size_t)K * sizeof(float), kAlign);
   size_t off = L.p_off + round_up((size_t)n_alpha * (size_t)L.tiles * sizeof(double), kAlign);
-  L.g32_off = L.gh_off = L.gdiag_off = L.tmax_off = L.gexp_off = off;
+  L.xt_off = L.gpart_off = L.g32_off = L.gh_off = L.gdiag_off = L.tmax_off = L.gexp_off = off;
   if (L.gram) {
     const size_t kk = (size_t)K * (size_t)K;
+    const awq::GramPlan g = awq::gram_plan(N, K);
+    L.xt_off = off;
+    off += round_up((size_t)K * (size_t)g.ld * sizeof(uint16_t), kAlign);
+    L.gpart_off = off;
+    if (g.splits > 1)
+      off += round_up((size_t)g.splits * (size_t)g.pairs * awq::kLossBM * awq::kLossBN * sizeof(float),
+                      kAlign);
     L.g32_off = off;
     off += round_up(kk * sizeof(float), kAlign);
     L.gh_off = off;
@@ -80,7 +91,7 @@ SearchLayout search_layout(int64_t M, int64_t K, int64_t N, int32_t n_alpha) {
     L.gdiag_off = off;
     off += round_up((size_t)K * sizeof(float), kAlign);
     L.tmax_off = off;
-    off += round_up((size_t)awq::gram_full_tiles(K) * sizeof(float), kAlign);
+    off += round_up((size_t)g.tmax * sizeof(float), kAlign);
     L.gexp_off = off;
     off += kAlign;
   }
@@ -134,7 +145,8 @@ int run_search(const void* W, const void* X, const float* s_table, int64_t M, in
     if (L.gram) {  // G = X^T X once, for every grid point
       if ((st = record(hook.gram_start, sm))) return st;
       st = hip_status(awq::launch_gram_full((const uint16_t*)X, (int)N, (int)K,
-                                            (float*)(ws + L.g32_off),
+                                            (uint16_t*)(ws + L.xt_off),
+                                            (float*)(ws + L.gpart_off), (float*)(ws + L.g32_off),
                                             (float*)(ws + L.tmax_off), Gh, gdiag, gexp, sm));
       if (st) return st;
       if ((st = record(hook.gram_stop, sm))) return st;
@@ -233,6 +245,7 @@ size_t awq_workspace_bytes(int64_t out_features, int64_t in_features, int64_t n_
   if (!cfg_valid(cfg)) return 0;
   if (weight_shape(out_features, in_features, cfg) != AWQ_OK) return 0;
   if (token_shape(n_tokens, in_features) != AWQ_OK) return 0;
+  if (in_features > kMaxSearchK) return 0;
   if (n_alpha < 1 || n_alpha > AWQ_MAX_ALPHA) return 0;
   if (alpha_batch <= 0 || alpha_batch > n_alpha) alpha_batch = n_alpha;
   SearchLayout L = search_layout(out_features, in_features, n_tokens, n_alpha);
@@ -240,7 +253,9 @@ size_t awq_workspace_bytes(int64_t out_features, int64_t in_features, int64_t n_
 }
 
 int awq_loss_form(int64_t out_features, int64_t in_features, int64_t n_tokens, int32_t n_alpha) {
-  if (out_features < 0 || in_features < 0 || token_shape(n_tokens, in_features) != AWQ_OK) return -1;
+  if (out_features < 0 || in_features < 0 || in_features > kMaxSearchK ||
+      token_shape(n_tokens, in_features) != AWQ_OK)
+    return -1;
   if (n_alpha < 1 || n_alpha > AWQ_MAX_ALPHA) return -1;
   return search_layout(out_features, in_features, n_tokens, n_alpha).gram ? AWQ_LOSS_GRAM
                                                                            : AWQ_LOSS_DIRECT;
@@ -259,6 +274,7 @@ int awq_search_scales(const void* W, const void* X, const float* a, int64_t out_
   int st = weight_shape(M, K, cfg);
   if (st != AWQ_OK) return st;
   if ((st = token_shape(N, K)) != AWQ_OK) return st;
+  if (K > kMaxSearchK) return AWQ_E_SHAPE;
   if (n_alpha < 1 || n_alpha > AWQ_MAX_ALPHA) return AWQ_E_ALPHA;
   awq::AlphaList al;
   memset(&al, 0, sizeof(al));
@@ -298,6 +314,7 @@ int awq_search_scale_table(const void* W, const void* X, const float* s_table, i
   int st = weight_shape(M, K, cfg);
   if (st != AWQ_OK) return st;
   if ((st = token_shape(N, K)) != AWQ_OK) return st;
+  if (K > kMaxSearchK) return AWQ_E_SHAPE;
   if (n_cand < 1 || n_cand > AWQ_MAX_ALPHA) return AWQ_E_ALPHA;
   if (K > 0 && (int64_t)n_cand * K >= kMaxElems) return AWQ_E_SHAPE;
   if (workspace_bytes < awq_workspace_bytes(M, K, N, cfg, n_cand, 1)) return AWQ_E_WORKSPACE;

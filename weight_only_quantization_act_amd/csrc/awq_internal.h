@@ -27,6 +27,8 @@ inline int64_t loss_tiles_n(int64_t N) { return (N + kLossBN - 1) / kLossBN; }
 constexpr double kGramPassWeight = 3.0;
 inline bool loss_use_gram(int64_t M, int64_t K, int64_t N, int64_t n_alpha) {
   if (M <= 0 || K <= 0 || N <= 0 || K > 32768) return false;
+  // the G pass reads X^T [K][N rounded up to 8] through 32-bit buffer offsets
+  if ((double)K * (double)(N + 8) * 2.0 > 2147483648.0) return false;
   const double k2 = (double)K * (double)K;
   const double gram = kGramPassWeight * (double)N * k2 +
                       (double)M * k2 * (double)n_alpha * (1.0 + (double)kLossBN / (double)K);
@@ -121,13 +123,24 @@ hipError_t launch_fold_inverse_scales(const uint16_t* x, const float* s, int T, 
 // partials[k * tiles + tm * tiles_n + tn] = sum over the tile of (dW_k X^T)^2.
 hipError_t launch_loss_gemm(const uint16_t* dW, const uint16_t* X, int M, int N, int K,
                             int nb, double* partials, hipStream_t stream);
-// From X fp16 [N][K] (K even): Gh = G' 2^-gexp (fp16 [K][K]; G with the kLossBN blocks
-// above its diagonal doubled, those below and the diagonal zero) and gdiag = diag(G)
-// 2^-gexp (fp32 [K]); fp32 G [K][K] and the per-tile maxima tmax [gram_full_tiles(K)] are
-// scratch.
-int gram_full_tiles(int64_t K);
-hipError_t launch_gram_full(const uint16_t* X, int N, int K, float* G, float* tmax,
-                            uint16_t* Gh, float* gdiag, int32_t* gexp, hipStream_t stream);
+// The G form's Gram pass (loss_gram.hip): Xt = X^T (fp16 [K][ld]) | split partials
+// (fp32 [splits][pairs][kLossBM][kLossBN], only with more than one split) | fp32 G [K][K]
+// (upper block triangle) | tile maxima tmax [tmax] are scratch; outputs Gh = G' 2^-gexp
+// (fp16 [K][K]; G with the kLossBN blocks above its diagonal doubled, those below and the
+// diagonal zero), gdiag = diag(G) 2^-gexp (fp32 [K]) and gexp.  Tokens are split in runs of
+// kGramSplitTokens, each summed in fp32 on the matrix cores; K a multiple of 8.
+constexpr int kGramSplitTokens = 8192;
+struct GramPlan {
+  int64_t ld, splits, pairs, tmax;
+};
+GramPlan gram_plan(int64_t N, int64_t K);
+hipError_t launch_gram_full(const uint16_t* X, int N, int K, uint16_t* Xt, float* part,
+                            float* G, float* tmax, uint16_t* Gh, float* gdiag, int32_t* gexp,
+                            hipStream_t stream);
+// G build mode of the loss kernel (loss_gemm.hip): tiles tm <= tn of G over splits of
+// kchunk tokens from Xt [K][ld]; out = G (one split, with tmax [pairs]) or the partials.
+hipError_t launch_gram_build(const uint16_t* Xt, int N, int ld, int K, int kchunk, int splits,
+                             float* out, float* tmax, hipStream_t stream);
 // partials as launch_loss_gemm (loss_tiles_m(M) x loss_tiles_n(K) tiles per grid point),
 // each the tile's share of sum_r dW_r G dW_r^T.
 hipError_t launch_loss_gemm_gram(const uint16_t* dW, const uint16_t* Gh, const float* gdiag,

@@ -139,8 +139,8 @@ struct Stage {
   }
 };
 
-// GRAM = false: C = dW_k X^T (X fp16 [N][K]) and the tile's sum of squares.
-// GRAM = true:  C = G' dW_k^T with G' 2^-gexp fp16 [K][K] passed as X (N = K): the A side
+// MODE kModeDirect: C = dW_k X^T (X fp16 [N][K]) and the tile's sum of squares.
+// MODE kModeGramLoss (GRAM below): C = G' dW_k^T with G' 2^-gexp fp16 [K][K] passed as X (N = K): the A side
 // of the tile is channels (rows of G'), the B side rows of dW_k.  G' is G with its BM x BM
 // blocks above the diagonal doubled, those below it zero and its diagonal zero, so tile
 // row tm needs k from tm BM on only.  The tile's sum over its positions (c, r) of
@@ -148,11 +148,21 @@ struct Stage {
 // 2^gexp, is the tile's share of sum_r dW_r G dW_r^T.  With channels on the A side, the
 // four consecutive C rows a lane holds are four consecutive channels of one dW row, so
 // the epilogue reads dW in 8-byte pieces.
-template <class S, bool GRAM>
+// MODE kModeGramBuild (BUILD below): G = X^T X itself from Xt = X^T (fp16 [K][ld], tokens
+// contiguous, passed as X): the A and B sides are both channels, the reduction runs over
+// the tokens [s kchunk, min(N, (s + 1) kchunk)) of split s (passed as the grid point), and
+// only tiles tm <= tn of G's upper block triangle are formed.  With one split the fp32
+// tile goes to gout = G (fp32 [K][K], upper block triangle only) and its largest |entry|
+// to tmax[pair]; with several, to gout = partial tiles [split][pair][BM][BN].
+constexpr int kModeDirect = 0, kModeGramLoss = 1, kModeGramBuild = 2;
+template <class S, int MODE>
 __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     const uint16_t* __restrict__ dW, const uint16_t* __restrict__ X,
-    const float* __restrict__ gdiag, int M, int N, int K, int tiles_m, int tiles_n, int nb,
-    const int32_t* __restrict__ gexp, double* __restrict__ partials) {
+    const float* __restrict__ gdiag, int M, int N, int K, int ld, int kchunk, int tiles_m,
+    int tiles_n, int nb, const int32_t* __restrict__ gexp, double* __restrict__ partials,
+    float* __restrict__ gout, float* __restrict__ tmax) {
+  constexpr bool GRAM = MODE == kModeGramLoss;
+  constexpr bool BUILD = MODE == kModeGramBuild;
   // One LDS array per pipeline stage: distinct objects let the compiler see that a DMA
   // into one stage never aliases fragment reads from another, so it does not drain the
   // DMA queue before every LDS read.
@@ -161,6 +171,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   __shared__ __attribute__((aligned(1024))) uint8_t sm2[S::NS > 2 ? S::BYTES : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t sm3[S::NS > 3 ? S::BYTES : 16];
   __shared__ double red[S::WAVES];
+  __shared__ float redf[S::WAVES];
   static_assert(S::NS >= 2 && S::NS <= 4, "2..4 stages");
 
   const int tid = threadIdx.x;
@@ -173,8 +184,10 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   // ---- block -> (grid point, tile row, tile column), XCD-contiguous ----------------
   // GRAM: tile row tm covers k from tm BM on, so a block takes the pair of tile rows tm
   // and tiles_m - 1 - tm (tiles_m + 1 blocks of G' between them): equal work per block.
+  // BUILD: grid point = token split, and a block's tile is the rem-th pair tm <= tn of
+  // the upper block triangle in row-major order.
   const int tm_count = GRAM ? (tiles_m + 1) / 2 : tiles_m;
-  const int per_alpha = tm_count * tiles_n;
+  const int per_alpha = BUILD ? tiles_m * (tiles_m + 1) / 2 : tm_count * tiles_n;
   const int total = nb * per_alpha;
   const int b = blockIdx.x;
   const int xcd = b & 7;
@@ -183,16 +196,32 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   const int logical = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
   const int kk_alpha = logical / per_alpha;
   const int rem = logical - kk_alpha * per_alpha;
-  const int band = rem / (kBandM * tiles_n);
-  const int first_m = band * kBandM;
-  const int band_rows = min(kBandM, tm_count - first_m);
-  const int in_band = rem - band * kBandM * tiles_n;
-  const int tm = first_m + in_band % band_rows;
-  const int tn = in_band / band_rows;
+  int tm, tn;
+  if constexpr (BUILD) {
+    int t = 0, left = rem;
+    while (left >= tiles_m - t) {
+      left -= tiles_m - t;
+      ++t;
+    }
+    tm = t;
+    tn = t + left;
+  } else {
+    const int band = rem / (kBandM * tiles_n);
+    const int first_m = band * kBandM;
+    const int band_rows = min(kBandM, tm_count - first_m);
+    const int in_band = rem - band * kBandM * tiles_n;
+    tm = first_m + in_band % band_rows;
+    tn = in_band / band_rows;
+  }
+  // reduction length KR of this block and row stride LD of both operands
+  const int k_first = BUILD ? kk_alpha * kchunk : 0;
+  const int KR = BUILD ? min(kchunk, N - k_first) : K;
+  const int LD = BUILD ? ld : K;
 
-  const uint16_t* B = GRAM ? dW + (size_t)kk_alpha * M * K + (size_t)tn * BN * K
-                           : X + (size_t)tn * BN * K;
-  const int rows_b = GRAM ? min(BN, M - tn * BN) : min(BN, N - tn * BN);
+  const uint16_t* B = BUILD  ? X + (size_t)tn * BN * LD + k_first
+                      : GRAM ? dW + (size_t)kk_alpha * M * K + (size_t)tn * BN * K
+                             : X + (size_t)tn * BN * K;
+  const int rows_b = BUILD ? min(BN, K - tn * BN) : GRAM ? min(BN, M - tn * BN) : min(BN, N - tn * BN);
 
   // ---- DMA through buffer resources.  Lane l of a wave-level buffer_load ... lds fills
   //      LDS bytes [16 l, 16 l + 16) of a 1 KiB block: row l / CPR of the block,
@@ -207,15 +236,15 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   const int dma_lchunk_even = (lane % S::CPR) ^ S::swz(dma_row_in);
   const int dma_lchunk_odd = (lane % S::CPR) ^ S::swz(dma_row_in + (S::ROWS_PER_DMA == 8 ? 8 : 0));
   int32x4 rsrc_a;  // set per tile row (part) below
-  const int32x4 rsrc_b = make_rsrc(B, (unsigned)rows_b * (unsigned)K * 2u);
+  const int32x4 rsrc_b = make_rsrc(B, (unsigned)rows_b * (unsigned)LD * 2u);
   static_assert(S::DMA_A % 2 == 0 && S::DMA_B % 2 == 0, "block parity follows j");
   const unsigned row_a = (unsigned)(wave * S::DMA_A * S::ROWS_PER_DMA + dma_row_in);
   const unsigned row_b = (unsigned)(wave * S::DMA_B * S::ROWS_PER_DMA + dma_row_in);
-  const unsigned vo_a0 = (row_a * (unsigned)K + dma_lchunk_even * 8) * 2u;
-  const unsigned vo_a1 = (row_a * (unsigned)K + dma_lchunk_odd * 8) * 2u;
-  const unsigned vo_b0 = (row_b * (unsigned)K + dma_lchunk_even * 8) * 2u;
-  const unsigned vo_b1 = (row_b * (unsigned)K + dma_lchunk_odd * 8) * 2u;
-  const unsigned dma_row_stride = (unsigned)S::ROWS_PER_DMA * (unsigned)K * 2u;  // bytes per j
+  const unsigned vo_a0 = (row_a * (unsigned)LD + dma_lchunk_even * 8) * 2u;
+  const unsigned vo_a1 = (row_a * (unsigned)LD + dma_lchunk_odd * 8) * 2u;
+  const unsigned vo_b0 = (row_b * (unsigned)LD + dma_lchunk_even * 8) * 2u;
+  const unsigned vo_b1 = (row_b * (unsigned)LD + dma_lchunk_odd * 8) * 2u;
+  const unsigned dma_row_stride = (unsigned)S::ROWS_PER_DMA * (unsigned)LD * 2u;  // bytes per j
   constexpr unsigned kOutOfRange = 0x80000000u;
 
   auto stage_ptr = [&](auto st) -> uint8_t* {
@@ -229,9 +258,10 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   // LDS byte addresses of the stage buffers (uniform, computed once).
   const unsigned lds_stage[4] = {lds_addr(sm0), lds_addr(sm1), lds_addr(sm2), lds_addr(sm3)};
 
-  // k-tiles rounded up to a multiple of NS: the padding tiles lie past in_features, read
-  // as zeros and add nothing, and the NS-unrolled loop below then has a single exit.
-  const int nk = ((K + S::BK * S::NS - 1) / (S::BK * S::NS)) * S::NS;
+  // k-tiles rounded up to a multiple of NS: the padding tiles lie past the reduction
+  // length, read as zeros and add nothing, and the NS-unrolled loop below then has a
+  // single exit.
+  const int nk = ((KR + S::BK * S::NS - 1) / (S::BK * S::NS)) * S::NS;
   // GRAM: k-tiles kt0 .. nk - 1 (kt0 a multiple of NS since BM / BK is); set per part
   static_assert(!GRAM || (BM / S::BK) % S::NS == 0, "the diagonal block starts on a whole pipeline step");
   int kt0 = 0, nkt = nk;
@@ -242,8 +272,8 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     const int k0 = (i < nkt ? kt0 + i : nk) * S::BK;
     const unsigned la = lds_stage[ST] + (unsigned)(wave * S::DMA_A) * 1024u;
     const unsigned lb = lds_stage[ST] + (unsigned)S::A_BYTES + (unsigned)(wave * S::DMA_B) * 1024u;
-    const bool k_ok0 = k0 + dma_lchunk_even * 8 < K;
-    const bool k_ok1 = k0 + dma_lchunk_odd * 8 < K;
+    const bool k_ok0 = k0 + dma_lchunk_even * 8 < KR;
+    const bool k_ok1 = k0 + dma_lchunk_odd * 8 < KR;
     const unsigned va0 = k_ok0 ? vo_a0 : kOutOfRange, va1 = k_ok1 ? vo_a1 : kOutOfRange;
     const unsigned vb0 = k_ok0 ? vo_b0 : kOutOfRange, vb1 = k_ok1 ? vo_b1 : kOutOfRange;
     const unsigned kbytes = (unsigned)k0 * 2u;
@@ -337,6 +367,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   };
 
   double ssum = 0.0;
+  float gmx = 0.0f;  // BUILD: largest |entry| of the tile
   // One pass per tile row of the block (two for a GRAM pair).  Between passes no barrier
   // is needed: every wave's DMAs of the next pass go to its own LDS blocks after its own
   // vmcnt(0), and other waves have finished their fragment reads of the last real stage
@@ -346,10 +377,11 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   for (int part = 0; part < nparts; ++part) {
   const int tmc = part == 0 ? tm : tiles_m - 1 - tm;
   {
-    const uint16_t* A = GRAM ? X + (size_t)tmc * BM * K
-                             : dW + (size_t)kk_alpha * M * K + (size_t)tmc * BM * K;
-    const int rows_a = GRAM ? min(BM, N - tmc * BM) : min(BM, M - tmc * BM);
-    rsrc_a = make_rsrc(A, (unsigned)rows_a * (unsigned)K * 2u);
+    const uint16_t* A = BUILD  ? X + (size_t)tmc * BM * LD + k_first
+                        : GRAM ? X + (size_t)tmc * BM * K
+                               : dW + (size_t)kk_alpha * M * K + (size_t)tmc * BM * K;
+    const int rows_a = BUILD ? min(BM, K - tmc * BM) : GRAM ? min(BM, N - tmc * BM) : min(BM, M - tmc * BM);
+    rsrc_a = make_rsrc(A, (unsigned)rows_a * (unsigned)LD * 2u);
     if constexpr (GRAM) {
       kt0 = min(tmc * (BM / S::BK), nk);
       nkt = nk - kt0;
@@ -383,9 +415,32 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   __builtin_amdgcn_s_waitcnt(WaitVmLgkm<0>::value);  // no LDS write may outlive the block
 
   // ---- epilogue: sum of squares of the 256 x 256 output tile (GRAM: sum of
-  //      dW (C + dW gdiag) at the output positions); element e of a 32x32 block is row
-  //      8 (e / 4) + 4 (l / 32) + (e mod 4), column l mod 32 ---------------------------
-  if constexpr (GRAM) {
+  //      dW (C + dW gdiag) at the output positions; BUILD: the tile itself); element e
+  //      of a 32x32 block is row 8 (e / 4) + 4 (l / 32) + (e mod 4), column l mod 32 ----
+  if constexpr (BUILD) {
+    // one split: G[a][b] (a row-contiguous 128-byte run per half-wave and e); several:
+    // the tile's partial, row-major within the tile
+    const int pair = rem;
+    float* dst = nb == 1 ? gout : gout + ((size_t)kk_alpha * per_alpha + pair) * (BM * BN);
+    const int ldo = nb == 1 ? K : BN;
+    const int a_base = nb == 1 ? tm * BM : 0, b_base = nb == 1 ? tn * BN : 0;
+#pragma unroll
+    for (int mi = 0; mi < S::MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < S::NI; ++ni) {
+        const int bl = wn * S::NI * 32 + ni * 32 + (lane & 31);
+        const int al0 = wm * S::MI * 32 + mi * 32 + 4 * (lane >> 5);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int al = al0 + 8 * (e >> 2) + (e & 3);
+          if (tm * BM + al < K && tn * BN + bl < K) {
+            const float v = acc[mi][ni][e];
+            dst[(size_t)(a_base + al) * ldo + b_base + bl] = v;
+            gmx = (fabsf(v) > gmx || v != v) ? fabsf(v) : gmx;
+          }
+        }
+      }
+  } else if constexpr (GRAM) {
     // dW_k and gdiag through buffer resources: a lane's piece outside the layer (row past
     // out_features or channel past in_features) takes an offset past the resource's range
     // and reads zeros.  M K < 2^31 and K is a multiple of 32, so dW_k's byte range ends
@@ -449,6 +504,24 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
       }
   }
   }  // part
+  if constexpr (BUILD) {
+    if (nb == 1) {  // the tile's largest |G| (NaN if any entry is NaN)
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float o = __shfl_xor(gmx, off);
+        gmx = (o > gmx || o != o) ? o : gmx;
+      }
+      if (lane == 0) redf[wave] = gmx;
+      __syncthreads();
+      if (tid == 0) {
+        float m = redf[0];
+#pragma unroll
+        for (int w = 1; w < S::WAVES; ++w) m = (redf[w] > m || redf[w] != redf[w]) ? redf[w] : m;
+        tmax[rem] = m;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off);
   if (lane == 0) red[wave] = ssum;
@@ -518,9 +591,9 @@ hipError_t launch_loss_gemm(const uint16_t* dW, const uint16_t* X, int M, int N,
   const int tm = (int)loss_tiles_m(M), tn = (int)loss_tiles_n(N);
   const long long blocks = (long long)nb * tm * tn;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_loss_gemm<LossStage, false>), dim3((unsigned)blocks),
-                     dim3(LossStage::THREADS), 0, stream, dW, X, nullptr, M, N, K, tm, tn, nb,
-                     nullptr, partials);
+  hipLaunchKernelGGL((k_loss_gemm<LossStage, kModeDirect>), dim3((unsigned)blocks),
+                     dim3(LossStage::THREADS), 0, stream, dW, X, nullptr, M, N, K, K, 0, tm, tn,
+                     nb, nullptr, partials, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -534,9 +607,22 @@ hipError_t launch_loss_gemm_gram(const uint16_t* dW, const uint16_t* Gh, const f
   const int tm = (int)loss_tiles_m(K), tn = (int)loss_tiles_n(M);
   const long long blocks = (long long)nb * ((tm + 1) / 2) * tn;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_loss_gemm<LossStage, true>), dim3((unsigned)blocks),
-                     dim3(LossStage::THREADS), 0, stream, dW, Gh, gdiag, M, K, K, tm, tn, nb, gexp,
-                     partials);
+  hipLaunchKernelGGL((k_loss_gemm<LossStage, kModeGramLoss>), dim3((unsigned)blocks),
+                     dim3(LossStage::THREADS), 0, stream, dW, Gh, gdiag, M, K, K, K, 0, tm, tn,
+                     nb, gexp, partials, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_gram_build(const uint16_t* Xt, int N, int ld, int K, int kchunk, int splits,
+                             float* out, float* tmax, hipStream_t stream) {
+  if (K <= 0 || N <= 0 || splits <= 0) return hipSuccess;
+  if (kchunk % 8 != 0 || ld % 8 != 0) return hipErrorInvalidValue;
+  const int T = (int)loss_tiles_m(K);
+  const long long blocks = (long long)splits * T * (T + 1) / 2;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_loss_gemm<LossStage, kModeGramBuild>), dim3((unsigned)blocks),
+                     dim3(LossStage::THREADS), 0, stream, nullptr, Xt, nullptr, 0, N, K, ld,
+                     kchunk, T, T, splits, nullptr, nullptr, out, tmax);
   return hipGetLastError();
 }
 

@@ -9,10 +9,16 @@
 // costs about M K^2 / 2 (the block upper triangle of G below) instead of M K N, which
 // pays once N is about as large as K.
 //
-//   k_gram_full        G's upper triangle in 128 x 128 tiles, every tile over all tokens:
-//                      fp16 products (exact in fp32) summed on the matrix cores in fp32 over
-//                      at most 256 tokens, those sums added in fp64, the total rounded to
-//                      fp32 and written at (a, b) and (b, a); each tile's largest |G|.
+//   k_transpose_x      Xt = X^T (fp16 [K][ld], tokens contiguous, ld = N rounded up to 8,
+//                      the padding tokens zero), so that G = Xt Xt^T is a product of two
+//                      row-contiguous operands like the loss product itself.
+//   k_loss_gemm (G build mode, loss_gemm.hip)
+//                      G's upper block triangle in 256 x 256 tiles on the matrix cores:
+//                      fp16 products (exact in fp32) summed in fp32 over one token split
+//                      of at most kGramSplitTokens tokens (at most 512 accumulator additions of
+//                      32x32x16 products, so within 2^-15 of the sum of |products|).
+//   k_gram_combine     with several splits: each entry the fp64 sum of its split partials
+//                      in split order, rounded to fp32; each quarter tile's largest |G|.
 //   k_gram_full_split  one power of two 2^-ex for the whole matrix (its largest magnitude
 //                      into [2^13, 2^14)) and the operand of the per-grid-point product:
 //                      G' 2^-ex in fp16, where G' is G with its blocks of kLossBN x kLossBN
@@ -24,6 +30,7 @@
 //                      and the diagonal term, which carries most of the sum, is taken in
 //                      fp32 from gdiag = diag(G) 2^-ex (fp32) in the product's epilogue,
 //                      so that only the off-diagonal entries are rounded to fp16.
+//                      Only G's upper block triangle is read.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -35,154 +42,88 @@ namespace awq {
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-constexpr int kGfThreads = 512;  // 8 waves, one 16-row tile row each
-constexpr int kGfSpan = 128;     // channels of a tile side
-#ifndef AWQ_GF_STAGE
-#define AWQ_GF_STAGE 128
-#endif
-constexpr int kGfStage = AWQ_GF_STAGE;  // tokens per LDS stage (32-token k-steps)
-constexpr int kGfOct = kGfStage / 64;   // 8-token octets a wave stages per stage
-constexpr int kGfFlush = 256;           // tokens summed in fp32 before adding into fp64
-constexpr int kGfXtp = kGfStage + 4;    // LDS row of a transposed stage (fp16, 8-byte aligned)
-static_assert(kGfStage == 64 || kGfStage == 128, "64 or 128 tokens a stage");
 constexpr int kGfSplitChunk = 4096;  // entries per block of the split pass
+constexpr int kTrTile = 64;          // tokens and channels of a transpose tile
+constexpr int kCombineRows = 64;     // tile rows per block of the combine pass
 
 __device__ __forceinline__ float nan_maxf(float m, float a) {
   return (a > m || a != a) ? a : m;
 }
 
-// Block b: the b-th pair (sa <= sb) of 128-channel spans in row-major order of the upper
-// triangle.  A stage of kGfStage tokens of both spans is stored transposed in LDS (xa, xb
-// [channel][token]): lane l of wave w loads the channel pair (2 l, 2 l + 1) of the 8-token
-// octets w (and w + 8) of each span and interleaves the halves with v_perm.  The MFMA fragment
-// (16x16x32 f16) of a 16-channel block and a 32-token k-step is then lane (p, q)'s 16 bytes
-// at row 16 block + p, token 32 ks + 8 q; wave w multiplies its tile row w of span a (A)
-// with the 8 tile columns of span b (B).  C element e of a tile is row 4 q + e, column p.
-__global__ __launch_bounds__(kGfThreads) void k_gram_full(const uint16_t* __restrict__ X,
-                                                          int N, int K, int nspan,
-                                                          float* __restrict__ G,
-                                                          float* __restrict__ tmax) {
-  __shared__ __attribute__((aligned(16))) uint16_t xa[kGfSpan * kGfXtp];
-  __shared__ __attribute__((aligned(16))) uint16_t xb[kGfSpan * kGfXtp];
-  __shared__ float wmax[kGfThreads / 64];
-  // (sa, sb) of this block
-  int sa = 0, rem = blockIdx.x;
-  while (rem >= nspan - sa) {
-    rem -= nspan - sa;
-    ++sa;
-  }
-  const int sb = sa + rem;
-  const int ca = sa * kGfSpan, cb = sb * kGfSpan;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q4 = lane >> 4, pl = lane & 15;
-  const bool pa_ok = ca + 2 * lane < K, pb_ok = cb + 2 * lane < K;
-
-  floatx4 acc[8];
-  double acc64[8][4];
+// Block (bx, by): tokens [64 bx, 64 bx + 64) x channels [64 by, 64 by + 64).  Loads are
+// 16-byte runs of 8 channels of one token, stores 16-byte runs of 8 tokens of one channel;
+// the tile passes through LDS with a row pitch of 66 halves (33 banks), so the column
+// reads of the store phase spread over the banks.
+__global__ __launch_bounds__(256) void k_transpose_x(const uint16_t* __restrict__ X, int N,
+                                                     int K, int ld, uint16_t* __restrict__ Xt) {
+  constexpr int P = kTrTile + 2;
+  __shared__ uint16_t t[kTrTile * P];
+  const int t0 = blockIdx.x * kTrTile, c0 = blockIdx.y * kTrTile;
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int tc = 0; tc < 8; ++tc) {
-    acc[tc] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < 2; ++i) {
+    const int u = tid + 256 * i;         // 512 runs: token u / 8, channels 8 (u mod 8) ..
+    const int tr = u >> 3, cc = (u & 7) * 8;
+    const int tok = t0 + tr, ch = c0 + cc;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (tok < N && ch < K) v = *(const uint4*)(X + (size_t)tok * K + ch);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc64[tc][e] = 0.0;
-  }
-
-  // the next stage's token values (octets wave, wave + 8), in flight during the MFMAs
-  uint32_t da[kGfOct][8], db[kGfOct][8];
-  auto load_stage = [&](int t0) {
-#pragma unroll
-    for (int o = 0; o < kGfOct; ++o)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = t0 + 8 * (wave + 8 * o) + e;
-        const size_t row = (size_t)t * K;
-        da[o][e] = (pa_ok && t < N) ? *(const uint32_t*)(X + row + ca + 2 * lane) : 0u;
-        db[o][e] = (pb_ok && t < N) ? *(const uint32_t*)(X + row + cb + 2 * lane) : 0u;
-      }
-  };
-  auto put = [&](uint16_t* xt, const uint32_t (&d)[8], int oct) {
-    uint2 lo0, lo1, hi0, hi1;  // channel 2 l (low halves) and 2 l + 1 (high halves)
-    lo0.x = __builtin_amdgcn_perm(d[1], d[0], 0x05040100u);
-    lo0.y = __builtin_amdgcn_perm(d[3], d[2], 0x05040100u);
-    lo1.x = __builtin_amdgcn_perm(d[5], d[4], 0x05040100u);
-    lo1.y = __builtin_amdgcn_perm(d[7], d[6], 0x05040100u);
-    hi0.x = __builtin_amdgcn_perm(d[1], d[0], 0x07060302u);
-    hi0.y = __builtin_amdgcn_perm(d[3], d[2], 0x07060302u);
-    hi1.x = __builtin_amdgcn_perm(d[5], d[4], 0x07060302u);
-    hi1.y = __builtin_amdgcn_perm(d[7], d[6], 0x07060302u);
-    uint16_t* r0 = xt + (2 * lane) * kGfXtp + 8 * oct;
-    *(uint2*)r0 = lo0;
-    *(uint2*)(r0 + 4) = lo1;
-    *(uint2*)(r0 + kGfXtp) = hi0;
-    *(uint2*)(r0 + kGfXtp + 4) = hi1;
-  };
-  auto frag = [&](const uint16_t* xt, int blk, int ks) {
-    const uint16_t* src = xt + (16 * blk + pl) * kGfXtp + 32 * ks + 8 * q4;
-    const uint2 u0 = *(const uint2*)src, u1 = *(const uint2*)(src + 4);
-    const u32x4 v = {u0.x, u0.y, u1.x, u1.y};
-    return __builtin_bit_cast(half8, v);
-  };
-
-  if (N > 0) load_stage(0);
-  for (int t0 = 0; t0 < N; t0 += kGfStage) {
-#pragma unroll
-    for (int o = 0; o < kGfOct; ++o) {
-      put(xa, da[o], wave + 8 * o);
-      put(xb, db[o], wave + 8 * o);
-    }
-    __syncthreads();
-    if (t0 + kGfStage < N) load_stage(t0 + kGfStage);
-#pragma unroll
-    for (int ks = 0; ks < kGfStage / 32; ++ks) {
-      const half8 fa = frag(xa, wave, ks);
-#pragma unroll
-      for (int tc = 0; tc < 8; ++tc)
-        acc[tc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, frag(xb, tc, ks), acc[tc], 0, 0, 0);
-    }
-    __syncthreads();
-    if ((t0 + kGfStage) % kGfFlush == 0 || t0 + kGfStage >= N) {
-#pragma unroll
-      for (int tc = 0; tc < 8; ++tc) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc64[tc][e] += (double)acc[tc][e];
-        acc[tc] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
+    for (int j = 0; j < 4; ++j) {
+      t[tr * P + cc + 2 * j] = (uint16_t)(w[j] & 0xffffu);
+      t[tr * P + cc + 2 * j + 1] = (uint16_t)(w[j] >> 16);
     }
   }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = tid + 256 * i;         // 512 runs: channel u / 8, tokens 8 (u mod 8) ..
+    const int cr = u >> 3, tt = (u & 7) * 8;
+    const int ch = c0 + cr, tok = t0 + tt;
+    if (ch < K && tok < ld) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)t[(tt + 2 * j) * P + cr] | ((uint32_t)t[(tt + 2 * j + 1) * P + cr] << 16);
+      *(uint4*)(Xt + (size_t)ch * ld + tok) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
 
-  // G[a][b] for a = ca + 16 w + 4 q + e, b = cb + 16 tc + p; the transposed tile as
-  // 16-byte rows G[b][a .. a + 3]
+// Block (quarter q of pair p): rows [64 q, 64 q + 64) of tile pair p = (tm, tn): each entry
+// the fp64 sum over splits of the partial tiles [split][pair][256][256] in split order,
+// rounded to fp32, written to G; the quarter's largest |entry| to tmax[4 p + q].
+__global__ __launch_bounds__(256) void k_gram_combine(const float* __restrict__ part,
+                                                      int splits, int npairs, int T, int K,
+                                                      float* __restrict__ G,
+                                                      float* __restrict__ tmax) {
+  __shared__ float wm[4];
+  const int p = blockIdx.x >> 2, qr = blockIdx.x & 3;
+  int tm = 0, left = p;
+  while (left >= T - tm) {
+    left -= T - tm;
+    ++tm;
+  }
+  const int tn = tm + left;
+  const int tid = threadIdx.x;
+  const int col = tn * kLossBN + tid;
   float mx = 0.0f;
-  const int a0 = ca + 16 * wave + 4 * q4;
-#pragma unroll
-  for (int tc = 0; tc < 8; ++tc) {
-    const int b = cb + 16 * tc + pl;
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = (float)acc64[tc][e];
-      mx = nan_maxf(mx, fabsf(v[e]));
-    }
-    if (b < K) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (a0 + e < K) G[(size_t)(a0 + e) * K + b] = v[e];
-      if (sa != sb && a0 < K) *(float4*)(G + (size_t)b * K + a0) = make_float4(v[0], v[1], v[2], v[3]);
-    }
+  for (int rr = 0; rr < kCombineRows; ++rr) {
+    const int rl = qr * kCombineRows + rr;
+    const int row = tm * kLossBM + rl;
+    if (row >= K || col >= K) continue;
+    double acc = 0.0;
+    for (int sp = 0; sp < splits; ++sp)
+      acc += (double)part[(((size_t)sp * npairs + p) * kLossBM + rl) * kLossBN + tid];
+    const float v = (float)acc;
+    G[(size_t)row * K + col] = v;
+    mx = nan_maxf(mx, fabsf(v));
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = nan_maxf(mx, __shfl_xor(mx, o));
-  if (lane == 0) wmax[wave] = mx;
+  if ((tid & 63) == 0) wm[tid >> 6] = mx;
   __syncthreads();
-  if (tid == 0) {
-    float m = wmax[0];
-#pragma unroll
-    for (int w = 1; w < kGfThreads / 64; ++w) m = nan_maxf(m, wmax[w]);
-    tmax[blockIdx.x] = m;
-  }
+  if (tid == 0) tmax[blockIdx.x] = nan_maxf(nan_maxf(wm[0], wm[1]), nan_maxf(wm[2], wm[3]));
 }
 
 // Block c: entries [c chunk, (c + 1) chunk) of G (K x K).  Every block derives the same
@@ -228,25 +169,41 @@ __global__ __launch_bounds__(256) void k_gram_full_split(const float* __restrict
 
 }  // namespace
 
-int gram_full_tiles(int64_t K) {
-  const int64_t ns = (K + kGfSpan - 1) / kGfSpan;
-  return (int)(ns * (ns + 1) / 2);
+GramPlan gram_plan(int64_t N, int64_t K) {
+  GramPlan g;
+  g.ld = (N + 7) / 8 * 8;
+  g.splits = (N + kGramSplitTokens - 1) / kGramSplitTokens;
+  const int64_t T = loss_tiles_m(K);
+  g.pairs = T * (T + 1) / 2;
+  g.tmax = g.splits > 1 ? 4 * g.pairs : g.pairs;
+  return g;
 }
 
-hipError_t launch_gram_full(const uint16_t* X, int N, int K, float* G, float* tmax,
-                            uint16_t* Gh, float* gdiag, int32_t* gexp, hipStream_t stream) {
+hipError_t launch_gram_full(const uint16_t* X, int N, int K, uint16_t* Xt, float* part,
+                            float* G, float* tmax, uint16_t* Gh, float* gdiag, int32_t* gexp,
+                            hipStream_t stream) {
   if (K <= 0) return hipSuccess;
-  if (K % 2 != 0) return hipErrorInvalidValue;
-  const int nspan = (K + kGfSpan - 1) / kGfSpan;
-  const int ntiles = gram_full_tiles(K);
-  hipLaunchKernelGGL(k_gram_full, dim3(ntiles), dim3(kGfThreads), 0, stream, X, N, K, nspan, G,
-                     tmax);
+  if (K % 8 != 0 || N <= 0) return hipErrorInvalidValue;
+  const GramPlan g = gram_plan(N, K);
+  hipLaunchKernelGGL(k_transpose_x, dim3((unsigned)((g.ld + kTrTile - 1) / kTrTile),
+                                         (unsigned)((K + kTrTile - 1) / kTrTile)),
+                     dim3(256), 0, stream, X, N, K, (int)g.ld, Xt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  e = launch_gram_build(Xt, N, (int)g.ld, K, kGramSplitTokens, (int)g.splits, g.splits > 1 ? part : G,
+                        tmax, stream);
+  if (e != hipSuccess) return e;
+  if (g.splits > 1) {
+    const int T = (int)loss_tiles_m(K);
+    hipLaunchKernelGGL(k_gram_combine, dim3((unsigned)(4 * g.pairs)), dim3(256), 0, stream, part,
+                       (int)g.splits, (int)g.pairs, T, K, G, tmax);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t KK = (int64_t)K * K;
   const int64_t blocks = (KK + kGfSplitChunk - 1) / kGfSplitChunk;
   hipLaunchKernelGGL(k_gram_full_split, dim3((unsigned)blocks), dim3(256), 0, stream, G, K, KK,
-                     tmax, ntiles, Gh, gdiag, gexp);
+                     tmax, (int)g.tmax, Gh, gdiag, gexp);
   return hipGetLastError();
 }
 
