@@ -172,6 +172,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   __shared__ __attribute__((aligned(1024))) uint8_t sm3[S::NS > 3 ? S::BYTES : 16];
   __shared__ double red[S::WAVES];
   __shared__ float redf[S::WAVES];
+  __shared__ __attribute__((aligned(16))) float gds[GRAM ? BM : 4];  // GRAM: the tile's diag(G)
   static_assert(S::NS >= 2 && S::NS <= 4, "2..4 stages");
 
   const int tid = threadIdx.x;
@@ -367,7 +368,8 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   };
 
   double ssum = 0.0;
-  float gmx = 0.0f;  // BUILD: largest |entry| of the tile
+  float gmx = 0.0f;     // BUILD: largest |entry| of the tile
+  float gd_pre = 0.0f;  // GRAM: this thread's entry of the tile's diag(G)
   // One pass per tile row of the block (two for a GRAM pair).  Between passes no barrier
   // is needed: every wave's DMAs of the next pass go to its own LDS blocks after its own
   // vmcnt(0), and other waves have finished their fragment reads of the last real stage
@@ -385,6 +387,9 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     if constexpr (GRAM) {
       kt0 = min(tmc * (BM / S::BK), nk);
       nkt = nk - kt0;
+      // diag(G) of the tile's channels, in flight during the pass (0 past in_features)
+      const int c = tmc * BM + tid;
+      gd_pre = (tid < BM && c < N) ? gdiag[c] : 0.0f;
     }
   }
 #pragma unroll
@@ -441,28 +446,22 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
         }
       }
   } else if constexpr (GRAM) {
-    // dW_k and gdiag through buffer resources: a lane's piece outside the layer (row past
+    // dW_k through a buffer resource: a lane's piece outside the layer (row past
     // out_features or channel past in_features) takes an offset past the resource's range
     // and reads zeros.  M K < 2^31 and K is a multiple of 32, so dW_k's byte range ends
-    // below the out-of-range offset.
+    // below the out-of-range offset.  All of a lane's pieces are requested at once (one
+    // memory latency per tile); the tile's 256 diagonal entries, loaded at the start of the
+    // pass, go through LDS.
     constexpr unsigned kOff = 0xfffffff0u;
     const __amdgpu_buffer_rsrc_t rs_d = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(dW + (size_t)kk_alpha * M * K), (short)0, (int)((unsigned)M * (unsigned)K * 2u),
         0x00020000);
-    const __amdgpu_buffer_rsrc_t rs_g =
-        __builtin_amdgcn_make_buffer_rsrc((void*)gdiag, (short)0, N * 4, 0x00020000);
+    u32x2 dv[S::MI][S::NI][4];
 #pragma unroll
     for (int mi = 0; mi < S::MI; ++mi) {
-      // channels c0 + 8 j + (0..3) of rows r_ni: one 8-byte piece of dW and one 16-byte
-      // piece of gdiag per j (c0 is a multiple of 4 and K of 32, so a piece is either
-      // wholly inside in_features or wholly past it)
+      // channels c0 + 8 j + (0..3) of row r_ni: one 8-byte piece per j (c0 is a multiple
+      // of 4 and K of 32, so a piece is either wholly inside in_features or wholly past it)
       const int c0 = tmc * BM + wm * S::MI * 32 + mi * 32 + 4 * (lane >> 5);
-      floatx4 gd[4];
-      u32x2 dv[S::NI][4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        gd[j] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rs_g, c0 + 8 * j < N ? (c0 + 8 * j) * 4u : kOff, 0, 0));
 #pragma unroll
       for (int ni = 0; ni < S::NI; ++ni) {
         const int r = tn * BN + wn * S::NI * 32 + ni * 32 + (lane & 31);
@@ -471,25 +470,31 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
           const unsigned off = (r < M && c0 + 8 * j < N)
                                    ? ((unsigned)r * (unsigned)K + (unsigned)(c0 + 8 * j)) * 2u
                                    : kOff;
-          dv[ni][j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs_d, off, 0, 0));
+          dv[mi][ni][j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs_d, off, 0, 0));
         }
       }
+    }
+    if (tid < BM) gds[tid] = gd_pre;
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < S::MI; ++mi) {
+      const int cl = wm * S::MI * 32 + mi * 32 + 4 * (lane >> 5);  // channel within the tile
 #pragma unroll
       for (int ni = 0; ni < S::NI; ++ni) {
         float t = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          const floatx4 g4 = *(const floatx4*)(gds + cl + 8 * j);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const unsigned w = dv[ni][j][q >> 1];
+            const unsigned w = dv[mi][ni][j][q >> 1];
             const float d = (float)__builtin_bit_cast(
                 _Float16, (uint16_t)(q & 1 ? w >> 16 : w & 0xffffu));
-            t = fmaf(d, fmaf(d, gd[j][q], acc[mi][ni][4 * j + q]), t);
+            t = fmaf(d, fmaf(d, g4[q], acc[mi][ni][4 * j + q]), t);
           }
         }
         ssum += (double)t;
       }
-      __builtin_amdgcn_sched_barrier(0);  // one block row at a time: low VGPR pressure
     }
   } else {
 #pragma unroll
