@@ -377,7 +377,10 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   // set nobody uses).
   const int nparts = (GRAM && tiles_m - 1 - tm != tm) ? 2 : 1;
   for (int part = 0; part < nparts; ++part) {
-  const int tmc = part == 0 ? tm : tiles_m - 1 - tm;
+  // the short row (tiles_m - 1 - tm) first: after it, every block of a pair set streams
+  // the same k-tile of its dW panel at the same time, so blocks sharing that panel share
+  // its reads in L2
+  const int tmc = (part == 0) == (nparts == 2) ? tiles_m - 1 - tm : tm;
   {
     const uint16_t* A = BUILD  ? X + (size_t)tmc * BM * LD + k_first
                         : GRAM ? X + (size_t)tmc * BM * K
