@@ -367,6 +367,40 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     mma(f1);
   };
 
+  // GRAM: the epilogue's dW pieces of tile row tmc for block rows [m0, m1); the first half
+  // is requested during the row's last loop iteration, so that its latency hides behind
+  // the matrix work, the second at the start of the epilogue.
+  u32x2 dv[S::MI][S::NI][4];
+  auto load_epilogue = [&](int tmc, int m0, int m1) {
+      // dW_k through a buffer resource: a lane's piece outside the layer (row past
+      // out_features or channel past in_features) takes an offset past the resource's range
+      // and reads zeros.  M K < 2^31 and K is a multiple of 32, so dW_k's byte range ends
+      // below the out-of-range offset.  All of a lane's pieces are requested at once (one
+      // memory latency per tile); the tile's 256 diagonal entries, loaded at the start of the
+      // pass, go through LDS.
+      constexpr unsigned kOff = 0xfffffff0u;
+      const __amdgpu_buffer_rsrc_t rs_d = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(dW + (size_t)kk_alpha * M * K), (short)0, (int)((unsigned)M * (unsigned)K * 2u),
+          0x00020000);
+  #pragma unroll
+      for (int mi = m0; mi < m1; ++mi) {
+        // channels c0 + 8 j + (0..3) of row r_ni: one 8-byte piece per j (c0 is a multiple
+        // of 4 and K of 32, so a piece is either wholly inside in_features or wholly past it)
+        const int c0 = tmc * BM + wm * S::MI * 32 + mi * 32 + 4 * (lane >> 5);
+  #pragma unroll
+        for (int ni = 0; ni < S::NI; ++ni) {
+          const int r = tn * BN + wn * S::NI * 32 + ni * 32 + (lane & 31);
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const unsigned off = (r < M && c0 + 8 * j < N)
+                                     ? ((unsigned)r * (unsigned)K + (unsigned)(c0 + 8 * j)) * 2u
+                                     : kOff;
+            dv[mi][ni][j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs_d, off, 0, 0));
+          }
+        }
+      }
+  };
+
   double ssum = 0.0;
   float gmx = 0.0f;     // BUILD: largest |entry| of the tile
   float gd_pre = 0.0f;  // GRAM: this thread's entry of the tile's diag(G)
@@ -415,6 +449,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   if (nk > 0) load_frag(I0{}, 0, f0);
 
   for (int kt = 0; kt < nkt; kt += S::NS) {
+    if (GRAM && kt + S::NS >= nkt) load_epilogue(tmc, 0, S::MI / 2);
     step(I0{}, kt);
     if constexpr (S::NS > 1) step(I1{}, kt + 1);
     if constexpr (S::NS > 2) step(I2{}, kt + 2);
@@ -449,34 +484,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
         }
       }
   } else if constexpr (GRAM) {
-    // dW_k through a buffer resource: a lane's piece outside the layer (row past
-    // out_features or channel past in_features) takes an offset past the resource's range
-    // and reads zeros.  M K < 2^31 and K is a multiple of 32, so dW_k's byte range ends
-    // below the out-of-range offset.  All of a lane's pieces are requested at once (one
-    // memory latency per tile); the tile's 256 diagonal entries, loaded at the start of the
-    // pass, go through LDS.
-    constexpr unsigned kOff = 0xfffffff0u;
-    const __amdgpu_buffer_rsrc_t rs_d = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(dW + (size_t)kk_alpha * M * K), (short)0, (int)((unsigned)M * (unsigned)K * 2u),
-        0x00020000);
-    u32x2 dv[S::MI][S::NI][4];
-#pragma unroll
-    for (int mi = 0; mi < S::MI; ++mi) {
-      // channels c0 + 8 j + (0..3) of row r_ni: one 8-byte piece per j (c0 is a multiple
-      // of 4 and K of 32, so a piece is either wholly inside in_features or wholly past it)
-      const int c0 = tmc * BM + wm * S::MI * 32 + mi * 32 + 4 * (lane >> 5);
-#pragma unroll
-      for (int ni = 0; ni < S::NI; ++ni) {
-        const int r = tn * BN + wn * S::NI * 32 + ni * 32 + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const unsigned off = (r < M && c0 + 8 * j < N)
-                                   ? ((unsigned)r * (unsigned)K + (unsigned)(c0 + 8 * j)) * 2u
-                                   : kOff;
-          dv[mi][ni][j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs_d, off, 0, 0));
-        }
-      }
-    }
+    load_epilogue(tmc, S::MI / 2, S::MI);
     if (tid < BM) gds[tid] = gd_pre;
     __syncthreads();
 #pragma unroll
