@@ -1,13 +1,17 @@
 // Output-error loss of each grid point:  L_k = || dW_k X^T ||_F^2  (fp16 MFMA, fp32
-// accumulation, squared-sum epilogue, fp64 per-tile partials), and the argmin.
+// accumulation, fp64 per-tile partials), and the argmin.  One kernel, three modes:
+//   direct     C = dW_k X^T, each 256 x 256 tile squared and summed in registers;
+//   G loss     the same L_k as sum_r dW_r G dW_r^T with G = X^T X: C = G' dW_k^T over the
+//              block upper triangle of G, epilogue sum dW (C + dW diag(G));
+//   G build    G itself, from X^T, as 256 x 256 tiles of its upper block triangle.
 //
 // Pages: "AWQ" scholia-log notes §1.1 (output error Delta Y = Delta W X) and §4.1
 // (argmin of the squared Frobenius norm over the scale family); ewbang.com GPTQ与AWQ
 // §3 二 (objective ||WX - Q(W s)(X/s)|| with a grid search over alpha in [0, 1]).
 //
 // dW_k is fp16 [M][K] and X is fp16 [N][K]: both operands are K-contiguous, so C = dW X^T
-// is a "TN" product whose tiles stream straight from HBM.  The product itself is never
-// stored: each 256 x 256 tile is squared and summed in registers.
+// is a "TN" product whose tiles stream straight from HBM (so are G' [K][K] and X^T [K][N]
+// in the G modes).  No product is stored except G in the build mode.
 //
 // Design for CDNA4 (gfx950, wave64, 160 KiB LDS per CU, 64-bank LDS):
 //   block = 8 waves (2 x 4), tile 256 dW rows x 256 tokens, wave sub-tile 128 x 64 =
