@@ -110,7 +110,17 @@ def cpu_baseline(layer, alphas, cfg, rows):
     O.quantize_pack(W[:rows], res["s_star"], ocfg)
     t2 = time.perf_counter()
     layer_s = (t1 - t0) + (t2 - t1) * (M / rows)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": 1.0 / layer_s, "unit": "layers/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model, "os_cpu_count": os.cpu_count(),
             "sample": (f"statistics over all {X.shape[0]} tokens, then the 20-alpha search and the "
                        f"pack on rows 0..{rows - 1} of {M}; search+pack time scaled by {M / rows:g} "
                        f"(the loss and the pack are sums/maps over rows); measured "
@@ -317,6 +327,7 @@ def main():
         line["variants"] = time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N)
         line["w4a16"] = time_w4a16(awq, torch, out, res["s"], Xd, cfg, sptr, M, K)
         line["large_layers"] = time_large_layers(awq, torch, alphas, sptr)
+    line["ceilings"] = measure_ceilings(torch, sptr)
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib * (1 << 20) // 2, dtype=torch.float16, device="cuda")
         dst = torch.empty_like(src)
@@ -329,6 +340,41 @@ def main():
         if not args.no_variants:
             line["cpu_oracle_widened"] = cpu_oracle_widened(layer, cfg)
     print(json.dumps(line), flush=True)
+
+
+def measure_ceilings(torch, sptr, reps=20):
+    """This box's practical ceilings, measured after the timed region: a 512 MiB
+    device-to-device copy (read + write bytes over time) and a plain fp16 4096^3 product
+    through torch.matmul (hipBLASLt), both on contiguous operands."""
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(sptr)
+        for _ in range(reps):
+            fn()
+        e1.record(sptr)
+        torch.cuda.synchronize()
+        return e0.elapsed_ms(e1) / reps
+
+    src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src))
+    copy_gbs = 2.0 * src.numel() / (ms * 1e-3) / 1e9
+    del src, dst
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    a = torch.randn((4096, 4096), device="cuda", generator=gen).half()
+    b = torch.randn((4096, 4096), device="cuda", generator=gen).half()
+    c = torch.empty((4096, 4096), device="cuda", dtype=torch.float16)
+    ms = timed(lambda: torch.matmul(a, b, out=c))
+    gemm_tf = 2.0 * 4096 ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_GB/s": copy_gbs, "copy_frac_of_8TBps": copy_gbs / HBM_PEAK_GBS,
+            "torch_matmul_fp16_4096^3_TFLOP/s": gemm_tf,
+            "torch_matmul_frac_of_2.5PF": gemm_tf / MFMA_F16_PEAK_TFLOPS}
 
 
 def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, reps=20):
