@@ -271,15 +271,21 @@ def main():
     # HBM bytes per launch from the committed counter summary, valid only for the kernel
     # source and workload it was measured on (null otherwise).
     traffic = None
+    counters = None  # matrix-core busy fraction and clock from the same summary
     if os.path.exists(args.traffic_summary):
         kv = {}
         with open(args.traffic_summary) as f:
             for ln in f:
-                m = re.match(r"^(kernel_source_sha|workload|hbm_bytes_per_launch): (\S+)\s*$", ln)
+                m = re.match(r"^(kernel_source_sha|workload|hbm_bytes_per_launch|mfma_busy_frac|"
+                             r"shader_clock_ghz): (\S+)\s*$", ln)
                 if m:
                     kv[m.group(1)] = m.group(2)
         if kv.get("workload") == spec.name and kv.get("kernel_source_sha") == _kernel_sha():
             traffic = float(kv["hbm_bytes_per_launch"])
+            if "mfma_busy_frac" in kv:
+                counters = {"mfma_busy_frac": float(kv["mfma_busy_frac"]),
+                            "shader_clock_GHz": float(kv["shader_clock_ghz"]),
+                            "source": os.path.basename(args.traffic_summary)}
 
     line = {
         "metric": "AWQ layers/s at 4096x4096; loss-GEMM TFLOP/s & MFMA util; pack GB/s",
@@ -304,7 +310,8 @@ def main():
                      "unit": "TFLOP/s", "frac": gemm_tflops / MFMA_F16_PEAK_TFLOPS,
                      "traffic": traffic,
                      "kernel": "k_loss_gemm" + ("<G form>" if gram else ""),
-                     "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms},
+                     "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms,
+                     "mfma_counters": counters},
         "kernels": {
             "act_stats": {"ms": stats_ms, "GB/s": stats_bytes / (stats_ms * 1e-3) / 1e9,
                           "frac_hbm": stats_bytes / (stats_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
