@@ -334,6 +334,7 @@ def main():
         line["variants"] = time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N)
         line["w4a16"] = time_w4a16(awq, torch, out, res["s"], Xd, cfg, sptr, M, K)
         line["large_layers"] = time_large_layers(awq, torch, alphas, sptr)
+        line["small_layer"] = time_small_layer(awq, torch, sptr)
     line["ceilings"] = measure_ceilings(torch, sptr)
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib * (1 << 20) // 2, dtype=torch.float16, device="cuda")
@@ -447,6 +448,55 @@ def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, reps=20):
                    "per element; SQ counters show the vector unit 60-65% busy, the matrix "
                    "cores about 30%)"}
     return out
+
+
+def time_small_layer(awq, torch, sptr, reps=50):
+    """The whole path (statistics, 20-alpha search, pack) of the 512 x 512 layer with 256
+    tokens, symmetric 4-bit: launch-bound, so timed both as eager calls and as replays of
+    the same calls captured in one HIP graph."""
+    from synth import CONFIGS, alpha_grid, make_layer
+    spec = CONFIGS["c1"][0]
+    L = make_layer(spec)
+    M, K, N = spec.out_features, spec.in_features, spec.n_tokens
+    cfg = awq.qconfig(spec.w_bit, spec.group_size, spec.zero_point)
+    alphas = alpha_grid(spec.n_alpha)
+    Wd, Xd = torch.from_numpy(L.W).cuda(), torch.from_numpy(L.X).cuda()
+    ws_s = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, len(alphas), 0), dtype=torch.uint8,
+                       device="cuda")
+    ws_a = torch.empty(awq.awq_act_stats_workspace_bytes(N, K), dtype=torch.uint8, device="cuda")
+
+    def layer():
+        return awq.quantize_layer(Wd, Xd, alphas, cfg, search_workspace=ws_s, stats_workspace=ws_a)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = HipEvent(), HipEvent()
+        s = int(torch.cuda.current_stream().cuda_stream)
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_ms(e1) / reps
+
+    eager_ms = timed(layer)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            layer()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer()
+    graph_ms = timed(g.replay)
+    del g
+    return {"workload": f"c1: W {M}x{K}, X {N} tokens, {spec.w_bit}-bit symmetric, group "
+                        f"{spec.group_size}, 20 alphas",
+            "eager_us": eager_ms * 1e3, "eager_layers/s": 1000.0 / eager_ms,
+            "graph_replay_us": graph_ms * 1e3, "graph_layers/s": 1000.0 / graph_ms}
 
 
 def w4a16_bytes(M, K, g, T, with_s):

@@ -23,6 +23,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsFQ = 8;    // rows per block, fake quantisation
+constexpr long long kFqSliceBelow = 256;    // fewer blocks than this: slice the grid points
+constexpr long long kFqSmallTarget = 1024;  // blocks to aim for when slicing
 constexpr int kRowsPack = 8;  // rows per block, packing
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -111,15 +113,20 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant_delta(
   }
   const float top = (float)((1 << w_bit) - 1);
   const float qmax = (float)((1 << (w_bit - 1)) - 1);
+  // grid points [k_begin, k_end) of this block: blockIdx.z slices the grid points when the
+  // layer alone gives fewer blocks than the chip has CUs
+  const int per_z = (nb + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int k_begin = (int)blockIdx.z * per_z;
+  const int k_end = min(nb, k_begin + per_z);
   float4 sn[4];
   auto load_s = [&](int k) {
     const float4* sp = (const float4*)(s_table + (size_t)k * K + col0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) sn[q] = col_ok ? sp[q] : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
   };
-  load_s(0);
+  load_s(k_begin);  // every slice has at least one grid point (see the launcher)
 
-  for (int k = 0; k < nb; ++k) {
+  for (int k = k_begin; k < k_end; ++k) {
     float s[16], is[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant_delta(
       s[4 * q + 2] = sn[q].z;
       s[4 * q + 3] = sn[q].w;
     }
-    if (k + 1 < nb) load_s(k + 1);
+    if (k + 1 < k_end) load_s(k + 1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) is[i] = __builtin_amdgcn_rcpf(s[i]);
 
@@ -275,6 +282,15 @@ hipError_t launch_fake_quant_delta(const uint16_t* W, const float* s_table, int 
   if (M <= 0 || K <= 0 || nb <= 0) return hipSuccess;
   const int chunks = K / 16;
   dim3 grid((chunks + kThreads - 1) / kThreads, (M + kRowsFQ - 1) / kRowsFQ);
+  // a small layer: slice the grid points over blockIdx.z (each slice re-reads its rows of
+  // W), about kFqSmallTarget blocks in all; every slice gets at least one grid point
+  const long long xy = (long long)grid.x * grid.y;
+  if (xy < kFqSliceBelow) {
+    long long nz = (kFqSmallTarget + xy - 1) / xy;
+    if (nz > nb) nz = nb;
+    const long long per = (nb + nz - 1) / nz;
+    grid.z = (unsigned)((nb + per - 1) / per);
+  }
 #define AWQ_FQ(L)                                                                         \
   if (zero_point)                                                                         \
     hipLaunchKernelGGL((k_fake_quant_delta<L, true>), grid, dim3(kThreads), 0, stream, W,  \
