@@ -371,40 +371,6 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     mma(f1);
   };
 
-  // GRAM: the epilogue's dW pieces of tile row tmc for block rows [m0, m1); the first half
-  // is requested during the row's last loop iteration, so that its latency hides behind
-  // the matrix work, the second at the start of the epilogue.
-  u32x2 dv[S::MI][S::NI][4];
-  auto load_epilogue = [&](int tmc, int m0, int m1) {
-      // dW_k through a buffer resource: a lane's piece outside the layer (row past
-      // out_features or channel past in_features) takes an offset past the resource's range
-      // and reads zeros.  M K < 2^31 and K is a multiple of 32, so dW_k's byte range ends
-      // below the out-of-range offset.  All of a lane's pieces are requested at once (one
-      // memory latency per tile); the tile's 256 diagonal entries, loaded at the start of the
-      // pass, go through LDS.
-      constexpr unsigned kOff = 0xfffffff0u;
-      const __amdgpu_buffer_rsrc_t rs_d = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(dW + (size_t)kk_alpha * M * K), (short)0, (int)((unsigned)M * (unsigned)K * 2u),
-          0x00020000);
-  #pragma unroll
-      for (int mi = m0; mi < m1; ++mi) {
-        // channels c0 + 8 j + (0..3) of row r_ni: one 8-byte piece per j (c0 is a multiple
-        // of 4 and K of 32, so a piece is either wholly inside in_features or wholly past it)
-        const int c0 = tmc * BM + wm * S::MI * 32 + mi * 32 + 4 * (lane >> 5);
-  #pragma unroll
-        for (int ni = 0; ni < S::NI; ++ni) {
-          const int r = tn * BN + wn * S::NI * 32 + ni * 32 + (lane & 31);
-  #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const unsigned off = (r < M && c0 + 8 * j < N)
-                                     ? ((unsigned)r * (unsigned)K + (unsigned)(c0 + 8 * j)) * 2u
-                                     : kOff;
-            dv[mi][ni][j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs_d, off, 0, 0));
-          }
-        }
-      }
-  };
-
   double ssum = 0.0;
   float gmx = 0.0f;     // BUILD: largest |entry| of the tile
   float gd_pre = 0.0f;  // GRAM: this thread's entry of the tile's diag(G)
@@ -453,7 +419,6 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   if (nk > 0) load_frag(I0{}, 0, f0);
 
   for (int kt = 0; kt < nkt; kt += S::NS) {
-    if (GRAM && kt + S::NS >= nkt) load_epilogue(tmc, 0, S::MI / 2);
     step(I0{}, kt);
     if constexpr (S::NS > 1) step(I1{}, kt + 1);
     if constexpr (S::NS > 2) step(I2{}, kt + 2);
@@ -488,29 +453,61 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
         }
       }
   } else if constexpr (GRAM) {
-    load_epilogue(tmc, S::MI / 2, S::MI);
+    // The tile's own dW block (its 256 rows x its 256 channels) is staged through the
+    // stage buffers, free now: every wave's DMAs have landed (vmcnt(0) above, then the
+    // barrier), and every fragment read of them finished before the loop's last barrier.
+    // Rows 0..127 go to sm0, 128..255 to sm1, 512 bytes each, the 16-byte chunk q of row r
+    // at chunk position q ^ (r & 31): one wave-DMA moves two whole rows (coalesced), and the
+    // output-layout reads below (32 rows, one chunk column) spread over the banks.  Rows
+    // past out_features lie past the tile's resource and read zeros; chunks past
+    // in_features take the out-of-range offset (K is a multiple of 8, so a chunk is wholly
+    // inside or outside).
+    static_assert(S::NS >= 2 && S::BYTES >= (BM / 2) * BN * 2, "two stage buffers hold the block");
+    static_assert(BM == 256 && BN == 256 && S::WAVES == 8, "epilogue staging geometry");
+    __syncthreads();
+    {
+      // rsrc_b is this tile's rows of dW_k (at most 256 K 2 bytes from row tn BN)
+      const int half = lane >> 5, pos = lane & 31;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = wave * 32 + 2 * i + half;     // row within the tile (wave-uniform pair)
+        const int q = pos ^ (rl & 31);                // logical chunk held at position pos
+        const int c = tmc * BM + 8 * q;
+        const unsigned voff = c < N ? ((unsigned)rl * (unsigned)K + (unsigned)c) * 2u : kOutOfRange;
+        const int rpair = wave * 32 + 2 * i;          // first row of this DMA (uniform)
+        const unsigned lds = (rpair < 128 ? lds_stage[0] + (unsigned)rpair * 512u
+                                          : lds_stage[1] + (unsigned)(rpair - 128) * 512u);
+        dma16(rsrc_b, lds, voff, 0u);
+      }
+    }
     if (tid < BM) gds[tid] = gd_pre;
+    __builtin_amdgcn_s_waitcnt(WaitVmLgkm<0>::value);
     __syncthreads();
 #pragma unroll
     for (int mi = 0; mi < S::MI; ++mi) {
       const int cl = wm * S::MI * 32 + mi * 32 + 4 * (lane >> 5);  // channel within the tile
 #pragma unroll
       for (int ni = 0; ni < S::NI; ++ni) {
+        const int rl = wn * S::NI * 32 + ni * 32 + (lane & 31);   // row within the tile
+        const uint8_t* rowp = (rl < 128 ? sm0 + rl * 512 : sm1 + (rl - 128) * 512);
         float t = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const floatx4 g4 = *(const floatx4*)(gds + cl + 8 * j);
+          const int q = (wm * S::MI * 32 + mi * 32 + 8 * j) / 8;   // logical chunk
+          const u32x2 w2 = *(const u32x2*)(rowp + ((q ^ (rl & 31)) * 16) + 8 * (lane >> 5));
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const unsigned w = dv[mi][ni][j][q >> 1];
+          for (int qq = 0; qq < 4; ++qq) {
+            const unsigned w = w2[qq >> 1];
             const float d = (float)__builtin_bit_cast(
-                _Float16, (uint16_t)(q & 1 ? w >> 16 : w & 0xffffu));
-            t = fmaf(d, fmaf(d, g4[q], acc[mi][ni][4 * j + q]), t);
+                _Float16, (uint16_t)(qq & 1 ? w >> 16 : w & 0xffffu));
+            t = fmaf(d, fmaf(d, g4[qq], acc[mi][ni][4 * j + qq]), t);
           }
         }
         ssum += (double)t;
       }
     }
+    __syncthreads();  // the next tile row's DMAs reuse the stage buffers
   } else {
 #pragma unroll
     for (int mi = 0; mi < S::MI; ++mi)
