@@ -144,14 +144,15 @@ struct Stage {
 };
 
 // MODE kModeDirect: C = dW_k X^T (X fp16 [N][K]) and the tile's sum of squares.
-// MODE kModeGramLoss (GRAM below): C = G' dW_k^T with G' 2^-gexp fp16 [K][K] passed as X (N = K): the A side
-// of the tile is channels (rows of G'), the B side rows of dW_k.  G' is G with its BM x BM
-// blocks above the diagonal doubled, those below it zero and its diagonal zero, so tile
-// row tm needs k from tm BM on only.  The tile's sum over its positions (c, r) of
-// dW_k[r][c] (C[c][r] + dW_k[r][c] gdiag[c]), with gdiag = diag(G) 2^-gexp in fp32, times
-// 2^gexp, is the tile's share of sum_r dW_r G dW_r^T.  With channels on the A side, the
-// four consecutive C rows a lane holds are four consecutive channels of one dW row, so
-// the epilogue reads dW in 8-byte pieces.
+// MODE kModeGramLoss (GRAM below): C = G' dW_k^T with G' 2^-gexp fp16 [K][K] passed as X
+// (N = K): the A side of the tile is channels (rows of G'), the B side rows of dW_k.  G' is
+// G with its BM x BM blocks above the diagonal doubled, those below it zero and its
+// diagonal zero, so tile row tm needs k from tm BM on only.  The tile's sum over its
+// positions (c, r) of dW_k[r][c] (C[c][r] + dW_k[r][c] gdiag[c]), with gdiag = diag(G)
+// 2^-gexp in fp32, times 2^gexp, is the tile's share of sum_r dW_r G dW_r^T.  With channels
+// on the A side, the four consecutive C rows a lane holds are four consecutive channels of
+// one dW row, so the epilogue reads its dW in 8-byte pieces (from the tile's dW block,
+// staged in LDS).
 // MODE kModeGramBuild (BUILD below): G = X^T X itself from Xt = X^T (fp16 [K][ld], tokens
 // contiguous, passed as X): the A and B sides are both channels, the reduction runs over
 // the tokens [s kchunk, min(N, (s + 1) kchunk)) of split s (passed as the grid point), and

@@ -30,7 +30,7 @@
 //                      and the diagonal term, which carries most of the sum, is taken in
 //                      fp32 from gdiag = diag(G) 2^-ex (fp32) in the product's epilogue,
 //                      so that only the off-diagonal entries are rounded to fp16.
-//                      Only G's upper block triangle is read.
+//                      Only G's upper block triangle is read, and only that of G' is written.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -126,9 +126,12 @@ __global__ __launch_bounds__(256) void k_gram_combine(const float* __restrict__ 
   if (tid == 0) tmax[blockIdx.x] = nan_maxf(nan_maxf(wm[0], wm[1]), nan_maxf(wm[2], wm[3]));
 }
 
-// Block c: entries [c chunk, (c + 1) chunk) of G (K x K).  Every block derives the same
-// exponent from all tile maxima (NaN if any entry is NaN: then ex = 0 and the NaN reaches
-// the losses); block 0 publishes it.
+// Block c: entries [c chunk, (c + 1) chunk) of G (K x K), eight consecutive entries of one
+// row a thread (K is a multiple of 8).  Every block derives the same exponent from all tile
+// maxima (NaN if any entry is NaN: then ex = 0 and the NaN reaches the losses); block 0
+// publishes it.  Runs in the blocks below the diagonal are skipped: the product never reads
+// them (a tile row of channels runs over k from its own diagonal block on), so G' there is
+// left unwritten.
 __global__ __launch_bounds__(256) void k_gram_full_split(const float* __restrict__ G, int K,
                                                          int64_t KK,
                                                          const float* __restrict__ tmax,
@@ -152,18 +155,31 @@ __global__ __launch_bounds__(256) void k_gram_full_split(const float* __restrict
   }
   if (blockIdx.x == 0 && tid == 0) gexp[0] = ex;
   const int64_t base = (int64_t)blockIdx.x * kGfSplitChunk;
-  for (int i = tid; i < kGfSplitChunk; i += 256) {
-    const int64_t j = base + i;
-    if (j >= KK) break;
-    const int64_t row = j / K, col = j - (j / K) * K;
-    const int64_t ra = row / kLossBN, cb = col / kLossBN;
-    if (row == col) {
-      gdiag[row] = ldexpf(G[j], -ex);
-      Gh[j] = 0;
-    } else {
-      const float g = cb < ra ? 0.0f : (cb > ra ? 2.0f * G[j] : G[j]);
-      Gh[j] = f2h(ldexpf(g, -ex));
+#pragma unroll
+  for (int run = 0; run < kGfSplitChunk / (256 * 8); ++run) {
+    const int64_t j0 = base + (int64_t)(run * 256 + tid) * 8;
+    if (j0 >= KK) break;
+    const int64_t row = j0 / K, col0 = j0 - (j0 / K) * K;
+    const int64_t ra = row / kLossBN, cb = col0 / kLossBN;
+    if (cb < ra) continue;
+    const float4 g0 = *(const float4*)(G + j0), g1 = *(const float4*)(G + j0 + 4);
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float f = cb > ra ? 2.0f : 1.0f;  // exact
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      uint16_t lo = f2h(ldexpf(f * g[i], -ex)), hi = f2h(ldexpf(f * g[i + 1], -ex));
+      if (col0 + i == row) {
+        gdiag[row] = ldexpf(g[i], -ex);
+        lo = 0;
+      }
+      if (col0 + i + 1 == row) {
+        gdiag[row] = ldexpf(g[i + 1], -ex);
+        hi = 0;
+      }
+      h[i >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
     }
+    *(uint4*)(Gh + j0) = make_uint4(h[0], h[1], h[2], h[3]);
   }
 }
 
