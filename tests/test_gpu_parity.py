@@ -249,8 +249,12 @@ def test_search_rows_additive(K, N):
     assert np.allclose(full, parts, rtol=1e-12, atol=0)
 
 
-def test_search_nonfinite_activations():
-    L = make_layer(small_spec("n", 64, 256, 100))
+@pytest.mark.parametrize("M,N", [(64, 100), (300, 3000)])
+def test_search_nonfinite_activations(M, N):
+    """A NaN activation reaches every loss in either form (in the G form through G's
+    entries and the scale exponent, which is then 0)."""
+    assert awq.awq_loss_form(M, 256, N, 5) == (awq.AWQ_LOSS_DIRECT if N < 256 else awq.AWQ_LOSS_GRAM)
+    L = make_layer(small_spec("n", M, 256, N))
     X = L.X.copy()
     X[5, 17] = np.nan
     cfg = awq.qconfig(4, 128, 1)
@@ -262,6 +266,25 @@ def test_search_nonfinite_activations():
     assert int(host(res["best"])[0]) == -1
     assert np.all(host(res["s"]) == 1.0)
     assert not np.isfinite(host(res["losses"])).any()
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 256, 100), (300, 256, 3000)])
+def test_search_zero_activations(M, K, N):
+    """All-zero activations: every loss is exactly 0 on both sides (G = 0 in the G form,
+    exponent 0), so the first grid point is chosen."""
+    L = make_layer(small_spec("z", M, K, N))
+    X = np.zeros_like(L.X)
+    cfg = awq.qconfig(4, 128, 1)
+    alphas = alpha_grid(5)
+    Xd = dev(X)
+    a = awq.awq_act_stats(Xd)
+    res = awq.awq_search_scales(dev(L.W), Xd, a, alphas, cfg)
+    torch.cuda.synchronize()
+    orc = O.search_scales(L.W, X, host(a), alphas, ocfg(cfg))
+    assert np.all(orc["losses"] == 0.0)
+    assert np.all(host(res["losses"]) == 0.0)
+    assert int(host(res["best"])[0]) == 0 == orc["best"]
+    assert int(host(res["status"])[0]) == awq.AWQ_OK
 
 
 def test_search_empty_rows_and_single_alpha():
