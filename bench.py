@@ -311,7 +311,11 @@ def main():
                      "traffic": traffic,
                      "kernel": "k_loss_gemm" + ("<G form>" if gram else ""),
                      "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms,
-                     "mfma_counters": counters},
+                     "mfma_counters": counters,
+                     # the G form executes M K^2 (1 + 256/K) per alpha instead of 2 M K N: the
+                     # direct product's flops over the Gram pass plus this launch, for scale
+                     "form": "gram" if gram else "direct",
+                     "direct_equivalent_TFLOP/s": direct_flops / ((gemm_ms + gram_ms) * 1e-3) / 1e12},
         "kernels": {
             "act_stats": {"ms": stats_ms, "GB/s": stats_bytes / (stats_ms * 1e-3) / 1e9,
                           "frac_hbm": stats_bytes / (stats_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
