@@ -510,12 +510,12 @@ def w4a16_bytes(M, K, g, T, with_s):
 
 
 def time_large_layers(awq, torch, alphas, sptr, reps=2):
-    """The whole 20-alpha search (statistics excluded) on the three large layer shapes, with
+    """The whole 20-alpha search (statistics excluded) on the four large layer shapes, with
     seeded device-side weights and activations (1% of the channels scaled by 20).  With
     many more tokens than channels the library takes the loss through X^T X; the
     direct-equivalent rate divides the direct form's 2 M K N per alpha by the time."""
-    shapes = [("c3 up", 11008, 4096, 16384, 4, 128, 1), ("c5", 13824, 5120, 32768, 3, 64, 1),
-              ("c4", 28672, 8192, 65536, 4, 128, 1)]
+    shapes = [("c3 up", 11008, 4096, 16384, 4, 128, 1), ("c3 down", 4096, 11008, 16384, 4, 128, 1),
+              ("c5", 13824, 5120, 32768, 3, 64, 1), ("c4", 28672, 8192, 65536, 4, 128, 1)]
     out = {}
     gen = torch.Generator(device="cuda")
     for name, M, K, N, b, g, zp in shapes:
@@ -539,6 +539,8 @@ def time_large_layers(awq, torch, alphas, sptr, reps=2):
         ms = e0.elapsed_ms(e1) / reps
         direct = 2.0 * M * K * N * len(alphas)
         out[name] = {"M": M, "K": K, "N": N, "w_bit": b, "group_size": g, "search_ms": ms,
+                     "form": "gram" if awq.awq_loss_form(M, K, N, len(alphas)) == awq.AWQ_LOSS_GRAM
+                     else "direct",
                      "direct_equivalent_TFLOP/s": direct / (ms * 1e-3) / 1e12}
         del W, X, a, ws
         torch.cuda.empty_cache()
