@@ -62,7 +62,8 @@ namespace awq {
 namespace {
 
 constexpr int BM = kLossBM, BN = kLossBN;
-constexpr int kBandM = 4;  // tile-rows per raster band
+constexpr int kBandM = 4;  // tile-rows per raster band (direct form)
+constexpr int kBandG = 8;  // tile-row pairs per raster band (G form; same-box sweep: 8 over 4 and 2)
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -212,10 +213,11 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     tm = t;
     tn = t + left;
   } else {
-    const int band = rem / (kBandM * tiles_n);
-    const int first_m = band * kBandM;
-    const int band_rows = min(kBandM, tm_count - first_m);
-    const int in_band = rem - band * kBandM * tiles_n;
+    constexpr int BMB = GRAM ? kBandG : kBandM;
+    const int band = rem / (BMB * tiles_n);
+    const int first_m = band * BMB;
+    const int band_rows = min(BMB, tm_count - first_m);
+    const int in_band = rem - band * BMB * tiles_n;
     tm = first_m + in_band % band_rows;
     tn = in_band / band_rows;
   }
