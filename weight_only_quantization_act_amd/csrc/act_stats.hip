@@ -34,7 +34,7 @@ constexpr int kThreads = 256;
 constexpr int kChunkLanes = 64;                     // chunks (8 channels) per block
 constexpr int kTokenLanes = kThreads / kChunkLanes;  // token strides per block
 constexpr int kTargetBlocks = 1024;
-constexpr int kMinTokensPerSplit = 64;
+constexpr int kMinTokensPerSplit = 32;
 constexpr int kMaxSplits = 128;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
