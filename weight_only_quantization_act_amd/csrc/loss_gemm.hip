@@ -32,8 +32,9 @@
 //   in place of rows.  The loss only needs the sum of squares of the output tile, so the
 //   accumulator layout never has to be decoded.
 //   Block-to-tile map: hardware hands block b to XCD (b mod 8); blocks are renumbered so
-//   each XCD walks a contiguous range of tiles, ordered in bands of 4 tile-rows, which
-//   keeps the panels its 32 CUs share resident in that XCD's L2.
+//   each XCD walks a contiguous range of tiles, ordered in bands of 4 tile-rows (8
+//   tile-row pairs in the G form), which keeps the panels its 32 CUs share resident in
+//   that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -41,6 +42,8 @@
 #include "awq_act.h"
 #include "awq_internal.h"
 
+// Stage geometry, overridable for sweeps; the defaults (64 channels per stage, 2 stages,
+// 2 x 4 waves) are the fastest measured on MI355X.
 #ifndef LOSS_BK
 #define LOSS_BK 64
 #endif
@@ -52,9 +55,6 @@
 #endif
 #ifndef LOSS_WN
 #define LOSS_WN 4
-#endif
-#ifndef LOSS_SCHED
-#define LOSS_SCHED 0
 #endif
 
 namespace awq {
@@ -317,19 +317,6 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
 
   floatx16 acc[S::MI][S::NI];
 
-  // Interleave one k-step's MFMAs with the LDS reads of the next step's fragments so
-  // that neither the matrix pipe nor the LDS sees a burst.
-  auto interleave = [&]() {
-#if LOSS_SCHED
-    constexpr int NM = S::MI * S::NI, ND = S::MI + S::NI;
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
-      if (i < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    }
-#endif
-  };
-
   auto mma = [&](const Frag& f) {
 #pragma unroll
     for (int mi = 0; mi < S::MI; ++mi)
@@ -358,14 +345,11 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     for (int ks = 0; ks + 2 < S::KSTEPS; ks += 2) {
       load_frag(st, ks + 1, f1);
       mma(f0);
-      interleave();
-      load_frag(st, ks + 2, f0);
+        load_frag(st, ks + 2, f0);
       mma(f1);
-      interleave();
-    }
+      }
     load_frag(st, S::KSTEPS - 1, f1);
     mma(f0);
-    interleave();
     // stage kt+1 has landed (own DMAs) and this wave's reads of stage kt are done
     __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 2) * S::PER_STAGE>::value);
     __builtin_amdgcn_s_barrier();
