@@ -89,8 +89,9 @@ class HipEvent:
         return float(f.value)
 
 
-def cpu_baseline(layer, alphas, cfg, rows):
-    """Time the oracle (as it stands) on rows [0, rows) of W with the full X."""
+def cpu_baseline(layer, alphas, cfg, rows, repeats=2):
+    """Time the oracle (as it stands) on rows [0, rows) of W with the full X, `repeats`
+    times (the mean is reported)."""
     import numpy as np
     from oracle import awq_oracle as O
     try:
@@ -103,13 +104,16 @@ def cpu_baseline(layer, alphas, cfg, rows):
     W, X = layer.W, layer.X
     M = W.shape[0]
     rows = min(rows, M)
-    t0 = time.perf_counter()
-    a = O.act_stats(X)
-    t1 = time.perf_counter()
-    res = O.search_scales(W[:rows], X, a, alphas, ocfg)
-    O.quantize_pack(W[:rows], res["s_star"], ocfg)
-    t2 = time.perf_counter()
-    layer_s = (t1 - t0) + (t2 - t1) * (M / rows)
+    layer_s, total = 0.0, 0.0
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        a = O.act_stats(X)
+        t1 = time.perf_counter()
+        res = O.search_scales(W[:rows], X, a, alphas, ocfg)
+        O.quantize_pack(W[:rows], res["s_star"], ocfg)
+        t2 = time.perf_counter()
+        layer_s += ((t1 - t0) + (t2 - t1) * (M / rows)) / repeats
+        total += t2 - t0
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -123,8 +127,8 @@ def cpu_baseline(layer, alphas, cfg, rows):
             "cpu_model": cpu_model, "os_cpu_count": os.cpu_count(),
             "sample": (f"statistics over all {X.shape[0]} tokens, then the 20-alpha search and the "
                        f"pack on rows 0..{rows - 1} of {M}; search+pack time scaled by {M / rows:g} "
-                       f"(the loss and the pack are sums/maps over rows); measured "
-                       f"{t2 - t0:.1f} s")}
+                       f"(the loss and the pack are sums/maps over rows); mean of {repeats} "
+                       f"runs, {total:.1f} s in all")}
 
 
 def cpu_oracle_widened(layer, cfg, rows_table=64, rows_clip=8, rows_w4=512):
