@@ -359,7 +359,11 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     // stage kt+1 has landed (own DMAs) and this wave's reads of stage kt are done
     __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 2) * S::PER_STAGE>::value);
     __builtin_amdgcn_s_barrier();
+    // the refill DMAs, too, go out at raised priority (same-box A/B, three rounds: loss
+    // product 1.339 against 1.370 ms)
+    __builtin_amdgcn_s_setprio(1);
     dma_stage(st, kt + S::NS);
+    __builtin_amdgcn_s_setprio(0);
     load_frag(NEXT{}, 0, f0);  // after the last k-tile this reads a slot nobody uses
     mma(f1);
   };
