@@ -261,8 +261,9 @@ def main():
     status = int(res["status"].cpu()[0])
     direct_flops = 2.0 * M * N * K * nA                     # the direct product dW_k X^T
     if gram:
-        # one launch = all alphas; column tile j of 256 channels runs over k >= 256 j
-        gemm_flops = nA * sum(2.0 * M * min(256, K - c0) * (K - c0) for c0 in range(0, K, 256))
+        # one launch = all alphas; each half (128 channels) of a 256-channel column tile runs
+        # over k from its own first channel on (the executed MFMA work)
+        gemm_flops = nA * sum(2.0 * M * min(128, K - c0) * (K - c0) for c0 in range(0, K, 128))
         gram_flops = sum(2.0 * N * min(128, K - c0) * (K - c0) for c0 in range(0, K, 128))
     else:
         gemm_flops, gram_flops = direct_flops, 0.0

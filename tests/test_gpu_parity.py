@@ -151,6 +151,8 @@ SEARCH_CASES = [
     (130, 320, 5000, 3, 32, 0),     # 128-channel Gram spans cut at in_features
     (64, 1024, 8192, 4, 128, 1),
     (100, 96, 3000, 3, 32, 1),      # 96 channels: partial transpose and G tiles
+    (300, 448, 2000, 4, 64, 1),     # last diagonal block of 192 channels: its upper half partial
+    (257, 704, 1500, 3, 32, 0),     # three tile rows, the last one 192 channels
     (200, 256, 20003, 4, 64, 1),    # three token splits of G, the last one ragged
 ]
 

@@ -8,7 +8,9 @@ separately:
     sum_r dW_r G dW_r^T = sum_c (sum_r dW_rc^2) G_cc
                           + sum over tile rows a (channels) of sum_{c in a, r} dW_rc (G' dW^T)_cr
 
-where tile row a only needs the columns of G' from block a on.  This is host logic (numpy,
+where tile row a only needs the columns of G' from block a on.  Inside each diagonal block
+the same structure holds at half size (upper-right half block doubled, lower-left zero), so
+the upper half of a tile row's channels needs the columns from its own half block on.  This is host logic (numpy,
 fp64), independent of the GPU code; the GPU path is compared with the oracle's direct
 definition in the GPU tests.
 """
@@ -52,6 +54,58 @@ def test_g_form_equals_direct(M, K, N, B):
     direct = np.sum((dW @ X.T) ** 2)
     G = X.T @ X
     assert abs(_g_form(dW, G, B) - direct) <= 1e-11 * direct
+
+
+def _g_prime_halves(G, B):
+    """G' with the diagonal blocks restructured at half size: inside each B x B diagonal
+    block, the upper-right (B/2) x (B/2) half block doubled and the lower-left one zero."""
+    K = G.shape[0]
+    Gp = _g_prime(G, B)
+    h = B // 2
+    for a0 in range(0, K, B):
+        p1, q0, q1 = min(K, a0 + h), min(K, a0 + h), min(K, a0 + B)
+        Gp[a0:p1, q0:q1] = 2.0 * G[a0:p1, q0:q1]
+        Gp[q0:q1, a0:p1] = 0.0
+    return Gp
+
+
+def _g_form_halves(dW, G, B):
+    """The G-form loss as the product computes it with half-size diagonal structure: the
+    upper half of a tile row's channels starts at k = its own half block."""
+    K = G.shape[0]
+    Gp = _g_prime_halves(G, B)
+    h = B // 2
+    total = np.sum((dW * dW) @ np.diag(G))
+    for a0 in range(0, K, B):
+        for c0, c1 in ((a0, min(K, a0 + h)), (min(K, a0 + h), min(K, a0 + B))):
+            if c0 >= c1:
+                continue
+            C = Gp[c0:c1, c0:] @ dW[:, c0:].T
+            total += np.sum(dW[:, c0:c1].T * C)
+    return total
+
+
+@pytest.mark.parametrize("M,K,N,B", [(7, 12, 30, 4), (33, 64, 17, 16), (20, 96, 200, 32),
+                                     (5, 40, 3, 16), (64, 256, 300, 256), (50, 300, 400, 256),
+                                     (9, 448, 500, 256), (11, 704, 300, 256)])
+def test_g_form_half_blocks_equal_direct(M, K, N, B):
+    rng = np.random.default_rng(M * 1000 + K + N + 1)
+    dW = rng.standard_normal((M, K))
+    X = rng.standard_normal((N, K)) * np.exp(rng.uniform(-2, 2, K))[None, :]
+    direct = np.sum((dW @ X.T) ** 2)
+    G = X.T @ X
+    assert abs(_g_form_halves(dW, G, B) - direct) <= 1e-11 * direct
+    # the half-block structure is what makes skipping k < c0 exact: with the plain G'
+    # (lower-left half block not zero, upper-right not doubled) the same skip is wrong
+    Gp = _g_prime(G, B)
+    h = B // 2
+    wrong = np.sum((dW * dW) @ np.diag(G))
+    for a0 in range(0, K, B):
+        for c0, c1 in ((a0, min(K, a0 + h)), (min(K, a0 + h), min(K, a0 + B))):
+            if c0 < c1:
+                wrong += np.sum(dW[:, c0:c1].T * (Gp[c0:c1, c0:] @ dW[:, c0:].T))
+    if K > h:
+        assert abs(wrong - direct) > 1e-6 * direct
 
 
 def test_g_form_diagonal_carries_the_independent_part():

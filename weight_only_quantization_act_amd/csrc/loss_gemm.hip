@@ -148,7 +148,9 @@ struct Stage {
 // MODE kModeGramLoss (GRAM below): C = G' dW_k^T with G' 2^-gexp fp16 [K][K] passed as X
 // (N = K): the A side of the tile is channels (rows of G'), the B side rows of dW_k.  G' is
 // G with its BM x BM blocks above the diagonal doubled, those below it zero and its
-// diagonal zero, so tile row tm needs k from tm BM on only.  The tile's sum over its
+// diagonal zero, so tile row tm needs k from tm BM on only; inside each diagonal block the
+// same holds at half size, so the tile's channels BM / 2 .. BM - 1 need k from
+// tm BM + BM / 2 on (their waves skip the first half block).  The tile's sum over its
 // positions (c, r) of dW_k[r][c] (C[c][r] + dW_k[r][c] gdiag[c]), with gdiag = diag(G)
 // 2^-gexp in fp32, times 2^gexp, is the tile's share of sum_r dW_r G dW_r^T.  With channels
 // on the A side, the four consecutive C rows a lane holds are four consecutive channels of
@@ -368,6 +370,24 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     mma(f1);
   };
 
+  // GRAM: a part's first BM / 2 channels of k are the first half of its diagonal block,
+  // where G' is zero for the tile's channels BM / 2 .. BM - 1 (its lower-left half block).
+  // The waves holding those channels (wm == 1) only keep the pipeline going there: the
+  // barrier, their share of the refill DMAs and the next stage's first fragments.
+  static_assert(!GRAM || (S::WM == 2 && (BM / 2) / S::BK == S::NS),
+                "the idle pass is one NS-stage iteration over half a diagonal block");
+  auto step_idle = [&](auto st, int kt) {
+    constexpr int ST = decltype(st)::value;
+    using NEXT = std::integral_constant<int, (ST + 1) % S::NS>;
+    __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 2) * S::PER_STAGE>::value);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_setprio(1);
+    dma_stage(st, kt + S::NS);
+    __builtin_amdgcn_s_setprio(0);
+    load_frag(NEXT{}, 0, f0);
+  };
+  const bool idle_first = GRAM && wm == 1;
+
   double ssum = 0.0;
   float gmx = 0.0f;     // BUILD: largest |entry| of the tile
   float gd_pre = 0.0f;  // GRAM: this thread's entry of the tile's diag(G)
@@ -415,7 +435,17 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   // k-step into f0 as well.
   if (nk > 0) load_frag(I0{}, 0, f0);
 
-  for (int kt = 0; kt < nkt; kt += S::NS) {
+  int kt_begin = 0;
+  if constexpr (GRAM) {
+    if (idle_first && nkt > 0) {  // wave-uniform
+      step_idle(I0{}, 0);
+      if constexpr (S::NS > 1) step_idle(I1{}, 1);
+      if constexpr (S::NS > 2) step_idle(I2{}, 2);
+      if constexpr (S::NS > 3) step_idle(I3{}, 3);
+      kt_begin = S::NS;
+    }
+  }
+  for (int kt = kt_begin; kt < nkt; kt += S::NS) {
     step(I0{}, kt);
     if constexpr (S::NS > 1) step(I1{}, kt + 1);
     if constexpr (S::NS > 2) step(I2{}, kt + 2);

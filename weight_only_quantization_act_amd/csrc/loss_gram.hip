@@ -23,10 +23,13 @@
 //                      into [2^13, 2^14)) and the operand of the per-grid-point product:
 //                      G' 2^-ex in fp16, where G' is G with its blocks of kLossBN x kLossBN
 //                      above the diagonal doubled (exact), those below it zero and its
-//                      diagonal zero.  With d the rows of dW,
+//                      diagonal zero; each diagonal block has the same structure at half
+//                      size (upper-right half block doubled, lower-left zero).  With d the
+//                      rows of dW,
 //                      sum_r d_r G d_r^T = sum over column blocks a of d_a . (G' d)_a
 //                                          + sum_c (sum_r d_rc^2) G_cc,
-//                      the product for column block a only runs over k from block a on,
+//                      the product for column block a only runs over k from block a on
+//                      (its upper half of channels from the half block on),
 //                      and the diagonal term, which carries most of the sum, is taken in
 //                      fp32 from gdiag = diag(G) 2^-ex (fp32) in the product's epilogue,
 //                      so that only the off-diagonal entries are rounded to fp16.
@@ -164,7 +167,11 @@ __global__ __launch_bounds__(256) void k_gram_full_split(const float* __restrict
     if (cb < ra) continue;
     const float4 g0 = *(const float4*)(G + j0), g1 = *(const float4*)(G + j0 + 4);
     const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const float f = cb > ra ? 2.0f : 1.0f;  // exact
+    // inside a diagonal block, the same at half size: its upper-right half block doubled,
+    // its lower-left half zero (so the product's waves holding a tile's upper 128
+    // channels start at the half block's diagonal)
+    const int64_t hr = (row % kLossBN) / (kLossBN / 2), hc = (col0 % kLossBN) / (kLossBN / 2);
+    const float f = (cb > ra || hc > hr) ? 2.0f : (hc < hr ? 0.0f : 1.0f);  // exact
     uint32_t h[4];
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
