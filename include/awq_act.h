@@ -124,8 +124,9 @@ int awq_act_stats_ex(const void* X, int64_t n_tokens, int64_t in_features, int32
  * accumulation, reduced in fp64 in a fixed order (bitwise repeatable run to run).  When
  * the estimated cost favours it (roughly n_tokens >= in_features), the same quantity is
  * taken as sum_r dW_r G dW_r^T with G = X^T X [AWQ-notes §1.1]: G summed on the matrix
- * cores (fp32 over at most 256 tokens, then fp64) and stored fp32; its off-diagonal
- * entries enter an fp16 MFMA product, its diagonal enters in fp32.
+ * cores (fp32 over runs of at most 8192 tokens, the runs added in fp64) and stored fp32;
+ * its off-diagonal entries, scaled by one power of two, enter an fp16 MFMA product, its
+ * diagonal enters in fp32.
  * out_features >= 0, in_features >= 0 (multiple of group_size, at most 4194304),
  * n_tokens >= 1.
  * ---------------------------------------------------------------------------------- */
