@@ -353,9 +353,9 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     for (int ks = 0; ks + 2 < S::KSTEPS; ks += 2) {
       load_frag(st, ks + 1, f1);
       mma(f0);
-        load_frag(st, ks + 2, f0);
+      load_frag(st, ks + 2, f0);
       mma(f1);
-      }
+    }
     load_frag(st, S::KSTEPS - 1, f1);
     mma(f0);
     // stage kt+1 has landed (own DMAs) and this wave's reads of stage kt are done
