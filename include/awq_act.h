@@ -58,9 +58,10 @@ typedef enum awq_status {
   AWQ_E_ALPHA = 4,      /* n_alpha outside [1, AWQ_MAX_ALPHA] or an alpha outside [0,1] */
   AWQ_E_WORKSPACE = 5,  /* workspace NULL or smaller than required                    */
   AWQ_E_DEVICE = 6,     /* a pointer that must be device memory is not                */
-  AWQ_E_ALIGN = 7,      /* a pointer is not aligned as required                       */
-  AWQ_E_HIP = 8,        /* a HIP runtime call or kernel launch failed                 */
-  AWQ_W_NONFINITE = 9   /* device status word only: no alpha gave a finite loss      */
+  AWQ_E_HIP = 7,        /* a HIP runtime call or kernel launch failed                 */
+  AWQ_W_NONFINITE = 8,  /* device status word only: no alpha gave a finite loss      */
+  AWQ_E_ALIGN = 9,      /* a pointer is not aligned as required                       */
+  AWQ_W_SCALE_OVERFLOW = 10 /* device status word only: a stored fp16 step is not finite */
 } awq_status;
 
 #define AWQ_MAX_ALPHA 64
@@ -179,8 +180,9 @@ int awq_threshold_scales(const float* a, int64_t in_features, double percentile,
  * so (W R)(X R)^T = W X^T when W and X are both rotated [AWQ-notes §5.1 (rotation keeps the
  * product and spreads an outlier channel), §5.2 (fast structured rotation)].
  *   A, out fp16 [rows][in] (device, 16-byte aligned; out may equal A); block a power of
- *   two in [2, 512] dividing in; in a multiple of 8.  fp32 butterflies, fp16 (nearest
- *   even) results. */
+ *   two in [2, 512] dividing in; in a multiple of 8.  The butterflies run in fp64, where
+ *   the +-1 sums of fp16 values are exact; the 1/sqrt(block) scaling is the one rounding,
+ *   and each result is the nearest-even fp16 of that. */
 int awq_hadamard_rotate(const void* A, int64_t rows, int64_t in_features, int32_t block,
                         void* out, void* stream);
 
@@ -193,8 +195,12 @@ int awq_hadamard_rotate(const void* A, int64_t rows, int64_t in_features, int32_
  *   chosen ratio is the first smallest finite e (ratio 1 when none is finite)
  *   [AWQ-notes closing note (the practical algorithm may add clipping), §2.3 (Q rounds
  *   and clips), §1.1 (output error = weight error times activations)].
- *   The GPU evaluates e = d^T (X_j^T X_j) d with the group Gram matrices (fp64 sums,
- *   stored fp32) and fp32 quadratic forms.
+ *   The GPU evaluates e = d^T (X_j^T X_j) d through the group Gram matrices: fp16
+ *   products summed on the matrix cores in fp32 over runs of at most 256 tokens, the runs
+ *   added in fp64; each group's matrix (divided by s_a s_b in fp64) is scaled by a power
+ *   of two and stored as fp16 hi + lo.  d is split into fp16 hi + lo the same way, and
+ *   the quadratic form takes three fp16 matrix-core passes (hi.hi, hi.lo, lo.hi) with
+ *   fp32 accumulation.
  *   W fp16 [out][in], X fp16 [n_tokens][in] (16-byte aligned), s fp32 [in] (the chosen
  *   scales, e.g. awq_search_scales' s_out), all device
  *   ratios_host  fp32 [n_ratio], HOST memory, each in (0, 1]; n_ratio in [1, 64]
@@ -275,6 +281,18 @@ int awq_quantize_pack(const void* W, const float* s, int64_t out_features,
                       int64_t in_features, const awq_qconfig* cfg, uint8_t* codes_out,
                       void* scales_out, void* zeros_out, void* stream);
 
+/* awq_quantize_pack (clip == NULL) or awq_quantize_pack_clipped (clip given) with a device
+ * status word: status_out (int32 [1], device) is written AWQ_W_SCALE_OVERFLOW when any
+ * stored fp16 step is not finite, AWQ_OK otherwise.  The pages store the step as FP16
+ * [AWQ-blog §2.1]; a group whose fp32 step is 65520 or more (the nearest-even fp16 of
+ * which is infinity), or not finite, cannot be dequantised from that format.  Codes,
+ * steps and zeros are written exactly as by the unchecked calls (such a step as fp16
+ * infinity).  One extra one-thread launch initialises the word before the pack. */
+int awq_quantize_pack_checked(const void* W, const float* s, const float* clip,
+                              int64_t out_features, int64_t in_features,
+                              const awq_qconfig* cfg, uint8_t* codes_out, void* scales_out,
+                              void* zeros_out, int32_t* status_out, void* stream);
+
 /* ------------------------------------------------------------------------------------
  * Profiling hook (per calling thread, one-shot): the next awq_search_scales call on
  * this thread records `gemm_start`/`gemm_stop` (hipEvent_t) on its stream immediately
@@ -287,6 +305,12 @@ int awq_quantize_pack(const void* W, const float* s, int64_t out_features,
  * ---------------------------------------------------------------------------------- */
 int awq_set_profile_events(void* gemm_start, void* gemm_stop, void* fq_start,
                            void* fq_stop, void* gram_start, void* gram_stop);
+
+/* The same kind of one-shot per-thread hook for the statistics: the next awq_act_stats or
+ * awq_act_stats_ex call on this thread (one that enqueues work) records `pass_start` and
+ * `pass_stop` (hipEvent_t, either may be NULL) on its stream right before and after its
+ * streaming pass over X, the first of its two launches.  Returns AWQ_OK. */
+int awq_set_stats_profile_events(void* pass_start, void* pass_stop);
 
 #ifdef __cplusplus
 }

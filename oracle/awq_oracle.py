@@ -31,7 +31,8 @@ Readings taken where the pages leave a step open (each repeated at its function)
   step in loss  the float32 step (fp16 rounding of the step happens only when packing)
   loss          sum of squares of the output error, via Delta Y = Delta W X
   argmin        over finite losses, first index on ties; none finite -> index -1, s := 1
-  packing       two 4-bit slots per byte, even input channel in the low nibble
+  packing       two 4-bit slots per byte, even input channel in the low nibble; a step
+                that overflows its fp16 storage is reported (stored_step_overflows)
   W4A16 product y = x~ W_dequant^T with x~ = fl16(fl32(x / s)) when s is given, fp64
   clipping      per (row, group) ratio rho multiplies the group's range (hi, lo or max|v|)
                 in float32 before the step; chosen by the group's own output error
@@ -297,7 +298,20 @@ def quantize_pack(W16, s32, cfg: QConfig, clip=None):
     zeros fp16 [M][K/g])."""
     codes, step, zero = (quantize(W16, s32, cfg) if clip is None
                          else quantize(W16, s32, cfg, clip=clip))
-    return pack_nibbles(codes), step.astype(np.float16), zero.astype(np.float16)
+    with np.errstate(over="ignore"):  # a step of 65520 or more becomes fp16 infinity
+        scales = step.astype(np.float16)
+    return pack_nibbles(codes), scales, zero.astype(np.float16)
+
+
+def stored_step_overflows(scales16) -> bool:
+    """Whether a packed layer holds a step that is not finite in its fp16 storage.
+
+    Reading of [AWQ-blog §2.1] (the step is stored as FP16) and §1.2 (the weight is
+    dequantised as code times that scale): a group whose float32 step rounds to fp16
+    infinity (round to nearest even, so every step of 65520 or more, fp16's largest finite
+    value being 65504) cannot be dequantised from the stored format, and the pack reports
+    the layer instead of returning such a step silently."""
+    return not bool(np.all(np.isfinite(np.asarray(scales16, dtype=np.float16))))
 
 
 def run_layer(W16, X16, alphas32, cfg: QConfig):

@@ -470,6 +470,32 @@ def pin_group_metadata_overhead():
 
 
 
+def pin_stored_step_overflow():
+    """The step is stored as FP16 [AWQ-blog §2.1].  IEEE binary16's largest finite value is
+    (2 - 2^-10) 2^15 = 65504 and the next representable magnitude would be 2^16, so round
+    to nearest even sends every value from the midpoint 65520 up to infinity and keeps
+    65519.99... at 65504.  A symmetric 4-bit group whose largest |w s| is 7 x 65520 has a
+    step of exactly 65520 and overflows; one fp16 spacing less in w does not."""
+    with np.errstate(over="ignore"):
+        assert F16(F32(65519.996)) == F16(65504.0) and np.isinf(F16(F32(65520.0)))
+    w = np.zeros((2, 128), F16)
+    w[0, 5] = 57344.0                       # 1792 x 32, exact in fp16
+    w[1, 5] = 57312.0                       # one fp16 spacing (32) lower
+    s = np.ones(128, F32)
+    s[5] = F32(8.0 - 2.0 ** -9)             # 57344 s = 458640 = 7 x 65520 exactly
+    cfg = _cfg(4, 128, 0)
+    codes, step, zero = O.quantize(w, s, cfg)
+    assert step[0, 0] == F32(65520.0) and step[1, 0] < F32(65520.0)
+    _, sc, _ = O.quantize_pack(w, s, cfg)
+    assert np.isinf(sc[0, 0]) and sc[1, 0] == F16(65472.0)   # 65483.4 to the nearest 32
+    assert O.stored_step_overflows(sc) and O.stored_step_overflows(sc[:1])
+    assert not O.stored_step_overflows(sc[1:])
+    assert codes[0, 5] == 15 and codes[1, 5] == 15          # the codes are unaffected
+    ordinary = O.quantize_pack((np.ones((3, 128)) * 0.02).astype(F16), np.ones(128, F32),
+                               _cfg(4, 128, 1))[1]
+    assert not O.stored_step_overflows(ordinary)
+
+
 # ---------------------------------------------------------------- statistic / scale variants
 def pin_max_abs_stat():
     """max |x| per channel over tokens [GPTQ-AWQ §3 二.2]: exact on constructed columns."""

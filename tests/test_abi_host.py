@@ -15,8 +15,11 @@ from weight_only_quantization_act_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "awq_act.h")
 
+# the numbering of the planned boundary (OK .. NONFINITE = 0 .. 8), then the two codes
+# added to it: ALIGN and SCALE_OVERFLOW
 E = {"OK": 0, "NULL": 1, "SHAPE": 2, "CONFIG": 3, "ALPHA": 4, "WORKSPACE": 5, "DEVICE": 6,
-     "ALIGN": 7, "HIP": 8, "NONFINITE": 9}
+     "HIP": 7, "NONFINITE": 8, "ALIGN": 9, "SCALE_OVERFLOW": 10}
+WARNINGS = ("NONFINITE", "SCALE_OVERFLOW")
 
 P = ctypes.c_void_p(0x10000)     # aligned fake device pointer (never dereferenced)
 P_ODD = ctypes.c_void_p(0x10002)  # misaligned
@@ -36,7 +39,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in awq_act.h but not exported"
     assert set(names) == set(_lib._SIGNATURES)
@@ -45,7 +48,7 @@ def test_exports_every_declared_symbol(L):
 def test_status_strings_and_enum(L):
     text = open(HEADER).read()
     for name, val in E.items():
-        key = "AWQ_OK" if name == "OK" else ("AWQ_W_NONFINITE" if name == "NONFINITE" else f"AWQ_E_{name}")
+        key = "AWQ_OK" if name == "OK" else (f"AWQ_W_{name}" if name in WARNINGS else f"AWQ_E_{name}")
         assert re.search(rf"\b{key}\s*=\s*{val}\b", text), key
         s = awq.status_str(val)
         assert s.startswith(key)
@@ -157,6 +160,13 @@ def test_pack_and_fake_quant_validation(L):
     # empty weights are a no-op that succeeds without touching memory
     assert f(P, P, 0, 128, _cfg(), P, P, P, None) == E["OK"]
     assert g(P, P, 8, 0, _cfg(), P, None) == E["OK"]
+    h = L.awq_quantize_pack_checked
+    assert h(P, P, None, 8, 128, _cfg(), P, P, P, None, None) == E["NULL"]   # no status word
+    assert h(None, P, None, 8, 128, _cfg(), P, P, P, P, None) == E["NULL"]
+    assert h(P, P, None, 8, 128, _cfg(4, 48), P, P, P, P, None) == E["CONFIG"]
+    assert h(P, P, None, 8, 96, _cfg(4, 64), P, P, P, P, None) == E["SHAPE"]
+    assert h(P, P, None, 8, 128, _cfg(), P, P, P, ctypes.c_void_p(0x10002), None) == E["ALIGN"]
+    assert h(P, P, ctypes.c_void_p(0x10002), 8, 128, _cfg(), P, P, P, P, None) == E["ALIGN"]
 
 
 def test_loss_form_choice():

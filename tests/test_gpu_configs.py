@@ -25,7 +25,8 @@ from tests.gpu_util import check_search, dev, host, ocfg, requires_gpu, say
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
-CASES = [("c3", 0, 512), ("c3", 1, 512), ("c4", 0, 256), ("c5", 0, 512)]
+# every workload checked on the 512 seeded rows its definition names
+CASES = [("c3", 0, 512), ("c3", 1, 512), ("c4", 0, 512), ("c5", 0, 512)]
 
 
 @pytest.mark.parametrize("cfg_name,layer,rows", CASES, ids=[f"{c}_{l}" for c, l, _ in CASES])

@@ -136,6 +136,126 @@ def test_fake_quant_delta(zp, g, w_bit):
     assert np.all(np.abs(dW - want) <= ulp + 5e-7 * np.abs(W.astype(np.float64)))
 
 
+def _check_delta(dW_gpu, W, s, cfg, where):
+    """dW from the GPU (fp16) against the oracle's fp64 W - Q(W s)/s: within one fp16 ulp
+    of the oracle's value plus the fp32 rounding of w s (2^-23 |w| covers it).  A wrong
+    code moves an element by a whole step / s, far outside this bar."""
+    dW = host(dW_gpu).astype(np.float64)
+    want = O.delta_weight(W, s, ocfg(cfg))
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(dW), fin), where
+    ulp = np.spacing(np.abs(want[fin]).astype(F16)).astype(np.float64)
+    err = np.abs(dW[fin] - want[fin])
+    bad = err > ulp + 5e-7 * np.abs(W.astype(np.float64)[fin])
+    assert not bad.any(), (where, int(bad.sum()), float(err.max()))
+
+
+@pytest.mark.parametrize("w_bit,zp,g", [(4, 0, 128), (4, 1, 128), (3, 1, 64), (2, 0, 32),
+                                        (2, 1, 32), (3, 0, 64), (4, 1, 32), (2, 0, 128)])
+def test_fake_quant_delta_adversarial_groups(w_bit, zp, g):
+    """The search's quantiser (the one awq_fake_quant_delta runs) on the groups built to hit
+    exact rounding ties, a zero step, one-signed groups, fp16's largest value and fp16
+    subnormals, with unit, random and doubled scales."""
+    rng = np.random.default_rng(70 + g + w_bit + zp)
+    say(f"fake-quant adversarial b={w_bit} zp={zp} g={g}")
+    blocks = [_adversarial(g, rng, w_bit) for _ in range(4)]
+    W = np.concatenate(blocks, axis=1).astype(F16)
+    W = np.concatenate([W, W[:, ::-1]], axis=0)
+    K = W.shape[1]
+    cfg = awq.qconfig(w_bit, g, zp)
+    for name, s in (("unit", np.ones(K, F32)), ("random", _rand_scales(rng, K)),
+                    ("x2", np.full(K, 2.0, F32))):
+        dW = awq.awq_fake_quant_delta(dev(W), dev(s), cfg)
+        torch.cuda.synchronize()
+        _check_delta(dW, W, s, cfg, f"adv b{w_bit} zp{zp} g{g} s={name}")
+
+
+@pytest.mark.parametrize("zp", [0, 1])
+def test_tiny_steps_take_exact_division(zp):
+    """Scales near 1e-36 put the scaled weights and their steps below the smallest normal
+    fp32, where the hardware reciprocal is not used: the codes of the pack and the search's
+    dW must still be the oracle's (correctly rounded divisions)."""
+    rng = np.random.default_rng(36 + zp)
+    M, K, g = 24, 512, 128
+    say(f"tiny steps zp={zp}")
+    W = (rng.standard_normal((M, K)) * 0.02).astype(F16)
+    W[3, :g] = _adversarial(g, rng, 4)[0].astype(F16)            # exact ties, scaled down
+    s = np.full(K, 1e-36, F32)
+    s[rng.choice(K, 40, replace=False)] = F32(3e-37)
+    s[K // 2:] = F32(1e-30)                                        # normal steps beside them
+    cfg = awq.qconfig(4, g, zp)
+    codes, scales, zeros = awq.awq_quantize_pack(dev(W), dev(s), cfg)
+    dW = awq.awq_fake_quant_delta(dev(W), dev(s), cfg)
+    torch.cuda.synchronize()
+    check_pack(codes, scales, zeros, W, s, cfg, f"tiny zp{zp}")
+    _check_delta(dW, W, s, cfg, f"tiny zp{zp}")
+
+
+def test_pack_step_overflow_status():
+    """A stored fp16 step that overflows (fp32 step >= 65520) is reported through the status
+    word of the checked pack; the codes, steps (as fp16 infinity) and zeros are still the
+    oracle's, and an ordinary layer reports AWQ_OK."""
+    K, g = 256, 128
+    W = np.zeros((4, K), F16)
+    W[:, 7] = F16(0.5)
+    W[1, 5] = F16(57344.0)
+    W[2, 130] = F16(57312.0)
+    s = np.ones(K, F32)
+    s[5] = s[130] = F32(8.0 - 2.0 ** -9)         # row 1: step 65520 exactly; row 2: below
+    cfg = awq.qconfig(4, g, 0)
+    say("pack step overflow")
+    codes, scales, zeros, st = awq.awq_quantize_pack_checked(dev(W), dev(s), cfg)
+    torch.cuda.synchronize()
+    pk, sc, zr = O.quantize_pack(W, s, ocfg(cfg))
+    assert O.stored_step_overflows(sc)
+    assert int(host(st)[0]) == awq.AWQ_W_SCALE_OVERFLOW
+    assert np.array_equal(host(codes), pk)
+    assert np.array_equal(host(scales).view(np.uint16), sc.view(np.uint16))
+    assert np.array_equal(host(zeros).view(np.uint16), zr.view(np.uint16))
+    ok = np.delete(W, 1, axis=0)
+    _, sc2, _ = O.quantize_pack(ok, s, ocfg(cfg))
+    assert not O.stored_step_overflows(sc2)
+    _, _, _, st2 = awq.awq_quantize_pack_checked(dev(ok), dev(s), cfg)
+    torch.cuda.synchronize()
+    assert int(host(st2)[0]) == awq.AWQ_OK
+    # the clipped form reports through the same word
+    clip = np.ones((4, K // g), F32)
+    _, _, _, st3 = awq.awq_quantize_pack_checked(dev(W), dev(s), cfg, clip=dev(clip))
+    torch.cuda.synchronize()
+    assert int(host(st3)[0]) == awq.AWQ_W_SCALE_OVERFLOW
+    empty = torch.empty((0, K), dtype=torch.float16, device="cuda")
+    _, _, _, st4 = awq.awq_quantize_pack_checked(empty, dev(s), cfg)
+    torch.cuda.synchronize()
+    assert int(host(st4)[0]) == awq.AWQ_OK
+
+
+def test_layer_on_a_side_stream():
+    """quantize_layer on a non-current stream, while the current stream allocates and fills
+    buffers of the same sizes: the outputs and temporaries belong to the side stream, so
+    the results equal those of a run on the current stream."""
+    L = make_layer(small_spec("ss", 700, 512, 900, outlier_count=5))
+    cfg = awq.qconfig(4, 128, 1)
+    alphas = alpha_grid(20)
+    Wd, Xd = dev(L.W), dev(L.X)
+    say("side stream")
+    ref = awq.quantize_layer(Wd, Xd, alphas, cfg)
+    torch.cuda.synchronize()
+    ref = {k: host(v).copy() for k, v in ref.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    res = awq.quantize_layer(Wd, Xd, alphas, cfg, stream=side)
+    need = awq.awq_workspace_bytes(700, 512, 900, cfg, 20, 0)
+    junk = [torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    junk += [torch.full((max(need // 8, 1),), float("nan"), dtype=torch.float64, device="cuda")
+             for _ in range(3)]
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    del junk
+    for k in ("a", "s", "losses", "best", "status", "codes", "scales", "zeros", "pack_status"):
+        got = host(res[k])
+        assert np.array_equal(got.view(np.uint8), ref[k].view(np.uint8)), k
+
+
 # ----------------------------------------------------------------------------- A2-A5 search
 SEARCH_CASES = [
     # M, K, N, w_bit, g, zp

@@ -342,6 +342,32 @@ MUTANTS.update({
 })
 
 
+def _overflow_nan_only(scales16):
+    return bool(np.isnan(np.asarray(scales16, np.float16)).any())
+
+
+def _overflow_strict_fp32(scales16):
+    # compares against fp16's largest finite value as if the step were still fp32
+    return bool((np.asarray(scales16, np.float16).astype(F32) > F32(65504.0)).any() is False)
+
+
+_orig_quantize_pack = O.quantize_pack
+
+
+def _pack_saturating(W16, s32, cfg, clip=None):
+    codes, step, zero = (O.quantize(W16, s32, cfg) if clip is None
+                         else O.quantize(W16, s32, cfg, clip=clip))
+    sat = np.minimum(step, F32(65504.0)).astype(np.float16)
+    return O.pack_nibbles(codes), sat, zero.astype(np.float16)
+
+
+MUTANTS.update({
+    "overflow_sees_only_nan": ("stored_step_overflows", _overflow_nan_only),
+    "overflow_inverted": ("stored_step_overflows", _overflow_strict_fp32),
+    "pack_step_saturates": ("quantize_pack", _pack_saturating),
+})
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]

@@ -7,7 +7,9 @@ the library is missing, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 from typing import Optional, Sequence
 
@@ -17,7 +19,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libawq_act.so")
 
 AWQ_OK = 0
-AWQ_W_NONFINITE = 9
+AWQ_E_HIP = 7
+AWQ_W_NONFINITE = 8
+AWQ_E_ALIGN = 9
+AWQ_W_SCALE_OVERFLOW = 10
 AWQ_MAX_ALPHA = 64
 
 
@@ -49,6 +54,7 @@ _SIGNATURES = {
     "awq_fake_quant_delta": (ctypes.c_int, [_vp, _vp, _i64, _i64, _cfgp, _vp, _vp]),
     "awq_quantize_pack": (ctypes.c_int, [_vp, _vp, _i64, _i64, _cfgp, _vp, _vp, _vp, _vp]),
     "awq_set_profile_events": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
+    "awq_set_stats_profile_events": (ctypes.c_int, [_vp, _vp]),
     "awq_act_stats_ex_workspace_bytes": (_sz, [_i64, _i64, _i32, _i64]),
     "awq_act_stats_ex": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i64, ctypes.c_double, _vp, _vp,
                                         _sz, _vp]),
@@ -65,6 +71,8 @@ _SIGNATURES = {
                                        _vp, _vp, _vp, _sz, _vp]),
     "awq_quantize_pack_clipped": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _cfgp, _vp, _vp, _vp,
                                                  _vp]),
+    "awq_quantize_pack_checked": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _cfgp, _vp, _vp, _vp,
+                                                 _vp, _vp]),
 }
 
 AWQ_STAT_MEAN_ABS, AWQ_STAT_MAX_ABS, AWQ_STAT_RMS_RATIO, AWQ_STAT_EMA_MEAN = 0, 1, 2, 3
@@ -107,6 +115,19 @@ def _stream_ptr(stream=None) -> int:
     return int(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run the wrapper with `stream` (when given) as torch's current stream, so that the
+    outputs and temporary workspaces it allocates belong to the stream the kernels are
+    enqueued on: the caching allocator then never hands a block that those kernels may
+    still use to work on another stream."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            return fn(*args, stream=stream, **kwargs)
+    return wrapper
+
+
 def _dev(t: torch.Tensor, dtype: torch.dtype, name: str, shape=None) -> torch.Tensor:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -141,6 +162,7 @@ def awq_act_stats_ex_workspace_bytes(n_tokens: int, in_features: int, statistic:
                                                       batch_tokens))
 
 
+@_on_stream
 def awq_act_stats(X: torch.Tensor, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """a_i = mean over tokens of |X[t, i]| for X fp16 [N, K]  ->  fp32 [K] (device)."""
@@ -171,6 +193,7 @@ def awq_loss_form(out_features: int, in_features: int, n_tokens: int, n_alpha: i
     return int(lib().awq_loss_form(out_features, in_features, n_tokens, n_alpha))
 
 
+@_on_stream
 def awq_search_scales(W: torch.Tensor, X: torch.Tensor, a: torch.Tensor,
                       alphas: Sequence[float], cfg: awq_qconfig,
                       workspace: Optional[torch.Tensor] = None, alpha_batch: int = 0,
@@ -204,6 +227,7 @@ def awq_search_scales(W: torch.Tensor, X: torch.Tensor, a: torch.Tensor,
     return {"s": s[:K], "losses": losses[:n_alpha], "best": best, "status": status}
 
 
+@_on_stream
 def awq_fake_quant_delta(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig,
                          stream=None) -> torch.Tensor:
     """fp16 W - Q(W diag(s)) diag(s)^-1 for one scale vector."""
@@ -219,6 +243,7 @@ def awq_fake_quant_delta(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig,
     return dW
 
 
+@_on_stream
 def awq_quantize_pack(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig, stream=None):
     """Packed codes uint8 [M, K/2], fp16 scales [M, K/g], fp16 zeros [M, K/g]."""
     _dev(W, torch.float16, "W")
@@ -236,6 +261,36 @@ def awq_quantize_pack(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig, stream
     return codes, scales, zeros
 
 
+@_on_stream
+def awq_quantize_pack_checked(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig,
+                              clip: Optional[torch.Tensor] = None, stream=None):
+    """awq_quantize_pack (or its clipped form) with the device status word: returns codes,
+    scales, zeros and status int32 [1] (AWQ_OK, or AWQ_W_SCALE_OVERFLOW when a stored
+    fp16 step is not finite)."""
+    _dev(W, torch.float16, "W")
+    M, K = W.shape
+    _dev(s, torch.float32, "s", (K,))
+    g = cfg.group_size
+    dev = W.device
+    if clip is not None:
+        _dev(clip, torch.float32, "clip", (M, K // g))
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // g), dtype=torch.float16, device=dev)
+    zeros = torch.empty_like(scales)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    if W.numel() == 0:  # nothing to pack; the call still writes the status word
+        dummy = _ptr(_buf(256, dev))
+        ptrs = (dummy, dummy, None, dummy, dummy, dummy)
+    else:
+        ptrs = (_ptr(W), _ptr(s), _ptr(clip) if clip is not None else None, _ptr(codes),
+                _ptr(scales), _ptr(zeros))
+    pw, ps, pcl, pc, psc, pz = ptrs
+    st = lib().awq_quantize_pack_checked(pw, ps, pcl, M, K, ctypes.byref(cfg), pc, psc, pz,
+                                         _ptr(status), _stream_ptr(stream))
+    _check(st, "awq_quantize_pack_checked")
+    return codes, scales, zeros, status
+
+
 def awq_set_profile_events(gemm_start=None, gemm_stop=None, fq_start=None, fq_stop=None,
                            gram_start=None, gram_stop=None):
     """Arm the one-shot per-thread event hook of the next awq_search_scales call.
@@ -249,17 +304,32 @@ def awq_set_profile_events(gemm_start=None, gemm_stop=None, fq_start=None, fq_st
            "awq_set_profile_events")
 
 
+def awq_set_stats_profile_events(pass_start=None, pass_stop=None):
+    """Arm the one-shot per-thread event hook of the next statistics call (events around
+    its streaming pass over X).  Arguments as for awq_set_profile_events."""
+    def h(e):
+        if e is None:
+            return None
+        return int(e) if isinstance(e, int) else int(e.handle)
+    _check(lib().awq_set_stats_profile_events(h(pass_start), h(pass_stop)),
+           "awq_set_stats_profile_events")
+
+
+@_on_stream
 def quantize_layer(W: torch.Tensor, X: torch.Tensor, alphas: Sequence[float],
                    cfg: awq_qconfig, search_workspace: Optional[torch.Tensor] = None,
                    stats_workspace: Optional[torch.Tensor] = None, stream=None):
-    """The whole per-layer path: statistics -> alpha search -> pack (all on device)."""
+    """The whole per-layer path: statistics -> alpha search -> pack (all on device).
+    The result holds the search's status word ("status": AWQ_OK or AWQ_W_NONFINITE) and
+    the pack's ("pack_status": AWQ_OK or AWQ_W_SCALE_OVERFLOW)."""
     a = awq_act_stats(X, workspace=stats_workspace, stream=stream)
     res = awq_search_scales(W, X, a, alphas, cfg, workspace=search_workspace, stream=stream)
-    codes, scales, zeros = awq_quantize_pack(W, res["s"], cfg, stream=stream)
-    res.update({"a": a, "codes": codes, "scales": scales, "zeros": zeros})
+    codes, scales, zeros, pst = awq_quantize_pack_checked(W, res["s"], cfg, stream=stream)
+    res.update({"a": a, "codes": codes, "scales": scales, "zeros": zeros, "pack_status": pst})
     return res
 
 
+@_on_stream
 def awq_act_stats_ex(X: torch.Tensor, statistic: int, batch_tokens: int = 0, momentum: float = 0.9,
                      stream=None) -> torch.Tensor:
     """Per-channel statistic of X fp16 [N, K] (see AWQ_STAT_*) -> fp32 [K]."""
@@ -274,6 +344,7 @@ def awq_act_stats_ex(X: torch.Tensor, statistic: int, batch_tokens: int = 0, mom
     return a[:K]
 
 
+@_on_stream
 def awq_search_scale_table(W: torch.Tensor, X: torch.Tensor, s_table: torch.Tensor,
                            cfg: awq_qconfig, workspace: Optional[torch.Tensor] = None,
                            stream=None):
@@ -304,6 +375,7 @@ def awq_search_scale_table(W: torch.Tensor, X: torch.Tensor, s_table: torch.Tens
     return {"s": s[:K], "losses": losses[:n], "best": best, "status": status}
 
 
+@_on_stream
 def awq_threshold_scales(a: torch.Tensor, percentile: float, factor: float,
                          stream=None) -> torch.Tensor:
     """s_i = factor where a_i exceeds the percentile threshold, else 1."""
@@ -316,6 +388,7 @@ def awq_threshold_scales(a: torch.Tensor, percentile: float, factor: float,
     return s
 
 
+@_on_stream
 def awq_hadamard_rotate(A: torch.Tensor, block: int, out: Optional[torch.Tensor] = None,
                         stream=None) -> torch.Tensor:
     """Rows of A fp16 [R, K] times blockwise H_block / sqrt(block)."""
@@ -333,6 +406,7 @@ def awq_w4a16_workspace_bytes(n_tokens: int, in_features: int) -> int:
     return int(lib().awq_w4a16_workspace_bytes(n_tokens, in_features))
 
 
+@_on_stream
 def awq_w4a16_matmul(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
                      zeros: torch.Tensor, cfg: awq_qconfig, s: Optional[torch.Tensor] = None,
                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
@@ -379,6 +453,7 @@ def awq_clip_workspace_bytes(out_features: int, in_features: int, n_tokens: int,
                                               ctypes.byref(cfg)))
 
 
+@_on_stream
 def awq_clip_search(W: torch.Tensor, X: torch.Tensor, s: torch.Tensor, ratios: Sequence[float],
                     cfg: awq_qconfig, want_errors: bool = False,
                     workspace: Optional[torch.Tensor] = None, stream=None):
@@ -409,6 +484,7 @@ def awq_clip_search(W: torch.Tensor, X: torch.Tensor, s: torch.Tensor, ratios: S
     return {"clip": clip, "best": best, "errors": errors}
 
 
+@_on_stream
 def awq_quantize_pack_clipped(W: torch.Tensor, s: torch.Tensor, clip: torch.Tensor,
                               cfg: awq_qconfig, stream=None):
     """awq_quantize_pack with per-(row, group) range ratios clip [M, K/g] fp32."""

@@ -228,9 +228,13 @@ StatsPlan stats_plan(int64_t N, int64_t K, int mode, int64_t batch_tokens) {
 template <int MODE>
 static hipError_t launch_stats_mode(const uint16_t* X, int N, int K, const StatsPlan& p,
                                     double momentum, float* a_out, double* partials,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int col_blocks = (K + kChunkLanes * 8 - 1) / (kChunkLanes * 8);
   dim3 grid(col_blocks, p.splits);
+  if (ev0) {
+    const hipError_t e = hipEventRecord(ev0, stream);
+    if (e != hipSuccess) return e;
+  }
   if (K % 8 == 0)
     hipLaunchKernelGGL((k_act_stats_partial<true, MODE>), grid, dim3(kThreads), 0, stream, X, N, K,
                        p.B, p.sub, p.tpb, partials, p.splits);
@@ -239,6 +243,7 @@ static hipError_t launch_stats_mode(const uint16_t* X, int N, int K, const Stats
                        K, p.B, p.sub, p.tpb, partials, p.splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   if constexpr (MODE == kStatEmaMean) {
     hipLaunchKernelGGL(k_act_stats_ema, dim3((K + kThreads - 1) / kThreads), dim3(kThreads), 0,
                        stream, partials, p.n_batches, p.sub, N, p.B, K, momentum, a_out);
@@ -250,17 +255,22 @@ static hipError_t launch_stats_mode(const uint16_t* X, int N, int K, const Stats
 }
 
 hipError_t launch_act_stats(const uint16_t* X, int N, int K, int mode, const StatsPlan& plan,
-                            double momentum, float* a_out, double* partials, hipStream_t stream) {
+                            double momentum, float* a_out, double* partials, hipStream_t stream,
+                            hipEvent_t ev0, hipEvent_t ev1) {
   if (K <= 0) return hipSuccess;
   switch (mode) {
     case kStatMeanAbs:
-      return launch_stats_mode<kStatMeanAbs>(X, N, K, plan, momentum, a_out, partials, stream);
+      return launch_stats_mode<kStatMeanAbs>(X, N, K, plan, momentum, a_out, partials, stream,
+                                             ev0, ev1);
     case kStatMaxAbs:
-      return launch_stats_mode<kStatMaxAbs>(X, N, K, plan, momentum, a_out, partials, stream);
+      return launch_stats_mode<kStatMaxAbs>(X, N, K, plan, momentum, a_out, partials, stream,
+                                            ev0, ev1);
     case kStatRmsRatio:
-      return launch_stats_mode<kStatRmsRatio>(X, N, K, plan, momentum, a_out, partials, stream);
+      return launch_stats_mode<kStatRmsRatio>(X, N, K, plan, momentum, a_out, partials, stream,
+                                              ev0, ev1);
     case kStatEmaMean:
-      return launch_stats_mode<kStatEmaMean>(X, N, K, plan, momentum, a_out, partials, stream);
+      return launch_stats_mode<kStatEmaMean>(X, N, K, plan, momentum, a_out, partials, stream,
+                                             ev0, ev1);
     default:
       return hipErrorInvalidValue;
   }

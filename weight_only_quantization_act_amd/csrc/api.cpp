@@ -109,6 +109,8 @@ struct ProfileHook {
   void* gram_stop = nullptr;
 };
 thread_local ProfileHook g_hook;
+// one-shot events around the statistics' streaming pass (awq_set_stats_profile_events)
+thread_local void* g_stats_ev[2] = {nullptr, nullptr};
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_E_HIP; }
 
@@ -188,9 +190,11 @@ const char* awq_status_str(int status) {
     case AWQ_E_ALPHA: return "AWQ_E_ALPHA: n_alpha or an alpha value out of range";
     case AWQ_E_WORKSPACE: return "AWQ_E_WORKSPACE: workspace missing or too small";
     case AWQ_E_DEVICE: return "AWQ_E_DEVICE: pointer is not HIP device memory";
-    case AWQ_E_ALIGN: return "AWQ_E_ALIGN: pointer not aligned as required";
     case AWQ_E_HIP: return "AWQ_E_HIP: HIP runtime call or kernel launch failed";
     case AWQ_W_NONFINITE: return "AWQ_W_NONFINITE: no grid point gave a finite loss";
+    case AWQ_E_ALIGN: return "AWQ_E_ALIGN: pointer not aligned as required";
+    case AWQ_W_SCALE_OVERFLOW:
+      return "AWQ_W_SCALE_OVERFLOW: a stored fp16 step is not finite (fp32 step >= 65520)";
     default: return "AWQ: unknown status";
   }
 }
@@ -229,9 +233,11 @@ int awq_act_stats_ex(const void* X, int64_t n_tokens, int64_t in_features, int32
   if (in_features == 0) return AWQ_OK;
   if ((st = device_ptr(X)) || (st = device_ptr(a_out)) || (st = device_ptr(workspace))) return st;
   const awq::StatsPlan p = awq::stats_plan(n_tokens, in_features, statistic, batch_tokens);
+  hipEvent_t ev0 = (hipEvent_t)g_stats_ev[0], ev1 = (hipEvent_t)g_stats_ev[1];
+  g_stats_ev[0] = g_stats_ev[1] = nullptr;
   return hip_status(awq::launch_act_stats((const uint16_t*)X, (int)n_tokens, (int)in_features,
                                           statistic, p, momentum, a_out, (double*)workspace,
-                                          (hipStream_t)stream));
+                                          (hipStream_t)stream, ev0, ev1));
 }
 
 int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* a_out,
@@ -425,15 +431,25 @@ int awq_fake_quant_delta(const void* W, const float* s, int64_t out_features,
 namespace {
 int pack_impl(const void* W, const float* s, const float* clip, int64_t out_features,
               int64_t in_features, const awq_qconfig* cfg, uint8_t* codes_out,
-              void* scales_out, void* zeros_out, void* stream) {
+              void* scales_out, void* zeros_out, int32_t* status_out, void* stream) {
   if (!W || !s || !cfg || !codes_out || !scales_out || !zeros_out) return AWQ_E_NULL;
   if (!cfg_valid(cfg)) return AWQ_E_CONFIG;
   int st = weight_shape(out_features, in_features, cfg);
   if (st != AWQ_OK) return st;
   if (!aligned(W, 16) || !aligned(s, 16) || !aligned(codes_out, 4) || !aligned(scales_out, 2) ||
-      !aligned(zeros_out, 2) || (clip && !aligned(clip, 4)))
+      !aligned(zeros_out, 2) || (clip && !aligned(clip, 4)) ||
+      (status_out && !aligned(status_out, 4)))
     return AWQ_E_ALIGN;
-  if (out_features == 0 || in_features == 0) return AWQ_OK;
+  if (status_out && (st = device_ptr(status_out))) return st;
+  if (out_features == 0 || in_features == 0) {
+    // an empty layer stores no step: the status word still reports AWQ_OK
+    if (status_out)
+      return hip_status(awq::launch_quant_pack(nullptr, nullptr, nullptr, 0, 0, cfg->w_bit,
+                                               cfg->group_size, cfg->zero_point, nullptr,
+                                               nullptr, nullptr, status_out,
+                                               (hipStream_t)stream));
+    return AWQ_OK;
+  }
   if ((st = device_ptr(W)) || (st = device_ptr(s)) || (st = device_ptr(codes_out)) ||
       (st = device_ptr(scales_out)) || (st = device_ptr(zeros_out)))
     return st;
@@ -441,7 +457,8 @@ int pack_impl(const void* W, const float* s, const float* clip, int64_t out_feat
   return hip_status(awq::launch_quant_pack((const uint16_t*)W, s, clip, (int)out_features,
                                            (int)in_features, cfg->w_bit, cfg->group_size,
                                            cfg->zero_point, codes_out, (uint16_t*)scales_out,
-                                           (uint16_t*)zeros_out, (hipStream_t)stream));
+                                           (uint16_t*)zeros_out, status_out,
+                                           (hipStream_t)stream));
 }
 }  // namespace
 
@@ -449,7 +466,16 @@ int awq_quantize_pack(const void* W, const float* s, int64_t out_features, int64
                       const awq_qconfig* cfg, uint8_t* codes_out, void* scales_out,
                       void* zeros_out, void* stream) {
   return pack_impl(W, s, nullptr, out_features, in_features, cfg, codes_out, scales_out,
-                   zeros_out, stream);
+                   zeros_out, nullptr, stream);
+}
+
+int awq_quantize_pack_checked(const void* W, const float* s, const float* clip,
+                              int64_t out_features, int64_t in_features,
+                              const awq_qconfig* cfg, uint8_t* codes_out, void* scales_out,
+                              void* zeros_out, int32_t* status_out, void* stream) {
+  if (!status_out) return AWQ_E_NULL;
+  return pack_impl(W, s, clip, out_features, in_features, cfg, codes_out, scales_out,
+                   zeros_out, status_out, stream);
 }
 
 int awq_quantize_pack_clipped(const void* W, const float* s, const float* clip,
@@ -458,7 +484,7 @@ int awq_quantize_pack_clipped(const void* W, const float* s, const float* clip,
                               void* stream) {
   if (!clip) return AWQ_E_NULL;
   return pack_impl(W, s, clip, out_features, in_features, cfg, codes_out, scales_out, zeros_out,
-                   stream);
+                   nullptr, stream);
 }
 
 size_t awq_clip_workspace_bytes(int64_t out_features, int64_t in_features, int64_t n_tokens,
@@ -527,6 +553,12 @@ int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_fe
                                             (int)K, cfg->w_bit, cfg->group_size,
                                             cfg->zero_point, rl, n_ratio, clip_out, best_out,
                                             errors_out, (hipStream_t)stream));
+}
+
+int awq_set_stats_profile_events(void* pass_start, void* pass_stop) {
+  g_stats_ev[0] = pass_start;
+  g_stats_ev[1] = pass_stop;
+  return AWQ_OK;
 }
 
 int awq_set_profile_events(void* gemm_start, void* gemm_stop, void* fq_start, void* fq_stop,

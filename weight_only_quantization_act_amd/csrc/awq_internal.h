@@ -47,8 +47,11 @@ struct StatsPlan {
   int B, n_batches, sub, tpb, splits, nq;
 };
 StatsPlan stats_plan(int64_t N, int64_t K, int mode, int64_t batch_tokens);
+// ev0 / ev1 (nullable) are recorded on the stream right before and after the streaming
+// pass over X (the first of the two launches).
 hipError_t launch_act_stats(const uint16_t* X, int N, int K, int mode, const StatsPlan& plan,
-                            double momentum, float* a_out, double* partials, hipStream_t stream);
+                            double momentum, float* a_out, double* partials, hipStream_t stream,
+                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // ---- scales, fake quantisation, packing ------------------------------------------------
 constexpr int kMaxAlpha = 64;
@@ -69,9 +72,12 @@ hipError_t launch_threshold_scales(const float* a, int K, double percentile, flo
 hipError_t launch_hadamard(const uint16_t* A, int rows, int K, int block, uint16_t* out,
                            hipStream_t stream);
 // clip (nullable, fp32 [M][K/group_size]) shrinks each group's range by its ratio.
+// status (nullable, device int32 [1]): set to AWQ_OK by a one-thread launch first, then
+// AWQ_W_SCALE_OVERFLOW by the pack wherever a stored fp16 step is not finite.
 hipError_t launch_quant_pack(const uint16_t* W, const float* s, const float* clip, int M,
                              int K, int w_bit, int group_size, int zero_point, uint8_t* codes,
-                             uint16_t* scales, uint16_t* zeros, hipStream_t stream);
+                             uint16_t* scales, uint16_t* zeros, int32_t* status,
+                             hipStream_t stream);
 
 // ---- clip search ------------------------------------------------------------------------
 constexpr int kMaxClip = 64;

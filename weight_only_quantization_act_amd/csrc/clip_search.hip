@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kClipThreads) void k_clip_mfma(
       // elements with the correctly rounded division.  The two agree for |v / st| <= 16, and
       // beyond that the clamp gives the same code either way (the argument of the pack's
       // quantiser).  Adding the integer zero after rounding keeps the pack's tie rule.
-      const float inv = __builtin_amdgcn_rcpf(st);
+      const float inv = step_reciprocal(st);
       auto quant_block = [&](int b, bool exact) {
         const float4 sv = *(const float4*)&ss[16 * b + 4 * q4];
         const float s4[4] = {sv.x, sv.y, sv.z, sv.w};

@@ -12,6 +12,7 @@
 // and a group of g channels is g/16 (g/8) consecutive lanes.
 #include <hip/hip_runtime.h>
 
+#include "awq_act.h"
 #include "awq_internal.h"
 #include "quantizer.h"
 
@@ -180,9 +181,12 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant_delta(
         chi = qmax;
         need = false;
       }
+      // a step below the smallest normal fp32 (or NaN) takes the divisions: the NaN-dropping
+      // maximum below would not see the non-finite quotients of an infinite reciprocal
+      need |= !(st >= kMinNormal);
       const float inv = __builtin_amdgcn_rcpf(st);
       float cz[16];
-      float dist = 0.0f;  // the largest |t - rint t| of the row (a NaN one leaves the errors NaN)
+      float dist = 0.0f;  // the largest |t - rint t| of the row
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const float t0 = v[i] * inv, t1 = v[i + 1] * inv;
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_pack(
     const uint16_t* __restrict__ W, const float* __restrict__ s_in,
     const float* __restrict__ clip, int M, int K, int w_bit, int zero_point,
     uint8_t* __restrict__ codes_out, uint16_t* __restrict__ scales,
-    uint16_t* __restrict__ zeros) {
+    uint16_t* __restrict__ zeros, int32_t* __restrict__ status) {
   const int chunk = blockIdx.x * kThreads + threadIdx.x;
   const int col0 = chunk * 8;
   const bool col_ok = col0 < K;
@@ -261,12 +265,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_pack(
       for (int i = 0; i < 8; ++i) packed |= ((uint32_t)code[i] & 0xfu) << (4 * i);
       *(uint32_t*)(codes_out + (size_t)row * (K / 2) + col0 / 2) = packed;
       if (leader) {
-        scales[(size_t)row * G + group] = f2h(st);
+        const uint16_t sh = f2h(st);
+        scales[(size_t)row * G + group] = sh;
         zeros[(size_t)row * G + group] = f2h(z);
+        // every writer stores the same value, after the one-thread initialisation that
+        // precedes this launch on the stream
+        if (status != nullptr && (sh & 0x7c00u) == 0x7c00u) status[0] = AWQ_W_SCALE_OVERFLOW;
       }
     }
   }
 }
+
+__global__ void k_status_init(int32_t* __restrict__ status) { status[0] = AWQ_OK; }
 
 }  // namespace
 
@@ -312,22 +322,28 @@ hipError_t launch_fake_quant_delta(const uint16_t* W, const float* s_table, int 
 
 hipError_t launch_quant_pack(const uint16_t* W, const float* s, const float* clip, int M,
                              int K, int w_bit, int group_size, int zero_point, uint8_t* codes,
-                             uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
+                             uint16_t* scales, uint16_t* zeros, int32_t* status,
+                             hipStream_t stream) {
+  if (status) {
+    hipLaunchKernelGGL(k_status_init, dim3(1), dim3(1), 0, stream, status);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (M <= 0 || K <= 0) return hipSuccess;
   const int chunks = K / 8;
   dim3 grid((chunks + kThreads - 1) / kThreads, (M + kRowsPack - 1) / kRowsPack);
   switch (group_size) {
     case 32:
       hipLaunchKernelGGL(k_quant_pack<4>, grid, dim3(kThreads), 0, stream, W, s, clip, M, K, w_bit,
-                         zero_point, codes, scales, zeros);
+                         zero_point, codes, scales, zeros, status);
       break;
     case 64:
       hipLaunchKernelGGL(k_quant_pack<8>, grid, dim3(kThreads), 0, stream, W, s, clip, M, K, w_bit,
-                         zero_point, codes, scales, zeros);
+                         zero_point, codes, scales, zeros, status);
       break;
     case 128:
       hipLaunchKernelGGL(k_quant_pack<16>, grid, dim3(kThreads), 0, stream, W, s, clip, M, K, w_bit,
-                         zero_point, codes, scales, zeros);
+                         zero_point, codes, scales, zeros, status);
       break;
     default:
       return hipErrorInvalidValue;

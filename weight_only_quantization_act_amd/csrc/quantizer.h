@@ -65,13 +65,23 @@ __device__ __forceinline__ float group_min(float x) {
 }
 
 // rint(fl(v / st)) computed as rint(fl(v * inv)) with inv the hardware reciprocal of st
-// (relative error <= 2^-23), except near a half-integer.  With |v / st| <= 16 (true for
-// every element of a group and for -min / st), fl(v * inv) is within 16 * 3 * 2^-24 and
-// fl(v / st) within 16 * 2^-24 of the exact quotient, so the two are at most 2^-18 apart
-// and round to the same integer unless the product lies within 2^-18 of a half-integer.
-// r = |t - rint(t)| and r - 0.5 are exact (Sterbenz), so the test is exact; lanes inside
-// the band (about 1 in 10^5) and any non-finite case take the correctly rounded division.
+// (relative error <= 2^-23 for a normal st), except near a half-integer.  Only quotients
+// with |v / st| <= 2^b can decide a code: every larger one (possible for a clipped group,
+// whose range is shrunk before the step is taken) is clamped to the same end code
+// whichever integer it rounds to, as is -min / st for the zero.  For |v / st| <= 16,
+// fl(v * inv) is within 16 * 3 * 2^-24 and fl(v / st) within 16 * 2^-24 of the exact
+// quotient, so the two are at most 2^-18 apart and round to the same integer unless the
+// product lies within 2^-18 of a half-integer.  r = |t - rint(t)| and r - 0.5 are exact
+// (Sterbenz), so the test is exact; lanes inside the band (about 1 in 10^5) and any
+// non-finite case take the correctly rounded division.  A step below the smallest normal
+// fp32 (where the reciprocal's error bound is not claimed) uses inv = +inf, which makes
+// every quotient non-finite and so takes the division too.
 constexpr float kTieBand = 7.62939453125e-06f;  // 2^-17, twice the bound above
+constexpr float kMinNormal = 1.17549435e-38f;   // 2^-126
+
+__device__ __forceinline__ float step_reciprocal(float st) {
+  return st >= kMinNormal ? __builtin_amdgcn_rcpf(st) : __builtin_inff();
+}
 
 __device__ __forceinline__ bool near_half(float t, float q) {
   return !(fabsf(fabsf(t - q) - 0.5f) > kTieBand);
@@ -117,7 +127,7 @@ __device__ __forceinline__ void quantize8(const float (&v)[8], int w_bit, bool z
     const float top = (float)((1 << w_bit) - 1);
     float st = (hi - lo) / top;
     if (st == 0.0f) st = 1.0f;
-    const float inv = __builtin_amdgcn_rcpf(st);
+    const float inv = step_reciprocal(st);
     const float tz = -lo * inv;
     float z = rintf(tz);
     if (near_half(tz, z)) z = rintf(-lo / st);
@@ -137,7 +147,7 @@ __device__ __forceinline__ void quantize8(const float (&v)[8], int w_bit, bool z
     const float off = (float)(1 << (w_bit - 1));
     float st = m / qmax;
     if (st == 0.0f) st = 1.0f;
-    const float inv = __builtin_amdgcn_rcpf(st);
+    const float inv = step_reciprocal(st);
     float q[8];
     round_quotients(v, st, inv, q);
 #pragma unroll
