@@ -215,6 +215,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev["st0"].record(sptr)
+            awq.awq_set_stats_profile_events(ev["sk0"], ev["sk1"])
         a = awq.awq_act_stats(Xd, workspace=ws_stats)
         if ev is not None:
             ev["st1"].record(sptr)
@@ -244,7 +245,7 @@ def main():
     total_ms = t_start.elapsed_ms(t_end)
     ms_per_step = total_ms / args.steps
 
-    names = ("st0", "st1", "g0", "g1", "f0", "f1", "r0", "r1", "p0", "p1")
+    names = ("st0", "st1", "sk0", "sk1", "g0", "g1", "f0", "f1", "r0", "r1", "p0", "p1")
     evs = [{n: HipEvent() for n in names} for _ in range(args.steps)]
     for i in range(args.steps):
         res, out = step(evs[i])
@@ -256,22 +257,25 @@ def main():
     gram = awq.awq_loss_form(M, K, N, nA) == awq.AWQ_LOSS_GRAM
     gemm_ms, fq_ms = avg("g0", "g1"), avg("f0", "f1")
     stats_ms, pack_ms = avg("st0", "st1"), avg("p0", "p1")
+    stats_pass_ms = avg("sk0", "sk1")
     gram_ms = avg("r0", "r1") if gram else 0.0
 
     status = int(res["status"].cpu()[0])
     direct_flops = 2.0 * M * N * K * nA                     # the direct product dW_k X^T
-    if gram:
-        # one launch = all alphas; each half (128 channels) of a 256-channel column tile runs
-        # over k from its own first channel on (the executed MFMA work)
-        gemm_flops = nA * sum(2.0 * M * min(128, K - c0) * (K - c0) for c0 in range(0, K, 128))
-        gram_flops = sum(2.0 * N * min(128, K - c0) * (K - c0) for c0 in range(0, K, 128))
-    else:
-        gemm_flops, gram_flops = direct_flops, 0.0
+    gemm_flops = loss_product_flops(M, K, N, nA, gram)
+    gram_flops = gram_build_flops(N, K) if gram else 0.0
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
     g = spec.group_size
     stats_bytes = 2.0 * N * K + 4.0 * K
     fq_bytes = 2.0 * M * K + 4.0 * K * nA + 2.0 * M * K * nA
     pack_bytes = 2.0 * M * K + 4.0 * K + M * K / 2 + 4.0 * M * K / g
+    ceilings = measure_ceilings(torch, sptr)
+    copy_gbs = ceilings["copy_GB/s"]
+
+    def hbm(nbytes, ms, what):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"ms": ms, "bytes": nbytes, "GB/s": gbs, "frac_hbm_8TBps": gbs / HBM_PEAK_GBS,
+                "frac_copy_ceiling": gbs / copy_gbs, "timed": what}
 
     # HBM bytes per launch from the committed counter summary, valid only for the kernel
     # source and workload it was measured on (null otherwise).
@@ -317,34 +321,34 @@ def main():
                      "kernel": "k_loss_gemm" + ("<G form>" if gram else ""),
                      "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms,
                      "mfma_counters": counters,
-                     # the G form executes M K^2 (1 + 256/K) per alpha instead of 2 M K N: the
-                     # direct product's flops over the Gram pass plus this launch, for scale
                      "form": "gram" if gram else "direct",
-                     "direct_equivalent_TFLOP/s": direct_flops / ((gemm_ms + gram_ms) * 1e-3) / 1e12},
+                     # the G form executes M K^2 (1 + 128/K) per alpha where the direct product
+                     # would take 2 M K N: the ratio of the two is work saved, not a rate
+                     "direct_over_executed_flops": direct_flops / (gemm_flops + gram_flops)},
         "kernels": {
-            "act_stats": {"ms": stats_ms, "GB/s": stats_bytes / (stats_ms * 1e-3) / 1e9,
-                          "frac_hbm": stats_bytes / (stats_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-            "fake_quant": {"ms": fq_ms, "GB/s": fq_bytes / (fq_ms * 1e-3) / 1e9,
-                           "frac_hbm": fq_bytes / (fq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "act_stats": {**hbm(stats_bytes, stats_pass_ms, "streaming pass (first of the two "
+                                                             "launches), library events"),
+                          "call_ms": stats_ms},
+            "fake_quant": hbm(fq_bytes, fq_ms, "one launch, library events"),
             "loss_gemm": {"ms": gemm_ms, "TFLOP/s": gemm_tflops,
                           "frac_mfma": gemm_tflops / MFMA_F16_PEAK_TFLOPS,
-                          "form": "gram" if gram else "direct",
-                          "direct_equivalent_TFLOP/s":
-                              direct_flops / ((gemm_ms + gram_ms) * 1e-3) / 1e12},
-            **({"gram": {"ms": gram_ms, "TFLOP/s": gram_flops / (gram_ms * 1e-3) / 1e12,
+                          "form": "gram" if gram else "direct"},
+            **({"gram": {"ms": gram_ms, "build_flops": gram_flops,
+                         "TFLOP/s": gram_flops / (gram_ms * 1e-3) / 1e12,
                          "frac_mfma": gram_flops / (gram_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                         "kernels": "k_transpose_x + k_loss_gemm<G build> + k_gram_full_split"}} if gram else {}),
-            "quant_pack": {"ms": pack_ms, "GB/s": pack_bytes / (pack_ms * 1e-3) / 1e9,
-                           "frac_hbm": pack_bytes / (pack_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                         "timed": "the whole Gram pass (transpose, build, combine, split) "
+                                  "against the build's executed flops"}} if gram else {}),
+            "quant_pack": hbm(pack_bytes, pack_ms, "one launch, events around the call"),
         },
         "search_status": status,
     }
     if not args.no_variants:
-        line["variants"] = time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N)
-        line["w4a16"] = time_w4a16(awq, torch, out, res["s"], Xd, cfg, sptr, M, K)
-        line["large_layers"] = time_large_layers(awq, torch, alphas, sptr)
+        line["variants"] = time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, copy_gbs)
+        line["w4a16"] = time_w4a16(awq, torch, out, res["s"], Xd, cfg, sptr, M, K, copy_gbs)
+        line["large_layers"] = time_large_layers(awq, torch, alphas, sptr, copy_gbs)
         line["small_layer"] = time_small_layer(awq, torch, sptr)
-    line["ceilings"] = measure_ceilings(torch, sptr)
+    line["ceilings"] = ceilings
+    line["size_floor"] = measure_size_floor(torch, Xd, Wd, sptr, copy_gbs)
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib * (1 << 20) // 2, dtype=torch.float16, device="cuda")
         dst = torch.empty_like(src)
@@ -357,6 +361,52 @@ def main():
         if not args.no_variants:
             line["cpu_oracle_widened"] = cpu_oracle_widened(layer, cfg)
     print(json.dumps(line), flush=True)
+
+
+def loss_product_flops(M, K, N, n_alpha, gram):
+    """Matrix-core flops of one loss-product launch over the whole grid, as executed.  G form:
+    each half (128 channels) of a 256-channel tile row runs over k from its own first channel
+    on, for 256-row tiles of dW (M a multiple of 256 here).  Direct form: 2 M K N per alpha."""
+    if not gram:
+        return 2.0 * M * K * N * n_alpha
+    m_pad = -(-M // 256) * 256
+    return n_alpha * sum(2.0 * m_pad * min(128, K - c0) * (K - c0) for c0 in range(0, K, 128))
+
+
+def gram_build_flops(N, K):
+    """Matrix-core flops of the Gram build as executed: every 256 x 256 tile of G's upper block
+    triangle (the diagonal tiles whole) over the N tokens."""
+    T = -(-K // 256)
+    return T * (T + 1) / 2 * 2.0 * 256 * 256 * N
+
+
+def measure_size_floor(torch, Xd, Wd, sptr, copy_gbs, reps=20):
+    """Plain device operations on the headline layer's own tensors, for the size floor of the
+    short statistics and pack launches: a full read of X (torch.sum over all elements, fp32
+    accumulation) and a copy of W (read + write of the same bytes)."""
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(sptr)
+        for _ in range(reps):
+            fn()
+        e1.record(sptr)
+        torch.cuda.synchronize()
+        return e0.elapsed_ms(e1) / reps
+
+    out = {}
+    ms = timed(lambda: torch.sum(Xd, dtype=torch.float32))
+    b = Xd.numel() * 2.0
+    out["read_X_torch_sum"] = {"ms": ms, "bytes": b, "GB/s": b / (ms * 1e-3) / 1e9,
+                               "frac_copy_ceiling": b / (ms * 1e-3) / 1e9 / copy_gbs}
+    dst = torch.empty_like(Wd)
+    ms = timed(lambda: dst.copy_(Wd))
+    b = Wd.numel() * 4.0
+    out["copy_W"] = {"ms": ms, "bytes": b, "GB/s": b / (ms * 1e-3) / 1e9,
+                     "frac_copy_ceiling": b / (ms * 1e-3) / 1e9 / copy_gbs}
+    return out
 
 
 def measure_ceilings(torch, sptr, reps=20):
@@ -394,7 +444,7 @@ def measure_ceilings(torch, sptr, reps=20):
             "torch_matmul_frac_of_2.5PF": gemm_tf / MFMA_F16_PEAK_TFLOPS}
 
 
-def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, reps=20):
+def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, copy_gbs, reps=20):
     """Average time per call of the widened entry points on the same layer, measured
     after the timed region (HIP events around `reps` back-to-back calls)."""
 
@@ -416,24 +466,28 @@ def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, reps=20):
                               ("stat_ema_mean_b512", awq.AWQ_STAT_EMA_MEAN, (512, 0.9))]:
         ms = timed(lambda: awq.awq_act_stats_ex(Xd, mode, *extra))
         gbs = x_bytes / (ms * 1e-3) / 1e9
-        out[name] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+        out[name] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                     "frac_copy_ceiling": gbs / copy_gbs, "timed": "whole call (two launches)"}
     a = awq.awq_act_stats(Xd)
     out["threshold_scales"] = {"ms": timed(lambda: awq.awq_threshold_scales(a, 70.0, 2.0)),
                                "in_features": K}
     Xr = torch.empty_like(Xd)
     ms = timed(lambda: awq.awq_hadamard_rotate(Xd, 128, out=Xr))
     gbs = 4.0 * N * K / (ms * 1e-3) / 1e9
-    out["hadamard_rotate_X_b128"] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    out["hadamard_rotate_X_b128"] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                                     "frac_copy_ceiling": gbs / copy_gbs}
     table = torch.stack([awq.awq_threshold_scales(a, p, f) for p in (50.0, 70.0, 85.0, 95.0, 99.0)
                          for f in (1.5, 2.0, 3.0, 4.0)]).contiguous()
     ws = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, table.shape[0], 0), dtype=torch.uint8,
                      device="cuda")
     ms = timed(lambda: awq.awq_search_scale_table(Wd, Xd, table, cfg, workspace=ws))
-    tf = 2.0 * M * N * K * table.shape[0] / (ms * 1e-3) / 1e12
-    form = awq.awq_loss_form(M, K, N, table.shape[0])
+    gram = awq.awq_loss_form(M, K, N, table.shape[0]) == awq.AWQ_LOSS_GRAM
+    ex = loss_product_flops(M, K, N, table.shape[0], gram) + (gram_build_flops(N, K) if gram else 0)
+    tfx = ex / (ms * 1e-3) / 1e12
     out["search_scale_table_20_threshold_rows"] = {
-        "ms": ms, "direct_equivalent_TFLOP/s": tf,
-        "form": "gram" if form == awq.AWQ_LOSS_GRAM else "direct"}
+        "ms": ms, "executed_mfma_flops": ex, "TFLOP/s_whole_search": tfx,
+        "frac_mfma_whole_search": tfx / MFMA_F16_PEAK_TFLOPS,
+        "form": "gram" if gram else "direct"}
     ratios = [1.0 - 0.025 * k for k in range(20)]
     s_best = awq.awq_search_scales(Wd, Xd, a, [0.5], cfg)["s"]
     ws_clip = torch.empty(awq.awq_clip_workspace_bytes(M, K, N, cfg), dtype=torch.uint8,
@@ -514,15 +568,22 @@ def w4a16_bytes(M, K, g, T, with_s):
     return M * K / 2 + 4.0 * M * K / g + 2.0 * T * K + (4.0 * K if with_s else 0.0) + 2.0 * T * M
 
 
-def time_large_layers(awq, torch, alphas, sptr, reps=2):
-    """The whole 20-alpha search (statistics excluded) on the four large layer shapes, with
-    seeded device-side weights and activations (1% of the channels scaled by 20).  With
-    many more tokens than channels the library takes the loss through X^T X; the
-    direct-equivalent rate divides the direct form's 2 M K N per alpha by the time."""
+def time_large_layers(awq, torch, alphas, sptr, copy_gbs, reps=2):
+    """The whole 20-alpha search on the four large layer shapes, with seeded device-side
+    weights and activations (1% of the channels scaled by 20).  The library's event hook
+    times the Gram pass and the loss product of each search separately; their rates are
+    executed matrix-core flops over kernel time.  On the 70B-class shape the statistics
+    (over its 1 GiB of activations) and the pack (of its 448 MiB weight) are timed too."""
     shapes = [("c3 up", 11008, 4096, 16384, 4, 128, 1), ("c3 down", 4096, 11008, 16384, 4, 128, 1),
               ("c5", 13824, 5120, 32768, 3, 64, 1), ("c4", 28672, 8192, 65536, 4, 128, 1)]
     out = {}
     gen = torch.Generator(device="cuda")
+    nA = len(alphas)
+
+    def tf(flops, ms):
+        v = flops / (ms * 1e-3) / 1e12
+        return {"TFLOP/s": v, "frac_mfma": v / MFMA_F16_PEAK_TFLOPS}
+
     for name, M, K, N, b, g, zp in shapes:
         gen.manual_seed(20260 + M)
         W = (torch.randn((M, K), device="cuda", generator=gen) * 0.02).half()
@@ -531,28 +592,76 @@ def time_large_layers(awq, torch, alphas, sptr, reps=2):
         X = X.half()
         cfg = awq.qconfig(b, g, zp)
         a = awq.awq_act_stats(X)
-        ws = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, len(alphas), 0),
+        ws = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, nA, 0),
                          dtype=torch.uint8, device="cuda")
         awq.awq_search_scales(W, X, a, alphas, cfg, workspace=ws)
         torch.cuda.synchronize()
-        e0, e1 = HipEvent(), HipEvent()
-        e0.record(sptr)
+        gram = awq.awq_loss_form(M, K, N, nA) == awq.AWQ_LOSS_GRAM
+        runs = []
         for _ in range(reps):
+            ev = [HipEvent() for _ in range(8)]
+            ev[0].record(sptr)
+            awq.awq_set_profile_events(ev[2], ev[3], ev[4], ev[5], ev[6], ev[7])
             awq.awq_search_scales(W, X, a, alphas, cfg, workspace=ws)
-        e1.record(sptr)
+            ev[1].record(sptr)
+            runs.append(ev)
         torch.cuda.synchronize()
-        ms = e0.elapsed_ms(e1) / reps
-        direct = 2.0 * M * K * N * len(alphas)
-        out[name] = {"M": M, "K": K, "N": N, "w_bit": b, "group_size": g, "search_ms": ms,
-                     "form": "gram" if awq.awq_loss_form(M, K, N, len(alphas)) == awq.AWQ_LOSS_GRAM
-                     else "direct",
-                     "direct_equivalent_TFLOP/s": direct / (ms * 1e-3) / 1e12}
+        search_ms = float(sum(e[0].elapsed_ms(e[1]) for e in runs) / reps)
+        gemm_ms = float(sum(e[2].elapsed_ms(e[3]) for e in runs) / reps)
+        fq_ms = float(sum(e[4].elapsed_ms(e[5]) for e in runs) / reps)
+        gflops = loss_product_flops(M, K, N, nA, gram)
+        entry = {"M": M, "K": K, "N": N, "w_bit": b, "group_size": g, "search_ms": search_ms,
+                 "form": "gram" if gram else "direct",
+                 "loss_product": {"ms": gemm_ms, "flops": gflops, **tf(gflops, gemm_ms)},
+                 "fake_quant": {"ms": fq_ms,
+                                "GB/s": (2.0 * M * K * (nA + 1)) / (fq_ms * 1e-3) / 1e9}}
+        bflops = 0.0
+        if gram:
+            gram_ms = float(sum(e[6].elapsed_ms(e[7]) for e in runs) / reps)
+            bflops = gram_build_flops(N, K)
+            entry["gram_pass"] = {"ms": gram_ms, "build_flops": bflops, **tf(bflops, gram_ms)}
+        entry["direct_over_executed_flops"] = 2.0 * M * K * N * nA / (gflops + bflops)
+        if name == "c4":
+            entry["act_stats"] = time_stats_and_pack(awq, torch, W, X, cfg, sptr, copy_gbs)
+        out[name] = entry
         del W, X, a, ws
         torch.cuda.empty_cache()
     return out
 
 
-def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, reps=50):
+def time_stats_and_pack(awq, torch, W, X, cfg, sptr, copy_gbs, reps=5):
+    """Statistics over a 1 GiB activation tensor and the pack of a 448 MiB weight: sizes at
+    which the HBM fraction of these streaming kernels is not set by launch overhead."""
+    N, K = X.shape
+    M = W.shape[0]
+    ws = torch.empty(awq.awq_act_stats_workspace_bytes(N, K), dtype=torch.uint8, device="cuda")
+    s = torch.ones(K, dtype=torch.float32, device="cuda") * 1.5
+    awq.awq_act_stats(X, workspace=ws)
+    awq.awq_quantize_pack(W, s, cfg)
+    torch.cuda.synchronize()
+    st, pk = [], []
+    for _ in range(reps):
+        e = [HipEvent() for _ in range(4)]
+        awq.awq_set_stats_profile_events(e[0], e[1])
+        awq.awq_act_stats(X, workspace=ws)
+        e[2].record(sptr)
+        awq.awq_quantize_pack(W, s, cfg)
+        e[3].record(sptr)
+        st.append(e)
+    torch.cuda.synchronize()
+    ms_s = float(sum(e[0].elapsed_ms(e[1]) for e in st) / reps)
+    ms_p = float(sum(e[2].elapsed_ms(e[3]) for e in st) / reps)
+    sb = 2.0 * N * K + 4.0 * K
+    pb = 2.0 * M * K + 4.0 * K + M * K / 2 + 4.0 * M * K / cfg.group_size
+    return {"stats_pass": {"ms": ms_s, "bytes": sb, "GB/s": sb / (ms_s * 1e-3) / 1e9,
+                           "frac_hbm_8TBps": sb / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "frac_copy_ceiling": sb / (ms_s * 1e-3) / 1e9 / copy_gbs},
+            "quant_pack": {"ms": ms_p, "bytes": pb, "GB/s": pb / (ms_p * 1e-3) / 1e9,
+                           "frac_hbm_8TBps": pb / (ms_p * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "frac_copy_ceiling": pb / (ms_p * 1e-3) / 1e9 / copy_gbs}}
+
+
+def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, copy_gbs, reps=50):
     """The packed layer's W4A16 product at decode batches 1 and 4: on the layer just packed,
     and on a 28672 x 8192 packed layer (the 70B-class MLP shape) of seeded random codes."""
 
@@ -578,7 +687,8 @@ def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, reps=50):
         ms = timed(lambda: awq.awq_w4a16_matmul(x, codes, scales, zeros, cfg, s=s, workspace=ws))
         b = w4a16_bytes(M, K, g, T, True)
         out[f"{M}x{K}_T{T}"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b,
-                                "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                                "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                "frac_copy_ceiling": b / (ms * 1e-3) / 1e9 / copy_gbs}
     M2, K2 = 28672, 8192
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20250)
@@ -593,13 +703,15 @@ def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, reps=50):
             ms = timed(lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg, s=s2, workspace=ws))
             b = w4a16_bytes(M2, K2, g, T, True)
             out[f"{M2}x{K2}_T{T}"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b,
-                                      "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                                      "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                "frac_copy_ceiling": b / (ms * 1e-3) / 1e9 / copy_gbs}
         # S^-1 already folded into the activations (the deployed form): no division
         ms = timed(lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg))
         b = w4a16_bytes(M2, K2, g, T, False)
         out[f"{M2}x{K2}_T{T}_folded"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9,
                                           "bytes": b,
-                                          "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                                          "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                "frac_copy_ceiling": b / (ms * 1e-3) / 1e9 / copy_gbs}
     return out
 
 
