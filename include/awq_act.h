@@ -84,6 +84,20 @@ size_t awq_act_stats_workspace_bytes(int64_t n_tokens, int64_t in_features);
 int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* a_out,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* awq_act_stats for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and the
+ * same result bit for bit, with the partial sums in a static device array of the library
+ * (AWQ_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, held until the process
+ * ends) instead of a workspace.  The array's address on the current device is looked up
+ * on the first call there.  Shapes whose partials need more than the array holds
+ * (awq_act_stats_workspace_bytes(N, K) > AWQ_NOALLOC_SCRATCH_BYTES; about 4 MiB suffices
+ * for every in_features up to 10^6) return AWQ_E_WORKSPACE.  Every call on one GPU uses
+ * that GPU's one array: calls that overlap on a GPU (other streams, other threads) race
+ * and must be ordered by the caller.  Other arguments and errors as for awq_act_stats. */
+#define AWQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+int awq_act_stats_noalloc(const void* X, int64_t n_tokens, int64_t in_features, float* a_out,
+                          void* stream);
+
 /* Other statistics (same workspace convention, sized by the _ex query):
  *   AWQ_STAT_MEAN_ABS   mean |x|                                     (as awq_act_stats)
  *   AWQ_STAT_MAX_ABS    max |x| over tokens [GPTQ-AWQ §3 二.2: s = (max|A|)^alpha]; exact

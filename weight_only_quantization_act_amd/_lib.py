@@ -47,6 +47,7 @@ _SIGNATURES = {
     "awq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "awq_act_stats_workspace_bytes": (_sz, [_i64, _i64]),
     "awq_act_stats": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "awq_act_stats_noalloc": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "awq_workspace_bytes": (_sz, [_i64, _i64, _i64, _cfgp, _i32, _i32]),
     "awq_loss_form": (ctypes.c_int, [_i64, _i64, _i64, _i32]),
     "awq_search_scales": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _cfgp, _vp, _i32,
@@ -177,6 +178,27 @@ def awq_act_stats(X: torch.Tensor, out: Optional[torch.Tensor] = None,
                              ws.numel() * ws.element_size(), _stream_ptr(stream))
     _check(st, "awq_act_stats")
     return a
+
+
+AWQ_NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+@_on_stream
+def awq_act_stats_noalloc(X: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """awq_act_stats with the library's static device scratch instead of a workspace (for
+    callers that cannot allocate: the output is the caller's, nothing is allocated here).
+    Calls that overlap on one GPU race on that scratch."""
+    _dev(X, torch.float16, "X")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [n_tokens, in_features]")
+    N, K = X.shape
+    _dev(out, torch.float32, "out")
+    if out.numel() < max(K, 1):
+        raise ValueError("out must hold in_features floats")
+    st = lib().awq_act_stats_noalloc(_ptr(X) if X.numel() else _ptr(out), N, K, _ptr(out),
+                                     _stream_ptr(stream))
+    _check(st, "awq_act_stats_noalloc")
+    return out[:K]
 
 
 def awq_workspace_bytes(out_features: int, in_features: int, n_tokens: int, cfg: awq_qconfig,
