@@ -56,6 +56,23 @@
 #ifndef LOSS_WN
 #define LOSS_WN 4
 #endif
+#ifndef LOSS_MIN_BLOCKS
+#define LOSS_MIN_BLOCKS 1
+#endif
+// Interleave pattern of a k-step (0: left to the compiler): LOSS_ILV MFMAs, then one
+// fragment read, repeated.
+#ifndef LOSS_ILV
+#define LOSS_ILV 0
+#endif
+// G form: each pass runs its k-tiles from the last one down to its diagonal block (1), so
+// that the tile's own dW block is in LDS when the pass ends, or upwards (0).
+#ifndef LOSS_GRAM_REV
+#define LOSS_GRAM_REV 1
+#endif
+// Raised wave priority around the fragment reads and refill DMAs (1) or none (0).
+#ifndef LOSS_PRIO
+#define LOSS_PRIO 1
+#endif
 
 namespace awq {
 
@@ -164,7 +181,7 @@ struct Stage {
 // to tmax[pair]; with several, to gout = partial tiles [split][pair][BM][BN].
 constexpr int kModeDirect = 0, kModeGramLoss = 1, kModeGramBuild = 2;
 template <class S, int MODE>
-__global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
+__global__ __launch_bounds__(S::THREADS, LOSS_MIN_BLOCKS) void k_loss_gemm(
     const uint16_t* __restrict__ dW, const uint16_t* __restrict__ X,
     const float* __restrict__ gdiag, int M, int N, int K, int ld, int kchunk, int tiles_m,
     int tiles_n, int nb, const int32_t* __restrict__ gexp, double* __restrict__ partials,
@@ -178,9 +195,16 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   __shared__ __attribute__((aligned(1024))) uint8_t sm1[S::NS > 1 ? S::BYTES : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t sm2[S::NS > 2 ? S::BYTES : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t sm3[S::NS > 3 ? S::BYTES : 16];
-  __shared__ double red[S::WAVES];
+  // REV (the G form in reverse k order) fills the whole 160 KiB: two stages and a spare
+  // buffer for the tile's upper 64 dW channels; its reduction slots and diag(G) staging
+  // then live in stage memory that is free when they are used.
+  constexpr bool REV = GRAM && LOSS_GRAM_REV;
+  __shared__ __attribute__((aligned(1024))) uint8_t smx[REV ? (BN * S::BK * 2) : 16];
+  __shared__ double red_a[S::WAVES];
   __shared__ float redf[S::WAVES];
-  __shared__ __attribute__((aligned(16))) float gds[GRAM ? BM : 4];  // GRAM: the tile's diag(G)
+  __shared__ __attribute__((aligned(16))) float gds_a[GRAM && !REV ? BM : 4];
+  static_assert(!REV || (S::NS == 2 && S::BK == 64 && 2 * S::BYTES + BN * S::BK * 2 == 163840),
+                "the reverse G form fills the LDS exactly");
   static_assert(S::NS >= 2 && S::NS <= 4, "2..4 stages");
 
   const int tid = threadIdx.x;
@@ -267,6 +291,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
 
   // LDS byte addresses of the stage buffers (uniform, computed once).
   const unsigned lds_stage[4] = {lds_addr(sm0), lds_addr(sm1), lds_addr(sm2), lds_addr(sm3)};
+  const unsigned lds_spare = REV ? lds_addr(smx) : 0u;
 
   // k-tiles rounded up to a multiple of NS: the padding tiles lie past the reduction
   // length, read as zeros and add nothing, and the NS-unrolled loop below then has a
@@ -276,10 +301,21 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   static_assert(!GRAM || (BM / S::BK) % S::NS == 0, "the diagonal block starts on a whole pipeline step");
   int kt0 = 0, nkt = nk;
 
-  // loop tile i -> k-tile kt0 + i; past the end: zeros
+  // loop tile i -> k-tile kt0 + i (REV: nk - 1 - i); past the end: zeros, or (REV) nothing,
+  // since the stages then hold the tile's dW block for the epilogue
+  // REV, the last two refills (loop tiles nkt - 2 and nkt - 1, k-tiles kt0 + 1 and kt0, in
+  // stages 0 and 1): the A rows BM / 2 .. BM - 1 of those k-tiles are zero in G' (the lower-left
+  // half of the diagonal block), so the waves that would load them (wave >= WAVES / 2) load
+  // dW channels kt0 + 2 of the tile instead, rows 0 .. 127 into stage 0 and rows 128 .. 255
+  // into stage 1 (A-region row 128 + (r mod 128)), and with the first of them every wave
+  // loads its rows of channels kt0 + 3 into the spare buffer.
+  const unsigned epi_shift = (unsigned)(BM / 2) * (unsigned)LD * 2u;  // 128 dW rows, bytes
   auto dma_stage = [&](auto st, int i) {
     constexpr int ST = decltype(st)::value;
-    const int k0 = (i < nkt ? kt0 + i : nk) * S::BK;
+    if constexpr (REV) {
+      if (i >= nkt) return;
+    }
+    const int k0 = (i < nkt ? (REV ? nk - 1 - i : kt0 + i) : nk) * S::BK;
     const unsigned la = lds_stage[ST] + (unsigned)(wave * S::DMA_A) * 1024u;
     const unsigned lb = lds_stage[ST] + (unsigned)S::A_BYTES + (unsigned)(wave * S::DMA_B) * 1024u;
     const bool k_ok0 = k0 + dma_lchunk_even * 8 < KR;
@@ -287,12 +323,36 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     const unsigned va0 = k_ok0 ? vo_a0 : kOutOfRange, va1 = k_ok1 ? vo_a1 : kOutOfRange;
     const unsigned vb0 = k_ok0 ? vo_b0 : kOutOfRange, vb1 = k_ok1 ? vo_b1 : kOutOfRange;
     const unsigned kbytes = (unsigned)k0 * 2u;
+    bool epi = false;
+    if constexpr (REV) epi = nkt >= 4 && i == nkt - 2 + ST && wave >= S::WAVES / 2;
+    if (!epi) {
 #pragma unroll
-    for (int j = 0; j < S::DMA_A; ++j)
-      dma16(rsrc_a, la + j * 1024u, (j & 1) ? va1 : va0, kbytes + j * dma_row_stride);
+      for (int j = 0; j < S::DMA_A; ++j)
+        dma16(rsrc_a, la + j * 1024u, (j & 1) ? va1 : va0, kbytes + j * dma_row_stride);
+    } else {
+      // dW rows (wave - WAVES/2) 32 + ... of channels kt0 + 2 into the A-region rows 128 + ...
+      const int ke = (kt0 + 2) * S::BK;
+      const bool e0 = ke + dma_lchunk_even * 8 < KR, e1 = ke + dma_lchunk_odd * 8 < KR;
+      const unsigned sh = ST == 0 ? epi_shift : 0u;
+      const unsigned ve0 = e0 ? vo_b0 - sh : kOutOfRange, ve1 = e1 ? vo_b1 - sh : kOutOfRange;
+#pragma unroll
+      for (int j = 0; j < S::DMA_A; ++j)
+        dma16(rsrc_b, la + j * 1024u, (j & 1) ? ve1 : ve0, (unsigned)ke * 2u + j * dma_row_stride);
+    }
 #pragma unroll
     for (int j = 0; j < S::DMA_B; ++j)
       dma16(rsrc_b, lb + j * 1024u, (j & 1) ? vb1 : vb0, kbytes + j * dma_row_stride);
+    if constexpr (REV && ST == 0) {
+      if (nkt >= 4 && i == nkt - 2) {  // channels kt0 + 3 of every row into the spare buffer
+        const int ks3 = (kt0 + 3) * S::BK;
+        const bool s0 = ks3 + dma_lchunk_even * 8 < KR, s1 = ks3 + dma_lchunk_odd * 8 < KR;
+        const unsigned vs0 = s0 ? vo_b0 : kOutOfRange, vs1 = s1 ? vo_b1 : kOutOfRange;
+        const unsigned ls = lds_spare + (unsigned)(wave * S::DMA_B) * 1024u;
+#pragma unroll
+        for (int j = 0; j < S::DMA_B; ++j)
+          dma16(rsrc_b, ls + j * 1024u, (j & 1) ? vs1 : vs0, (unsigned)ks3 * 2u + j * dma_row_stride);
+      }
+    }
   };
 
   // ---- fragment reads: MFMA 32x32x16 f16 operand = row (l mod 32), channels
@@ -311,7 +371,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   // the other wave's MFMAs take the issue slots (same-box A/B of the 20-alpha search,
   // three rounds: 1.696 against 1.727 ms; priority around the MFMAs instead: 1.698).
   auto load_frag = [&](auto st, int ks, Frag& f) {
-    __builtin_amdgcn_s_setprio(1);
+    if constexpr (LOSS_PRIO) __builtin_amdgcn_s_setprio(1);
     const uint8_t* base = stage_ptr(st);
     const int chunk = ((2 * ks + frag_half) ^ frag_swz) * 16;
 #pragma unroll
@@ -320,7 +380,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
 #pragma unroll
     for (int ni = 0; ni < S::NI; ++ni)
       f.b[ni] = *(const half8*)(base + b_off + ni * 32 * S::BK * 2 + chunk);
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (LOSS_PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   floatx16 acc[S::MI][S::NI];
@@ -345,6 +405,17 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   static_assert(S::KSTEPS % 2 == 0, "even number of 16-channel steps per stage");
   Frag f0, f1;
 
+  // optional explicit interleave of a k-step's MFMAs with the next k-step's fragment reads
+  auto ilv = [&]() {
+    if constexpr (LOSS_ILV > 0) {
+#pragma unroll
+      for (int i = 0; i < S::MI + S::NI; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, LOSS_ILV, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, S::MI * S::NI, 0);
+    }
+  };
   // one k-tile held in stage ST (k-tile index kt)
   auto step = [&](auto st, int kt) {
     constexpr int ST = decltype(st)::value;
@@ -353,19 +424,22 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     for (int ks = 0; ks + 2 < S::KSTEPS; ks += 2) {
       load_frag(st, ks + 1, f1);
       mma(f0);
+      ilv();
       load_frag(st, ks + 2, f0);
       mma(f1);
+      ilv();
     }
     load_frag(st, S::KSTEPS - 1, f1);
     mma(f0);
+    ilv();
     // stage kt+1 has landed (own DMAs) and this wave's reads of stage kt are done
     __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 2) * S::PER_STAGE>::value);
     __builtin_amdgcn_s_barrier();
     // the refill DMAs, too, go out at raised priority (same-box A/B, three rounds: loss
     // product 1.339 against 1.370 ms)
-    __builtin_amdgcn_s_setprio(1);
+    if constexpr (LOSS_PRIO) __builtin_amdgcn_s_setprio(1);
     dma_stage(st, kt + S::NS);
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (LOSS_PRIO) __builtin_amdgcn_s_setprio(0);
     load_frag(NEXT{}, 0, f0);  // after the last k-tile this reads a slot nobody uses
     mma(f1);
   };
@@ -381,9 +455,9 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     using NEXT = std::integral_constant<int, (ST + 1) % S::NS>;
     __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 2) * S::PER_STAGE>::value);
     __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_s_setprio(1);
+    if constexpr (LOSS_PRIO) __builtin_amdgcn_s_setprio(1);
     dma_stage(st, kt + S::NS);
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (LOSS_PRIO) __builtin_amdgcn_s_setprio(0);
     load_frag(NEXT{}, 0, f0);
   };
   const bool idle_first = GRAM && wm == 1;
@@ -398,10 +472,11 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   // set nobody uses).
   const int nparts = (GRAM && tiles_m - 1 - tm != tm) ? 2 : 1;
   for (int part = 0; part < nparts; ++part) {
-  // the short row (tiles_m - 1 - tm) first: after it, every block of a pair set streams
-  // the same k-tile of its dW panel at the same time, so blocks sharing that panel share
-  // its reads in L2
-  const int tmc = (part == 0) == (nparts == 2) ? tiles_m - 1 - tm : tm;
+  // the blocks of a pair set that share a dW panel stream the same k-tile of it at the same
+  // time during their long row, so they share its reads in L2: in forward k order the short
+  // row (tiles_m - 1 - tm) comes first, in reverse order (REV) the long row (tm), both rows
+  // ending at their diagonal blocks
+  const int tmc = ((part == 0) == (nparts == 2)) != REV ? tiles_m - 1 - tm : tm;
   {
     const uint16_t* A = BUILD  ? X + (size_t)tmc * BM * LD + k_first
                         : GRAM ? X + (size_t)tmc * BM * K
@@ -435,8 +510,8 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   // k-step into f0 as well.
   if (nk > 0) load_frag(I0{}, 0, f0);
 
-  int kt_begin = 0;
-  if constexpr (GRAM) {
+  int kt_begin = 0, kt_end = nkt;
+  if constexpr (GRAM && !REV) {
     if (idle_first && nkt > 0) {  // wave-uniform
       step_idle(I0{}, 0);
       if constexpr (S::NS > 1) step_idle(I1{}, 1);
@@ -445,11 +520,20 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
       kt_begin = S::NS;
     }
   }
-  for (int kt = kt_begin; kt < nkt; kt += S::NS) {
+  if constexpr (REV) {
+    if (idle_first) kt_end = nkt - S::NS;  // the half block comes last (nkt >= 2, even)
+  }
+  for (int kt = kt_begin; kt < kt_end; kt += S::NS) {
     step(I0{}, kt);
     if constexpr (S::NS > 1) step(I1{}, kt + 1);
     if constexpr (S::NS > 2) step(I2{}, kt + 2);
     if constexpr (S::NS > 3) step(I3{}, kt + 3);
+  }
+  if constexpr (REV) {
+    if (idle_first) {
+      step_idle(I0{}, nkt - 2);
+      step_idle(I1{}, nkt - 1);
+    }
   }
   __builtin_amdgcn_s_waitcnt(WaitVmLgkm<0>::value);  // no LDS write may outlive the block
 
@@ -479,6 +563,48 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
           }
         }
       }
+  } else if constexpr (REV) {
+    // The tile's own dW block is in LDS already: channels 0..63 of the tile in stage 1's B
+    // half (k-tile kt0), 64..127 in stage 0's B half (kt0 + 1), 128..191 in the A regions'
+    // rows 128..255 (dW rows 0..127 in stage 0, 128..255 in stage 1), 192..255 in the spare
+    // buffer; each region has 128-byte rows with the stages' chunk swizzle.  diag(G) of the
+    // tile goes to stage 0's A rows 0..3, free once every wave has passed the last barrier.
+    float* gds = (float*)sm0;
+    __syncthreads();
+    if (tid < BM) gds[tid] = gd_pre;
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < S::MI; ++mi) {
+      const int cl = wm * S::MI * 32 + mi * 32 + 4 * (lane >> 5);  // channel within the tile
+      const int q = cl >> 6;                                        // 64-channel slice
+#pragma unroll
+      for (int ni = 0; ni < S::NI; ++ni) {
+        const int rl = wn * S::NI * 32 + ni * 32 + (lane & 31);   // row within the tile
+        const uint8_t* rowp;
+        if (q == 0)      rowp = sm1 + S::A_BYTES + rl * (S::BK * 2);
+        else if (q == 1) rowp = sm0 + S::A_BYTES + rl * (S::BK * 2);
+        else if (q == 2) rowp = (rl < BM / 2 ? sm0 : sm1) + ((rl & (BM / 2 - 1)) + BM / 2) * (S::BK * 2);
+        else             rowp = smx + rl * (S::BK * 2);
+        const int sw = S::swz(rl);
+        float tsum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = cl + 8 * j;                                   // first of 4 channels
+          const floatx4 g4 = *(const floatx4*)(gds + c);
+          u32x2 w2 = *(const u32x2*)(rowp + ((((c & 63) >> 3) ^ sw) * 16) + 8 * (lane >> 5));
+          if (tmc * BM + c >= N) w2 = u32x2{0u, 0u};                  // past in_features
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const unsigned w = w2[qq >> 1];
+            const float d = (float)__builtin_bit_cast(
+                _Float16, (uint16_t)(qq & 1 ? w >> 16 : w & 0xffffu));
+            tsum = fmaf(d, fmaf(d, g4[qq], acc[mi][ni][4 * j + qq]), tsum);
+          }
+        }
+        ssum += (double)tsum;
+      }
+    }
+    __syncthreads();  // the next tile row's DMAs reuse the stage buffers
   } else if constexpr (GRAM) {
     // The tile's own dW block (its 256 rows x its 256 channels) is staged through the
     // stage buffers, free now: every wave's DMAs have landed (vmcnt(0) above, then the
@@ -490,23 +616,25 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     // in_features take the out-of-range offset (K is a multiple of 8, so a chunk is wholly
     // inside or outside).
     static_assert(S::NS >= 2 && S::BYTES >= (BM / 2) * BN * 2, "two stage buffers hold the block");
-    static_assert(BM == 256 && BN == 256 && S::WAVES == 8, "epilogue staging geometry");
+    static_assert(BM == 256 && BN == 256 && (BN / S::WAVES) % 2 == 0, "epilogue staging geometry");
+    constexpr int kRowsPerWave = BN / S::WAVES;  // tile rows each wave stages, two per DMA
     __syncthreads();
     {
       // rsrc_b is this tile's rows of dW_k (at most 256 K 2 bytes from row tn BN)
       const int half = lane >> 5, pos = lane & 31;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rl = wave * 32 + 2 * i + half;     // row within the tile (wave-uniform pair)
+      for (int i = 0; i < kRowsPerWave / 2; ++i) {
+        const int rl = wave * kRowsPerWave + 2 * i + half;  // row within the tile (uniform pair)
         const int q = pos ^ (rl & 31);                // logical chunk held at position pos
         const int c = tmc * BM + 8 * q;
         const unsigned voff = c < N ? ((unsigned)rl * (unsigned)K + (unsigned)c) * 2u : kOutOfRange;
-        const int rpair = wave * 32 + 2 * i;          // first row of this DMA (uniform)
+        const int rpair = wave * kRowsPerWave + 2 * i;  // first row of this DMA (uniform)
         const unsigned lds = (rpair < 128 ? lds_stage[0] + (unsigned)rpair * 512u
                                           : lds_stage[1] + (unsigned)(rpair - 128) * 512u);
         dma16(rsrc_b, lds, voff, 0u);
       }
     }
+    float* gds = gds_a;
     if (tid < BM) gds[tid] = gd_pre;
     __builtin_amdgcn_s_waitcnt(WaitVmLgkm<0>::value);
     __syncthreads();
@@ -566,6 +694,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     }
     return;
   }
+  double* red = REV ? (double*)sm1 : red_a;  // REV: stage 1 is free after the last epilogue
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off);
   if (lane == 0) red[wave] = ssum;
