@@ -27,7 +27,10 @@
  *     call synchronises the host.
  *   - Errors are return codes (awq_status); nothing throws across the ABI.  All
  *     argument checks run on the host before any launch; a failed check enqueues
- *     nothing.  AWQ_E_HIP reports a failed launch or HIP runtime call.
+ *     nothing.  AWQ_E_HIP reports a failed launch or HIP runtime call.  Before its first
+ *     launch every entry point clears the calling thread's pending HIP error (as
+ *     hipGetLastError does), so that an earlier, unrelated failed runtime call is not
+ *     reported as its own.
  *   - Calls are thread-safe given distinct workspaces (no global mutable state other
  *     than the per-thread profiling hook below).
  *   - Sizes: M*K and N*K must stay below 2^31 elements.

@@ -256,6 +256,32 @@ def test_layer_on_a_side_stream():
         assert np.array_equal(got.view(np.uint8), ref[k].view(np.uint8)), k
 
 
+def test_stale_runtime_error_is_not_reported():
+    """An error left pending by an earlier, unrelated HIP call of the thread (here the elapsed
+    time of two events that were never recorded) is not reported as the library's own
+    launch failure: the search in either form, the statistics and the pack still succeed."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipPeekAtLastError.restype = ctypes.c_int
+    cfg = awq.qconfig(4, 128, 1)
+    for M, K, N in [(300, 256, 100), (300, 256, 3000)]:            # direct form, G form
+        L = make_layer(small_spec("st", M, K, N, outlier_count=2))
+        Wd, Xd = dev(L.W), dev(L.X)
+        e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e0)) == 0 and hip.hipEventCreate(ctypes.byref(e1)) == 0
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1) != 0  # never recorded
+        assert hip.hipPeekAtLastError() != 0                           # the error is pending
+        say(f"stale error, then the layer {M}x{K}x{N}")
+        res = awq.quantize_layer(Wd, Xd, alpha_grid(4), cfg)
+        torch.cuda.synchronize()
+        assert int(host(res["status"])[0]) == awq.AWQ_OK
+        assert int(host(res["pack_status"])[0]) == awq.AWQ_OK
+
+
 # ----------------------------------------------------------------------------- A2-A5 search
 SEARCH_CASES = [
     # M, K, N, w_bit, g, zp

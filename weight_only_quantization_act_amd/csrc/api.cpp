@@ -114,6 +114,12 @@ thread_local void* g_stats_ev[2] = {nullptr, nullptr};
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_E_HIP; }
 
+// The launchers report a failed launch through hipGetLastError, which would also return an
+// error left pending by an earlier, unrelated runtime call of the calling thread (an event
+// query that failed, say).  Every entry point clears that pending error before its first
+// launch, so AWQ_E_HIP reports its own launches only.
+inline void clear_pending_error() { (void)hipGetLastError(); }
+
 inline int record(void* ev, hipStream_t st) {
   if (!ev) return AWQ_OK;
   return hip_status(hipEventRecord((hipEvent_t)ev, st));
@@ -232,6 +238,7 @@ int awq_act_stats_ex(const void* X, int64_t n_tokens, int64_t in_features, int32
     return AWQ_E_ALIGN;
   if (in_features == 0) return AWQ_OK;
   if ((st = device_ptr(X)) || (st = device_ptr(a_out)) || (st = device_ptr(workspace))) return st;
+  clear_pending_error();
   const awq::StatsPlan p = awq::stats_plan(n_tokens, in_features, statistic, batch_tokens);
   hipEvent_t ev0 = (hipEvent_t)g_stats_ev[0], ev1 = (hipEvent_t)g_stats_ev[1];
   g_stats_ev[0] = g_stats_ev[1] = nullptr;
@@ -301,6 +308,7 @@ int awq_search_scales(const void* W, const void* X, const float* a, int64_t out_
     return st;
   if (status_out && (st = device_ptr(status_out))) return st;
 
+  clear_pending_error();
   if ((st = hip_status(awq::launch_make_scales(a, (int)K, al, n_alpha,
                                                (float*)workspace, (hipStream_t)stream))))
     return st;
@@ -333,6 +341,7 @@ int awq_search_scale_table(const void* W, const void* X, const float* s_table, i
       (st = device_ptr(workspace)))
     return st;
   if (status_out && (st = device_ptr(status_out))) return st;
+  clear_pending_error();
   return run_search(W, X, s_table, M, K, N, cfg, n_cand, s_out, losses_out, best_out, status_out,
                     workspace, workspace_bytes, stream);
 }
@@ -346,6 +355,7 @@ int awq_threshold_scales(const float* a, int64_t in_features, double percentile,
   if (!aligned(a, 4) || !aligned(s_out, 4)) return AWQ_E_ALIGN;
   int st;
   if ((st = device_ptr(a)) || (st = device_ptr(s_out))) return st;
+  clear_pending_error();
   return hip_status(awq::launch_threshold_scales(a, (int)in_features, percentile, factor, s_out,
                                                  (hipStream_t)stream));
 }
@@ -361,6 +371,7 @@ int awq_hadamard_rotate(const void* A, int64_t rows, int64_t in_features, int32_
   if (rows == 0 || in_features == 0) return AWQ_OK;
   int st;
   if ((st = device_ptr(A)) || (st = device_ptr(out))) return st;
+  clear_pending_error();
   return hip_status(awq::launch_hadamard((const uint16_t*)A, (int)rows, (int)in_features, block,
                                          (uint16_t*)out, (hipStream_t)stream));
 }
@@ -396,6 +407,7 @@ int awq_w4a16_matmul(const void* x, const float* s, int64_t n_tokens, const void
       (st = device_ptr(zeros)) || (st = device_ptr(y)))
     return st;
   if (s && (st = device_ptr(s))) return st;
+  clear_pending_error();
   if (fold) {
     if ((st = device_ptr(workspace))) return st;
     uint16_t* xt = (uint16_t*)workspace;
@@ -423,6 +435,7 @@ int awq_fake_quant_delta(const void* W, const float* s, int64_t out_features,
   if (!aligned(W, 16) || !aligned(s, 16) || !aligned(dW_out, 16)) return AWQ_E_ALIGN;
   if (out_features == 0 || in_features == 0) return AWQ_OK;
   if ((st = device_ptr(W)) || (st = device_ptr(s)) || (st = device_ptr(dW_out))) return st;
+  clear_pending_error();
   return hip_status(awq::launch_fake_quant_delta(
       (const uint16_t*)W, s, (int)out_features, (int)in_features, 1, cfg->w_bit,
       cfg->group_size, cfg->zero_point, (uint16_t*)dW_out, (hipStream_t)stream));
@@ -441,6 +454,7 @@ int pack_impl(const void* W, const float* s, const float* clip, int64_t out_feat
       (status_out && !aligned(status_out, 4)))
     return AWQ_E_ALIGN;
   if (status_out && (st = device_ptr(status_out))) return st;
+  clear_pending_error();
   if (out_features == 0 || in_features == 0) {
     // an empty layer stores no step: the status word still reports AWQ_OK
     if (status_out)
@@ -545,6 +559,7 @@ int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_fe
   double* G64 = (double*)(ws + off);
   off += round_up(kg * sizeof(double), kAlign);
   float* partials = (float*)(ws + off);
+  clear_pending_error();
   if ((st = hip_status(awq::launch_group_gram((const uint16_t*)X, s, (int)N, (int)K,
                                               cfg->group_size, partials, G64, cmax, Ghi, Glo,
                                               gexp, (hipStream_t)stream))))
