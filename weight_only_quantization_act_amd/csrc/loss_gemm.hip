@@ -56,18 +56,17 @@
 #ifndef LOSS_WN
 #define LOSS_WN 4
 #endif
-#ifndef LOSS_MIN_BLOCKS
-#define LOSS_MIN_BLOCKS 1
-#endif
-// Interleave pattern of a k-step (0: left to the compiler): LOSS_ILV MFMAs, then one
-// fragment read, repeated.
-#ifndef LOSS_ILV
-#define LOSS_ILV 0
-#endif
 // G form: each pass runs its k-tiles from the last one down to its diagonal block (1), so
 // that the tile's own dW block is in LDS when the pass ends, or upwards (0).
 #ifndef LOSS_GRAM_REV
 #define LOSS_GRAM_REV 1
+#endif
+// Keep each k-step's fragment reads for the next k-step ahead of the current MFMAs (1), or
+// leave their placement to the compiler (0).  The default eight-wave tiling runs the same
+// either way (two waves per SIMD hide the reads); four waves of 128 x 128 need 1, where the
+// compiler otherwise issues a k-step's reads right before its own MFMAs.
+#ifndef LOSS_SB
+#define LOSS_SB 0
 #endif
 // Raised wave priority around the fragment reads and refill DMAs (1) or none (0).
 #ifndef LOSS_PRIO
@@ -181,7 +180,7 @@ struct Stage {
 // to tmax[pair]; with several, to gout = partial tiles [split][pair][BM][BN].
 constexpr int kModeDirect = 0, kModeGramLoss = 1, kModeGramBuild = 2;
 template <class S, int MODE>
-__global__ __launch_bounds__(S::THREADS, LOSS_MIN_BLOCKS) void k_loss_gemm(
+__global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     const uint16_t* __restrict__ dW, const uint16_t* __restrict__ X,
     const float* __restrict__ gdiag, int M, int N, int K, int ld, int kchunk, int tiles_m,
     int tiles_n, int nb, const int32_t* __restrict__ gexp, double* __restrict__ partials,
@@ -405,33 +404,25 @@ __global__ __launch_bounds__(S::THREADS, LOSS_MIN_BLOCKS) void k_loss_gemm(
   static_assert(S::KSTEPS % 2 == 0, "even number of 16-channel steps per stage");
   Frag f0, f1;
 
-  // optional explicit interleave of a k-step's MFMAs with the next k-step's fragment reads
-  auto ilv = [&]() {
-    if constexpr (LOSS_ILV > 0) {
-#pragma unroll
-      for (int i = 0; i < S::MI + S::NI; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, LOSS_ILV, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, S::MI * S::NI, 0);
-    }
-  };
   // one k-tile held in stage ST (k-tile index kt)
   auto step = [&](auto st, int kt) {
     constexpr int ST = decltype(st)::value;
     using NEXT = std::integral_constant<int, (ST + 1) % S::NS>;
+    auto sb = [&]() {
+      if constexpr (LOSS_SB) __builtin_amdgcn_sched_barrier(0);
+    };
 #pragma unroll
     for (int ks = 0; ks + 2 < S::KSTEPS; ks += 2) {
       load_frag(st, ks + 1, f1);
+      sb();
       mma(f0);
-      ilv();
       load_frag(st, ks + 2, f0);
+      sb();
       mma(f1);
-      ilv();
     }
     load_frag(st, S::KSTEPS - 1, f1);
+    sb();
     mma(f0);
-    ilv();
     // stage kt+1 has landed (own DMAs) and this wave's reads of stage kt are done
     __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 2) * S::PER_STAGE>::value);
     __builtin_amdgcn_s_barrier();
@@ -441,6 +432,7 @@ __global__ __launch_bounds__(S::THREADS, LOSS_MIN_BLOCKS) void k_loss_gemm(
     dma_stage(st, kt + S::NS);
     if constexpr (LOSS_PRIO) __builtin_amdgcn_s_setprio(0);
     load_frag(NEXT{}, 0, f0);  // after the last k-tile this reads a slot nobody uses
+    if constexpr (LOSS_SB) __builtin_amdgcn_sched_barrier(0);
     mma(f1);
   };
 
