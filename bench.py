@@ -444,9 +444,51 @@ def measure_ceilings(torch, sptr, reps=20):
             "torch_matmul_frac_of_2.5PF": gemm_tf / MFMA_F16_PEAK_TFLOPS}
 
 
+def graph_and_eager_ms(torch, fn, sptr, reps):
+    """(GPU time, host-inclusive time) per call of `fn`, in ms.  The GPU time comes from
+    replays of `reps` calls captured in one HIP graph (HIP events around a replay), so the
+    host's per-call marshalling and launch cost drop out; the eager figure is `reps` calls
+    issued back to back, which for calls of a few microseconds is set by the host."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = HipEvent(), HipEvent()
+    e0.record(sptr)
+    for _ in range(reps):
+        fn()
+    e1.record(sptr)
+    torch.cuda.synchronize()
+    eager = e0.elapsed_ms(e1) / reps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(sptr)
+        g.replay()
+        e1.record(sptr)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_ms(e1) / reps
+        best = ms if best is None else min(best, ms)
+    del g
+    return best, eager
+
+
 def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, copy_gbs, reps=20):
     """Average time per call of the widened entry points on the same layer, measured
-    after the timed region (HIP events around `reps` back-to-back calls)."""
+    after the timed region: the streaming calls as graph replays (with the eager per-call
+    time beside them), the two searches as `reps` back-to-back calls (milliseconds each,
+    so host overhead does not count)."""
 
     def timed(fn):
         fn()
@@ -464,18 +506,24 @@ def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, copy_gbs, reps=20):
     for name, mode, extra in [("stat_max_abs", awq.AWQ_STAT_MAX_ABS, ()),
                               ("stat_rms_ratio", awq.AWQ_STAT_RMS_RATIO, ()),
                               ("stat_ema_mean_b512", awq.AWQ_STAT_EMA_MEAN, (512, 0.9))]:
-        ms = timed(lambda: awq.awq_act_stats_ex(Xd, mode, *extra))
+        ms, eager = graph_and_eager_ms(torch, lambda: awq.awq_act_stats_ex(Xd, mode, *extra),
+                                       sptr, reps)
         gbs = x_bytes / (ms * 1e-3) / 1e9
         out[name] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
-                     "frac_copy_ceiling": gbs / copy_gbs, "timed": "whole call (two launches)"}
+                     "frac_copy_ceiling": gbs / copy_gbs, "eager_call_ms": eager,
+                     "timed": "whole call (two launches), graph replay"}
     a = awq.awq_act_stats(Xd)
-    out["threshold_scales"] = {"ms": timed(lambda: awq.awq_threshold_scales(a, 70.0, 2.0)),
-                               "in_features": K}
+    ms, eager = graph_and_eager_ms(torch, lambda: awq.awq_threshold_scales(a, 70.0, 2.0), sptr,
+                                   reps)
+    out["threshold_scales"] = {"ms": ms, "eager_call_ms": eager, "in_features": K,
+                               "timed": "graph replay"}
     Xr = torch.empty_like(Xd)
-    ms = timed(lambda: awq.awq_hadamard_rotate(Xd, 128, out=Xr))
+    ms, eager = graph_and_eager_ms(torch, lambda: awq.awq_hadamard_rotate(Xd, 128, out=Xr), sptr,
+                                   reps)
     gbs = 4.0 * N * K / (ms * 1e-3) / 1e9
     out["hadamard_rotate_X_b128"] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
-                                     "frac_copy_ceiling": gbs / copy_gbs}
+                                     "frac_copy_ceiling": gbs / copy_gbs, "eager_call_ms": eager,
+                                     "timed": "graph replay"}
     table = torch.stack([awq.awq_threshold_scales(a, p, f) for p in (50.0, 70.0, 85.0, 95.0, 99.0)
                          for f in (1.5, 2.0, 3.0, 4.0)]).contiguous()
     ws = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, table.shape[0], 0), dtype=torch.uint8,
@@ -663,32 +711,28 @@ def time_stats_and_pack(awq, torch, W, X, cfg, sptr, copy_gbs, reps=5):
 
 def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, copy_gbs, reps=50):
     """The packed layer's W4A16 product at decode batches 1 and 4: on the layer just packed,
-    and on a 28672 x 8192 packed layer (the 70B-class MLP shape) of seeded random codes."""
-
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = HipEvent(), HipEvent()
-        e0.record(sptr)
-        for _ in range(reps):
-            fn()
-        e1.record(sptr)
-        torch.cuda.synchronize()
-        return e0.elapsed_ms(e1) / reps
-
+    and on a 28672 x 8192 packed layer (the 70B-class MLP shape) of seeded random codes.
+    Kernel time from graph replays; the eager per-call time (host marshalling and launch
+    included) is reported beside it."""
     out = {}
     codes, scales, zeros = packed
     g = cfg.group_size
     # the fold workspace of the s-given calls is allocated once, outside the timed loops
     ws = torch.empty(max(256, awq.awq_w4a16_workspace_bytes(16, max(K, 8192))),
                      dtype=torch.uint8, device="cuda")
+
+    def entry(fn, b):
+        ms, eager = graph_and_eager_ms(torch, fn, sptr, reps)
+        gbs = b / (ms * 1e-3) / 1e9
+        return {"us": ms * 1e3, "GB/s": gbs, "bytes": b, "frac_hbm": gbs / HBM_PEAK_GBS,
+                "frac_copy_ceiling": gbs / copy_gbs, "eager_call_us": eager * 1e3}
+
     for T in (1, 4):
         x = Xd[:T].contiguous()
-        ms = timed(lambda: awq.awq_w4a16_matmul(x, codes, scales, zeros, cfg, s=s, workspace=ws))
-        b = w4a16_bytes(M, K, g, T, True)
-        out[f"{M}x{K}_T{T}"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b,
-                                "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                "frac_copy_ceiling": b / (ms * 1e-3) / 1e9 / copy_gbs}
+        y = torch.empty((T, M), dtype=torch.float16, device="cuda")
+        out[f"{M}x{K}_T{T}"] = entry(
+            lambda: awq.awq_w4a16_matmul(x, codes, scales, zeros, cfg, s=s, out=y, workspace=ws),
+            w4a16_bytes(M, K, g, T, True))
     M2, K2 = 28672, 8192
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20250)
@@ -699,19 +743,15 @@ def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, copy_gbs, reps=50):
     x2 = torch.randn((16, K2), device="cuda", generator=gen).half()
     for T in (1, 4, 16):
         x = x2[:T].contiguous()
+        y = torch.empty((T, M2), dtype=torch.float16, device="cuda")
         if T <= 4:
-            ms = timed(lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg, s=s2, workspace=ws))
-            b = w4a16_bytes(M2, K2, g, T, True)
-            out[f"{M2}x{K2}_T{T}"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b,
-                                      "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                "frac_copy_ceiling": b / (ms * 1e-3) / 1e9 / copy_gbs}
+            out[f"{M2}x{K2}_T{T}"] = entry(
+                lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg, s=s2, out=y, workspace=ws),
+                w4a16_bytes(M2, K2, g, T, True))
         # S^-1 already folded into the activations (the deployed form): no division
-        ms = timed(lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg))
-        b = w4a16_bytes(M2, K2, g, T, False)
-        out[f"{M2}x{K2}_T{T}_folded"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9,
-                                          "bytes": b,
-                                          "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                "frac_copy_ceiling": b / (ms * 1e-3) / 1e9 / copy_gbs}
+        out[f"{M2}x{K2}_T{T}_folded"] = entry(
+            lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg, out=y),
+            w4a16_bytes(M2, K2, g, T, False))
     return out
 
 

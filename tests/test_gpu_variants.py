@@ -5,7 +5,8 @@ against the CPU oracle.
     one fp32 ulp (its fp64 sum of squares is not exact, so the summation order can move
     the last bit); ragged token counts, batches that do not divide N, one token, NaN;
   - percentile-threshold scales bit-exact (ties, K not a power of two, the extremes
-    0 and 100, the 32768-channel maximum);
+    0 and 100, the 32768-channel maximum; negative scores, +-0, subnormals, +-inf and
+    NaN, which both sides order last);
   - the search over an explicit scale table: the same bars as the alpha-grid search;
   - the blockwise Hadamard rotation: equal fp16 values (+0 and -0 count as equal; both
     sides take the exact +-1 sums in fp64, one rounding for the normalisation and a
@@ -107,11 +108,17 @@ def _scores(rng, K, kind):
         return rng.integers(0, 5, K).astype(F32) * F32(0.25)
     if kind == "constant":
         return np.full(K, 1.5, F32)
+    if kind == "special":                       # signs, +-0, subnormals, +-inf, NaN
+        v = rng.normal(0.0, 1.0, K).astype(F32)
+        pool = np.array([0.0, -0.0, 1e-42, -1e-42, np.inf, -np.inf, np.nan, 2.0], F32)
+        pick = rng.random(K) < 0.3
+        v[pick] = pool[rng.integers(0, pool.size, int(pick.sum()))]
+        return v
     raise ValueError(kind)
 
 
 @pytest.mark.parametrize("K", [1, 2, 7, 128, 1000, 4096, 11008, 32768])
-@pytest.mark.parametrize("kind", ["lognormal", "ties", "constant"])
+@pytest.mark.parametrize("kind", ["lognormal", "ties", "constant", "special"])
 def test_threshold_scales(K, kind):
     say(f"threshold K={K} {kind}")
     rng = np.random.default_rng(K * 7 + len(kind))

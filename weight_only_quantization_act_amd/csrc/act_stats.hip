@@ -36,6 +36,13 @@ constexpr int kTokenLanes = kThreads / kChunkLanes;  // token strides per block
 constexpr int kTargetBlocks = 1024;
 constexpr int kMinTokensPerSplit = 32;
 constexpr int kMaxSplits = 128;
+#ifndef AWQ_STATS_LOAD_BATCH
+#define AWQ_STATS_LOAD_BATCH 4
+#endif
+// token rows a lane loads at once (same-box graph replays of the pass over 65536 x 8192
+// activations: 196.5 us for 1, 175.8 for 4, 186.2 for 8, 191.9 for 16; 12.4 to 14.2 us
+// for all four at 4096 x 4096)
+constexpr int kLoadBatch = AWQ_STATS_LOAD_BATCH;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -88,13 +95,25 @@ __global__ __launch_bounds__(kThreads) void k_act_stats_partial(const uint16_t* 
 
   if (VEC) {
     if (col0 < K) {
-      for (int t = t0 + lt; t < t1; t += kTokenLanes) {
-        const u32x4 raw = *(const u32x4*)(X + (size_t)t * K + col0);
+      // kLoadBatch rows are loaded before any is added, so a wave keeps that many 1 KiB
+      // reads in flight (one at a time leaves a short split waiting out each round trip).
+      // Rows past the split's end load as zeros, which change no statistic: |0| adds
+      // nothing to a sum or a sum of squares and never exceeds a running max.
+      const uint16_t* xc = X + col0;
+      for (int t = t0 + lt; t < t1; t += kLoadBatch * kTokenLanes) {
+        u32x4 raw[kLoadBatch];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          add(2 * jj, h2f((uint16_t)(raw[jj] & 0xffffu)));
-          add(2 * jj + 1, h2f((uint16_t)(raw[jj] >> 16)));
+        for (int u = 0; u < kLoadBatch; ++u) {
+          const int tt = t + u * kTokenLanes;
+          raw[u] = tt < t1 ? *(const u32x4*)(xc + (size_t)tt * K) : u32x4{0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            add(2 * jj, h2f((uint16_t)(raw[u][jj] & 0xffffu)));
+            add(2 * jj + 1, h2f((uint16_t)(raw[u][jj] >> 16)));
+          }
       }
     }
   } else {
@@ -169,24 +188,35 @@ __global__ __launch_bounds__(kThreads) void k_act_stats_finalize(const double* _
   }
 }
 
-// Pass 2 (EMA): per channel, batch sums (pieces added in order) -> batch mean ->
-// e = momentum * e + (1 - momentum) * mean, from e = 0, over the batches in order.
+// Pass 2 (EMA): per channel, batch sums -> batch mean -> e = momentum * e + (1 - momentum) *
+// mean, from e = 0, over the batches in order.  A wave covers 16 channels with 4 lanes
+// each: lane slot q sums the batch's pieces q, q + 4, ..., and the four slots are added
+// across lanes.  The pieces are exact fp64 sums of fp16 magnitudes (while a batch's sum
+// stays below 2^29), so any order of these additions gives the same batch sum; every lane
+// of a channel then runs the same recurrence and slot 0 writes the result.
+constexpr int kEmaSlots = 4;
+constexpr int kEmaChannelsPerBlock = kThreads / kEmaSlots;
 __global__ __launch_bounds__(kThreads) void k_act_stats_ema(const double* __restrict__ part,
                                                             int n_batches, int sub, int N, int B,
                                                             int K, double momentum,
                                                             float* __restrict__ a) {
-  const int i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= K) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4;  // slot 0..3
+  const int i = blockIdx.x * kEmaChannelsPerBlock + wave * 16 + (lane & 15);
+  const bool ok = i < K;
   const double keep = 1.0 - momentum;
   double e = 0.0;
   for (int b = 0; b < n_batches; ++b) {
     double sum = 0.0;
-    for (int j = 0; j < sub; ++j) sum += part[(size_t)(b * sub + j) * K + i];
+    if (ok)
+      for (int j = q; j < sub; j += kEmaSlots) sum += part[(size_t)(b * sub + j) * K + i];
+    sum += __shfl_xor(sum, 16);
+    sum += __shfl_xor(sum, 32);
     const int cnt = (int)min((long long)B, (long long)N - (long long)b * B);
     const double m = sum / (double)cnt;
     e = momentum * e + keep * m;
   }
-  a[i] = (float)e;
+  if (ok && q == 0) a[i] = (float)e;
 }
 
 }  // namespace
@@ -245,7 +275,8 @@ static hipError_t launch_stats_mode(const uint16_t* X, int N, int K, const Stats
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   if constexpr (MODE == kStatEmaMean) {
-    hipLaunchKernelGGL(k_act_stats_ema, dim3((K + kThreads - 1) / kThreads), dim3(kThreads), 0,
+    hipLaunchKernelGGL(k_act_stats_ema,
+                       dim3((K + kEmaChannelsPerBlock - 1) / kEmaChannelsPerBlock), dim3(kThreads), 0,
                        stream, partials, p.n_batches, p.sub, N, p.B, K, momentum, a_out);
   } else {
     hipLaunchKernelGGL(k_act_stats_finalize<MODE>, dim3((K + kChunkLanes - 1) / kChunkLanes),

@@ -34,13 +34,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #ifndef AWQ_GEMV_RB
-#define AWQ_GEMV_RB 4  // rows whose code loads are in flight together (256-thread blocks)
+#define AWQ_GEMV_RB 2  // rows whose code loads are in flight together (256-thread blocks)
 #endif
 #ifndef AWQ_GEMV_TARGET_WAVES
 #define AWQ_GEMV_TARGET_WAVES 4096  // waves the row split aims for
 #endif
 #ifndef AWQ_GEMV_MAX_ROWS
 #define AWQ_GEMV_MAX_ROWS 64
+#endif
+#ifndef AWQ_GEMV_MIN_ROWS
+// rows per block at least (a multiple of the row batch).  Same-box graph replays, one
+// token, S^-1 folded / s given: 4096 x 4096 6.3 / 8.3 us against 6.7 / 8.7 for 8 rows and
+// batches of 4; 28672 x 8192 28.1 / 32.9 against 30.3 / 35.4; 11008 x 4096 9.1 / 15.1
+// against 9.4 / 13.5
+#define AWQ_GEMV_MIN_ROWS 4
 #endif
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
@@ -203,14 +210,14 @@ __global__ __launch_bounds__(MAXT) void k_w4a16_gemv(const uint8_t* __restrict__
 }
 
 // Rows per block for T tokens: the plan's count, cut so that the LDS partials
-// (K/32 chunks x (rows*T + 1) floats) stay within kGemvLdsFloats; at least 8.
+// (K/32 chunks x (rows*T + 1) floats) stay within kGemvLdsFloats; at least AWQ_GEMV_MIN_ROWS.
 constexpr int kGemvLdsFloats = 24576;  // 96 KiB
 int gemv_rows(const GemvPlan& p, int T, int K) {
   const int nchunks = K / 32 > 0 ? K / 32 : 1;
   int cap = (kGemvLdsFloats / nchunks - 1) / T;
-  cap = (cap / 8) * 8;
+  cap = (cap / AWQ_GEMV_MIN_ROWS) * AWQ_GEMV_MIN_ROWS;
   int rows = p.rows < cap ? p.rows : cap;
-  return rows < 8 ? 8 : rows;
+  return rows < AWQ_GEMV_MIN_ROWS ? AWQ_GEMV_MIN_ROWS : rows;
 }
 
 template <int T, int MAXT, int RB>
@@ -475,8 +482,8 @@ GemvPlan w4a16_gemv_plan(int64_t M, int64_t K) {
   const int nwaves = p.threads / 64;
   // enough blocks to give every CU several waves; whole row batches; at most 64 rows
   int64_t rows = (M * nwaves) / AWQ_GEMV_TARGET_WAVES;
-  rows = (rows / 8) * 8;
-  if (rows < 8) rows = 8;
+  rows = (rows / AWQ_GEMV_MIN_ROWS) * AWQ_GEMV_MIN_ROWS;
+  if (rows < AWQ_GEMV_MIN_ROWS) rows = AWQ_GEMV_MIN_ROWS;
   if (rows > AWQ_GEMV_MAX_ROWS) rows = AWQ_GEMV_MAX_ROWS;
   p.rows = (int)rows;
   return p;
