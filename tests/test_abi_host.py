@@ -106,22 +106,27 @@ def test_workspace_query(L):
     assert one == fixed + M * K * 2
     assert full == fixed + 20 * M * K * 2
     assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 7) == fixed + 7 * M * K * 2
-    # the G form: tiles over K, then X^T (fp16 [K][N]; one token split, so no partials),
-    # fp32 G, fp16 G', fp32 diagonal, the maxima of the 136 tiles of G's upper block
-    # triangle, and the exponent, each 256-byte aligned
+    # the G form: tiles over K, then X^T (fp16 [K][N]), the fp32 split partials of the 136
+    # tiles of G's upper block triangle, fp16 G', fp32 diagonal, the partials' tile maxima,
+    # and the exponent, each 256-byte aligned.  The 4096 tokens go in two splits (2752 and
+    # 1344): on 136 tiles one split leaves 120 of 256 compute units idle, and with two
+    # uneven splits the short blocks run on the units the long ones leave free.
     N = 4096
     assert awq.awq_loss_form(M, K, N, 20) == awq.AWQ_LOSS_GRAM
     tiles = (M // 256) * (K // 256)
-    fixed = (20 * K * 4 + 20 * tiles * 8 + K * N * 2 + K * K * 4 + K * K * 2 + K * 4 + 768
-             + 256)
+    splits = 2
+    fixed = (20 * K * 4 + 20 * tiles * 8 + K * N * 2 + splits * 136 * 256 * 256 * 4 + K * K * 2
+             + K * 4 + 1280 + 256)
     assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 1) == fixed + M * K * 2
     assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 0) == fixed + 20 * M * K * 2
-    # more tokens than one split (8192) holds: fp32 partial tiles per split besides
+    # more tokens than one split (8192) holds: at least three splits; the plan takes four
+    # (three of 5760 tokens and one of 2720: the busiest compute unit then runs 11520
+    # tokens' worth of tiles, against 13440 with three equal splits)
     N = 20000
     ld = 20000                                    # already a multiple of 8
-    splits, pairs = 3, 136
+    splits, pairs = 4, 136
     fixed = (20 * K * 4 + 20 * tiles * 8 + K * ld * 2 + splits * pairs * 256 * 256 * 4
-             + K * K * 4 + K * K * 2 + K * 4 + ((4 * pairs * 4 + 255) // 256) * 256 + 256)
+             + K * K * 2 + K * 4 + ((splits * pairs * 4 + 255) // 256) * 256 + 256)
     assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 1) == fixed + M * K * 2
     assert awq.awq_workspace_bytes(M, K, N, cfg, 0, 0) == 0
     assert awq.awq_workspace_bytes(M, 100, N, cfg, 20, 0) == 0
@@ -184,11 +189,12 @@ def test_loss_form_choice():
         assert q(*bad) == -1
     # in_features beyond 2^22: the search rejects the shape
     assert awq.awq_workspace_bytes(1, 1 << 23, 16, awq.qconfig(4, 128, 1), 20, 0) == 0
-    # the choice agrees with the workspace: the G form holds G (fp32 and fp16) besides dW
+    # the choice agrees with the workspace: the G form holds X^T, G' (fp16) and at least one
+    # fp32 partial of G's upper block triangle (136 tiles of 256 x 256) besides dW
     cfg = awq.qconfig(4, 128, 1)
     direct = awq.awq_workspace_bytes(4096, 4096, 1024, cfg, 20, 0)
     gram = awq.awq_workspace_bytes(4096, 4096, 4096, cfg, 20, 0)
-    assert gram - direct >= 4096 * 4096 * 6
+    assert gram - direct >= 4096 * 4096 * 2 * 2 + 136 * 256 * 256 * 4
 
 
 def test_profile_hook_set_and_clear(L):

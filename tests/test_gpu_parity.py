@@ -299,7 +299,7 @@ SEARCH_CASES = [
     (100, 96, 3000, 3, 32, 1),      # 96 channels: partial transpose and G tiles
     (300, 448, 2000, 4, 64, 1),     # last diagonal block of 192 channels: its upper half partial
     (257, 704, 1500, 3, 32, 0),     # three tile rows, the last one 192 channels
-    (200, 256, 20003, 4, 64, 1),    # three token splits of G, the last one ragged
+    (200, 256, 20003, 4, 64, 1),    # several token splits of G, the last one ragged
 ]
 
 

@@ -56,11 +56,11 @@ int device_ptr(const void* p) {
   return AWQ_E_DEVICE;
 }
 
-// Workspace of the search: s table | loss partials | (Gram form: X^T, split partials,
-// fp32 G, fp16 G', fp32 diagonal, tile maxima, exponent) | dW batch.
+// Workspace of the search: s table | loss partials | (Gram form: X^T, split partials of
+// G's upper block triangle, fp16 G', fp32 diagonal, tile maxima, exponent) | dW batch.
 struct SearchLayout {
   size_t s_off, p_off, dw_off;
-  size_t xt_off, gpart_off, g32_off, gh_off, gdiag_off, tmax_off, gexp_off;
+  size_t xt_off, gpart_off, gh_off, gdiag_off, tmax_off, gexp_off;
   size_t dw_bytes_per_alpha;
   int64_t tiles;
   bool gram;
@@ -74,18 +74,15 @@ SearchLayout search_layout(int64_t M, int64_t K, int64_t N, int32_t n_alpha) {
   L.s_off = 0;
   L.p_off = round_up((size_t)n_alpha * (size_t)K * sizeof(float), kAlign);
   size_t off = L.p_off + round_up((size_t)n_alpha * (size_t)L.tiles * sizeof(double), kAlign);
-  L.xt_off = L.gpart_off = L.g32_off = L.gh_off = L.gdiag_off = L.tmax_off = L.gexp_off = off;
+  L.xt_off = L.gpart_off = L.gh_off = L.gdiag_off = L.tmax_off = L.gexp_off = off;
   if (L.gram) {
     const size_t kk = (size_t)K * (size_t)K;
     const awq::GramPlan g = awq::gram_plan(N, K);
     L.xt_off = off;
     off += round_up((size_t)K * (size_t)g.ld * sizeof(uint16_t), kAlign);
     L.gpart_off = off;
-    if (g.splits > 1)
-      off += round_up((size_t)g.splits * (size_t)g.pairs * awq::kLossBM * awq::kLossBN * sizeof(float),
-                      kAlign);
-    L.g32_off = off;
-    off += round_up(kk * sizeof(float), kAlign);
+    off += round_up((size_t)g.splits * (size_t)g.pairs * awq::kLossBM * awq::kLossBN * sizeof(float),
+                    kAlign);
     L.gh_off = off;
     off += round_up(kk * sizeof(uint16_t), kAlign);
     L.gdiag_off = off;
@@ -154,7 +151,7 @@ int run_search(const void* W, const void* X, const float* s_table, int64_t M, in
       if ((st = record(hook.gram_start, sm))) return st;
       st = hip_status(awq::launch_gram_full((const uint16_t*)X, (int)N, (int)K,
                                             (uint16_t*)(ws + L.xt_off),
-                                            (float*)(ws + L.gpart_off), (float*)(ws + L.g32_off),
+                                            (float*)(ws + L.gpart_off),
                                             (float*)(ws + L.tmax_off), Gh, gdiag, gexp, sm));
       if (st) return st;
       if ((st = record(hook.gram_stop, sm))) return st;

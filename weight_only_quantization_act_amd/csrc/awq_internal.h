@@ -129,22 +129,24 @@ hipError_t launch_fold_inverse_scales(const uint16_t* x, const float* s, int T, 
 // partials[k * tiles + tm * tiles_n + tn] = sum over the tile of (dW_k X^T)^2.
 hipError_t launch_loss_gemm(const uint16_t* dW, const uint16_t* X, int M, int N, int K,
                             int nb, double* partials, hipStream_t stream);
-// The G form's Gram pass (loss_gram.hip): Xt = X^T (fp16 [K][ld]) | split partials
-// (fp32 [splits][pairs][kLossBM][kLossBN], only with more than one split) | fp32 G [K][K]
-// (upper block triangle) | tile maxima tmax [tmax] are scratch; outputs Gh = G' 2^-gexp
-// (fp16 [K][K]; G with the kLossBN blocks above its diagonal doubled, those below and the
-// diagonal zero), gdiag = diag(G) 2^-gexp (fp32 [K]) and gexp.  Tokens are split in runs of
-// kGramSplitTokens, each summed in fp32 on the matrix cores; K a multiple of 8.
+// The G form's Gram pass (loss_gram.hip): Xt = X^T (fp16 [K][ld]) | split partials of G's
+// upper block triangle (fp32 [splits][pairs][kLossBM][kLossBN]) | their tile maxima
+// tmax [splits][pairs] are scratch; outputs Gh = G' 2^-gexp (fp16 [K][K]; G with the
+// kLossBN blocks above its diagonal doubled, the diagonal zero, the blocks below it not
+// written), gdiag = diag(G) 2^-gexp (fp32 [K]) and gexp.  Tokens are split in runs of
+// kchunk <= kGramSplitTokens (gram_split_tokens), each summed in fp32 on the matrix cores;
+// K a multiple of 8.
 constexpr int kGramSplitTokens = 8192;
 struct GramPlan {
-  int64_t ld, splits, pairs, tmax;
+  int64_t ld, kchunk, splits, pairs, tmax;
 };
+int64_t gram_split_tokens(int64_t N, int64_t pairs);
 GramPlan gram_plan(int64_t N, int64_t K);
 hipError_t launch_gram_full(const uint16_t* X, int N, int K, uint16_t* Xt, float* part,
-                            float* G, float* tmax, uint16_t* Gh, float* gdiag, int32_t* gexp,
+                            float* tmax, uint16_t* Gh, float* gdiag, int32_t* gexp,
                             hipStream_t stream);
 // G build mode of the loss kernel (loss_gemm.hip): tiles tm <= tn of G over splits of
-// kchunk tokens from Xt [K][ld]; out = G (one split, with tmax [pairs]) or the partials.
+// kchunk tokens from Xt [K][ld]; out = the split partials, tmax [splits][pairs].
 hipError_t launch_gram_build(const uint16_t* Xt, int N, int ld, int K, int kchunk, int splits,
                              float* out, float* tmax, hipStream_t stream);
 // partials as launch_loss_gemm (loss_tiles_m(M) x loss_tiles_n(K) tiles per grid point),

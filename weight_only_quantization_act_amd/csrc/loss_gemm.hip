@@ -175,9 +175,9 @@ struct Stage {
 // MODE kModeGramBuild (BUILD below): G = X^T X itself from Xt = X^T (fp16 [K][ld], tokens
 // contiguous, passed as X): the A and B sides are both channels, the reduction runs over
 // the tokens [s kchunk, min(N, (s + 1) kchunk)) of split s (passed as the grid point), and
-// only tiles tm <= tn of G's upper block triangle are formed.  With one split the fp32
-// tile goes to gout = G (fp32 [K][K], upper block triangle only) and its largest |entry|
-// to tmax[pair]; with several, to gout = partial tiles [split][pair][BM][BN].
+// only tiles tm <= tn of G's upper block triangle are formed.  Each split's fp32 tile goes
+// to gout = partial tiles [split][pair][BM][BN] and its largest |entry| to
+// tmax[split][pair].
 constexpr int kModeDirect = 0, kModeGramLoss = 1, kModeGramBuild = 2;
 template <class S, int MODE>
 __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
@@ -218,16 +218,21 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   // and tiles_m - 1 - tm (tiles_m + 1 blocks of G' between them): equal work per block.
   // BUILD: grid point = token split, and a block's tile is the rem-th pair tm <= tn of
   // the upper block triangle in row-major order.
+  // BUILD: the splits are dispatched in order (all blocks of split 0 first), and within a
+  // split each XCD takes a contiguous run of pairs; XCDs take blocks round-robin, so every
+  // XCD starts on the longer splits and gets an even share of each split.
   const int tm_count = GRAM ? (tiles_m + 1) / 2 : tiles_m;
   const int per_alpha = BUILD ? tiles_m * (tiles_m + 1) / 2 : tm_count * tiles_n;
-  const int total = nb * per_alpha;
   const int b = blockIdx.x;
-  const int xcd = b & 7;
-  const int local = b >> 3;
+  const int split_b = BUILD ? b / per_alpha : 0;
+  const int bb = b - split_b * per_alpha;
+  const int total = BUILD ? per_alpha : nb * per_alpha;
+  const int xcd = bb & 7;
+  const int local = bb >> 3;
   const int q = total >> 3, r = total & 7;
   const int logical = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-  const int kk_alpha = logical / per_alpha;
-  const int rem = logical - kk_alpha * per_alpha;
+  const int kk_alpha = BUILD ? split_b : logical / per_alpha;
+  const int rem = BUILD ? logical : logical - kk_alpha * per_alpha;
   int tm, tn;
   if constexpr (BUILD) {
     int t = 0, left = rem;
@@ -533,12 +538,10 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   //      dW (C + dW gdiag) at the output positions; BUILD: the tile itself); element e
   //      of a 32x32 block is row 8 (e / 4) + 4 (l / 32) + (e mod 4), column l mod 32 ----
   if constexpr (BUILD) {
-    // one split: G[a][b] (a row-contiguous 128-byte run per half-wave and e); several:
-    // the tile's partial, row-major within the tile
+    // the split's partial of the tile, row-major within the tile (a row-contiguous
+    // 128-byte run per half-wave and e); entries past in_features are not written
     const int pair = rem;
-    float* dst = nb == 1 ? gout : gout + ((size_t)kk_alpha * per_alpha + pair) * (BM * BN);
-    const int ldo = nb == 1 ? K : BN;
-    const int a_base = nb == 1 ? tm * BM : 0, b_base = nb == 1 ? tn * BN : 0;
+    float* dst = gout + ((size_t)kk_alpha * per_alpha + pair) * (BM * BN);
 #pragma unroll
     for (int mi = 0; mi < S::MI; ++mi)
 #pragma unroll
@@ -550,7 +553,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
           const int al = al0 + 8 * (e >> 2) + (e & 3);
           if (tm * BM + al < K && tn * BN + bl < K) {
             const float v = acc[mi][ni][e];
-            dst[(size_t)(a_base + al) * ldo + b_base + bl] = v;
+            dst[(size_t)al * BN + bl] = v;
             gmx = (fabsf(v) > gmx || v != v) ? fabsf(v) : gmx;
           }
         }
@@ -669,20 +672,19 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   }
   }  // part
   if constexpr (BUILD) {
-    if (nb == 1) {  // the tile's largest |G| (NaN if any entry is NaN)
+    // the largest |entry| of the split's partial tile (NaN if any entry is NaN)
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float o = __shfl_xor(gmx, off);
-        gmx = (o > gmx || o != o) ? o : gmx;
-      }
-      if (lane == 0) redf[wave] = gmx;
-      __syncthreads();
-      if (tid == 0) {
-        float m = redf[0];
+    for (int off = 32; off > 0; off >>= 1) {
+      const float o = __shfl_xor(gmx, off);
+      gmx = (o > gmx || o != o) ? o : gmx;
+    }
+    if (lane == 0) redf[wave] = gmx;
+    __syncthreads();
+    if (tid == 0) {
+      float m = redf[0];
 #pragma unroll
-        for (int w = 1; w < S::WAVES; ++w) m = (redf[w] > m || redf[w] != redf[w]) ? redf[w] : m;
-        tmax[rem] = m;
-      }
+      for (int w = 1; w < S::WAVES; ++w) m = (redf[w] > m || redf[w] != redf[w]) ? redf[w] : m;
+      tmax[(size_t)kk_alpha * per_alpha + rem] = m;
     }
     return;
   }

@@ -13,14 +13,17 @@
 //                      the padding tokens zero), so that G = Xt Xt^T is a product of two
 //                      row-contiguous operands like the loss product itself.
 //   k_loss_gemm (G build mode, loss_gemm.hip)
-//                      G's upper block triangle in 256 x 256 tiles on the matrix cores:
-//                      fp16 products (exact in fp32) summed in fp32 over one token split
-//                      of at most kGramSplitTokens tokens (at most 512 accumulator additions of
-//                      32x32x16 products, so within 2^-15 of the sum of |products|).
-//   k_gram_combine     with several splits: each entry the fp64 sum of its split partials
-//                      in split order, rounded to fp32; each quarter tile's largest |G|.
-//   k_gram_full_split  one power of two 2^-ex for the whole matrix (its largest magnitude
-//                      into [2^13, 2^14)) and the operand of the per-grid-point product:
+//                      G's upper block triangle in 256 x 256 tiles on the matrix cores,
+//                      one block per (token split, tile): fp16 products (exact in fp32)
+//                      summed in fp32 over a split of at most kGramSplitTokens tokens (at
+//                      most 512 accumulator additions of 32x32x16 products, so within
+//                      2^-15 of the sum of |products|), written as that split's partial
+//                      tile with its largest |entry|.  The split length is planned so
+//                      that the blocks fill the compute units (gram_split_tokens).
+//   k_gram_split       each entry of G the fp64 sum of its split partials in split order,
+//                      rounded to fp32; one power of two 2^-ex for the whole matrix (a
+//                      bound on its largest magnitude into [2^13, 2^14)) and the operand
+//                      of the per-grid-point product:
 //                      G' 2^-ex in fp16, where G' is G with its blocks of kLossBN x kLossBN
 //                      above the diagonal doubled (exact), those below it zero and its
 //                      diagonal zero; each diagonal block has the same structure at half
@@ -38,6 +41,11 @@
 
 #include <math.h>
 
+#include <functional>
+#include <mutex>
+#include <queue>
+#include <vector>
+
 #include "awq_internal.h"
 #include "quantizer.h"
 
@@ -45,13 +53,8 @@ namespace awq {
 
 namespace {
 
-constexpr int kGfSplitChunk = 4096;  // entries per block of the split pass
 constexpr int kTrTile = 64;          // tokens and channels of a transpose tile
-constexpr int kCombineRows = 64;     // tile rows per block of the combine pass
-
-__device__ __forceinline__ float nan_maxf(float m, float a) {
-  return (a > m || a != a) ? a : m;
-}
+constexpr int kSplitRows = 64;       // tile rows per block of the split pass
 
 // Block (bx, by): tokens [64 bx, 64 bx + 64) x channels [64 by, 64 by + 64).  Loads are
 // 16-byte runs of 8 channels of one token, stores 16-byte runs of 8 tokens of one channel;
@@ -93,117 +96,187 @@ __global__ __launch_bounds__(256) void k_transpose_x(const uint16_t* __restrict_
   }
 }
 
-// Block (quarter q of pair p): rows [64 q, 64 q + 64) of tile pair p = (tm, tn): each entry
-// the fp64 sum over splits of the partial tiles [split][pair][256][256] in split order,
-// rounded to fp32, written to G; the quarter's largest |entry| to tmax[4 p + q].
-__global__ __launch_bounds__(256) void k_gram_combine(const float* __restrict__ part,
-                                                      int splits, int npairs, int T, int K,
-                                                      float* __restrict__ G,
-                                                      float* __restrict__ tmax) {
-  __shared__ float wm[4];
-  const int p = blockIdx.x >> 2, qr = blockIdx.x & 3;
-  int tm = 0, left = p;
-  while (left >= T - tm) {
-    left -= T - tm;
-    ++tm;
+// The tile pair p of G's upper block triangle in row-major order: (tm, tn), tm <= tn.
+__device__ __forceinline__ void pair_tiles(int p, int T, int& tm, int& tn) {
+  int t = 0, left = p;
+  while (left >= T - t) {
+    left -= T - t;
+    ++t;
   }
-  const int tn = tm + left;
-  const int tid = threadIdx.x;
-  const int col = tn * kLossBN + tid;
-  float mx = 0.0f;
-  for (int rr = 0; rr < kCombineRows; ++rr) {
-    const int rl = qr * kCombineRows + rr;
-    const int row = tm * kLossBM + rl;
-    if (row >= K || col >= K) continue;
-    double acc = 0.0;
-    for (int sp = 0; sp < splits; ++sp)
-      acc += (double)part[(((size_t)sp * npairs + p) * kLossBM + rl) * kLossBN + tid];
-    const float v = (float)acc;
-    G[(size_t)row * K + col] = v;
-    mx = nan_maxf(mx, fabsf(v));
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = nan_maxf(mx, __shfl_xor(mx, o));
-  if ((tid & 63) == 0) wm[tid >> 6] = mx;
-  __syncthreads();
-  if (tid == 0) tmax[blockIdx.x] = nan_maxf(nan_maxf(wm[0], wm[1]), nan_maxf(wm[2], wm[3]));
+  tm = t;
+  tn = t + left;
 }
 
-// Block c: entries [c chunk, (c + 1) chunk) of G (K x K), eight consecutive entries of one
-// row a thread (K is a multiple of 8).  Every block derives the same exponent from all tile
-// maxima (NaN if any entry is NaN: then ex = 0 and the NaN reaches the losses); block 0
-// publishes it.  Runs in the blocks below the diagonal are skipped: the product never reads
-// them (a tile row of channels runs over k from its own diagonal block on), so G' there is
-// left unwritten.
-__global__ __launch_bounds__(256) void k_gram_full_split(const float* __restrict__ G, int K,
-                                                         int64_t KK,
-                                                         const float* __restrict__ tmax,
-                                                         int ntiles, uint16_t* __restrict__ Gh,
-                                                         float* __restrict__ gdiag,
-                                                         int32_t* __restrict__ gexp) {
-  __shared__ float red[4];
+// Block (quarter q of pair p): rows [64 q, 64 q + 64) of tile pair p = (tm, tn); a thread
+// takes eight consecutive columns of one row at a time (32 threads a row, 8 rows a pass).
+// Each entry of G is the fp64 sum of the split partials [split][pair][256][256] in split
+// order, rounded to fp32 (one split: the partial itself).  One power of two 2^-ex serves
+// the whole matrix: every block derives it from the tile maxima of the partials (the sum
+// over splits of a tile's largest |partial| bounds its largest |G|; NaN if any entry is
+// NaN, and then ex = 0 and the NaN reaches the losses).  Then G' 2^-ex goes to Gh (fp16,
+// row-major [K][K]) and diag(G) 2^-ex to gdiag (fp32); block 0 publishes ex.  Blocks
+// below the diagonal are not formed: the product never reads them.
+__global__ __launch_bounds__(256) void k_gram_split(const float* __restrict__ part, int splits,
+                                                    int npairs, int T, int K,
+                                                    const float* __restrict__ tmax,
+                                                    uint16_t* __restrict__ Gh,
+                                                    float* __restrict__ gdiag,
+                                                    int32_t* __restrict__ gexp) {
+  __shared__ double red[4];
   const int tid = threadIdx.x;
-  float m = 0.0f;
-  for (int i = tid; i < ntiles; i += 256) m = nan_maxf(m, tmax[i]);
+  double m = 0.0;
+  for (int p = tid; p < npairs; p += 256) {
+    double ub = 0.0;
+    for (int sp = 0; sp < splits; ++sp) ub += (double)tmax[(size_t)sp * npairs + p];
+    m = (ub > m || ub != ub) ? ub : m;
+  }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = nan_maxf(m, __shfl_xor(m, o));
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double v = __shfl_xor(m, o);
+    m = (v > m || v != v) ? v : m;
+  }
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
-  m = nan_maxf(nan_maxf(red[0], red[1]), nan_maxf(red[2], red[3]));
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) m = (red[w] > m || red[w] != red[w]) ? red[w] : m;
   int ex = 0;
-  if (m > 0.0f && m < INFINITY) {
+  if (m > 0.0 && m < INFINITY) {
     int e2;
-    frexpf(m, &e2);  // m = f 2^e2, f in [0.5, 1)
-    ex = e2 - 14;    // m 2^-ex in [2^13, 2^14)
+    frexp(m, &e2);  // m = f 2^e2, f in [0.5, 1)
+    ex = e2 - 14;   // m 2^-ex in [2^13, 2^14)
   }
   if (blockIdx.x == 0 && tid == 0) gexp[0] = ex;
-  const int64_t base = (int64_t)blockIdx.x * kGfSplitChunk;
+
+  const int p = blockIdx.x >> 2, qr = blockIdx.x & 3;
+  int tm, tn;
+  pair_tiles(p, T, tm, tn);
+  const int cl = (tid & 31) * 8;
+  const int col0 = tn * kLossBN + cl;
+  if (col0 >= K) return;  // K is a multiple of 8, so a run is wholly in or out
+  const size_t split_stride = (size_t)npairs * kLossBM * kLossBN;
+  const float* src = part + (size_t)p * kLossBM * kLossBN + cl;
+  for (int it = 0; it < kSplitRows / 8; ++it) {
+    const int rl = qr * kSplitRows + it * 8 + (tid >> 5);
+    const int row = tm * kLossBM + rl;
+    if (row >= K) break;
+    double acc[8];
 #pragma unroll
-  for (int run = 0; run < kGfSplitChunk / (256 * 8); ++run) {
-    const int64_t j0 = base + (int64_t)(run * 256 + tid) * 8;
-    if (j0 >= KK) break;
-    const int64_t row = j0 / K, col0 = j0 - (j0 / K) * K;
-    const int64_t ra = row / kLossBN, cb = col0 / kLossBN;
-    if (cb < ra) continue;
-    const float4 g0 = *(const float4*)(G + j0), g1 = *(const float4*)(G + j0 + 4);
-    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    // inside a diagonal block, the same at half size: its upper-right half block doubled,
-    // its lower-left half zero (so the product's waves holding a tile's upper 128
-    // channels start at the half block's diagonal)
-    const int64_t hr = (row % kLossBN) / (kLossBN / 2), hc = (col0 % kLossBN) / (kLossBN / 2);
-    const float f = (cb > ra || hc > hr) ? 2.0f : (hc < hr ? 0.0f : 1.0f);  // exact
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+    for (int sp = 0; sp < splits; ++sp) {
+      const float* q = src + sp * split_stride + (size_t)rl * kLossBN;
+      const float4 a = *(const float4*)q, b = *(const float4*)(q + 4);
+      acc[0] += (double)a.x; acc[1] += (double)a.y; acc[2] += (double)a.z; acc[3] += (double)a.w;
+      acc[4] += (double)b.x; acc[5] += (double)b.y; acc[6] += (double)b.z; acc[7] += (double)b.w;
+    }
+    // G' = G with the blocks above the diagonal doubled; inside a diagonal block the same
+    // at half size: its upper-right half block doubled, its lower-left half zero (so the
+    // product's waves holding a tile's upper 128 channels start at the half block's
+    // diagonal); the diagonal itself zero, kept in fp32 apart
+    const int hr = rl / (kLossBN / 2), hc = cl / (kLossBN / 2);
+    const float f = (tn > tm || hc > hr) ? 2.0f : (hc < hr ? 0.0f : 1.0f);  // exact
     uint32_t h[4];
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
-      uint16_t lo = f2h(ldexpf(f * g[i], -ex)), hi = f2h(ldexpf(f * g[i + 1], -ex));
+      const float g0 = (float)acc[i], g1 = (float)acc[i + 1];
+      uint16_t lo = f2h(ldexpf(f * g0, -ex)), hi = f2h(ldexpf(f * g1, -ex));
       if (col0 + i == row) {
-        gdiag[row] = ldexpf(g[i], -ex);
+        gdiag[row] = ldexpf(g0, -ex);
         lo = 0;
       }
       if (col0 + i + 1 == row) {
-        gdiag[row] = ldexpf(g[i + 1], -ex);
+        gdiag[row] = ldexpf(g1, -ex);
         hi = 0;
       }
       h[i >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
     }
-    *(uint4*)(Gh + j0) = make_uint4(h[0], h[1], h[2], h[3]);
+    *(uint4*)(Gh + (size_t)row * K + col0) = make_uint4(h[0], h[1], h[2], h[3]);
   }
 }
 
 }  // namespace
 
+// Tokens per split.  A block of the build runs one tile over one split; the blocks go out
+// split by split, round-robin over the 8 XCDs, each XCD filling its 32 compute units as
+// they free up.  Candidates: s splits for s from the fewest that keep every split within
+// kGramSplitTokens to 6 more, the last split a whole, 2/3, 1/2 or 1/3 share of the others
+// (so that the short blocks fill the units the long ones leave idle).  Each is priced by
+// list-scheduling the busiest XCD's blocks in that order (its longest unit, in block-time
+// per token) plus the partial tiles written and read back (about 4.3 token-times per
+// 256 x 256 fp32 tile: 512 KiB of traffic at about 5 TB/s against about 0.024 us a token
+// for a block).  The cheapest wins; ties keep fewer splits.  The host computes this once
+// per (tokens, tile pairs) and keeps the last few answers.
+static int64_t gram_split_tokens_uncached(int64_t N, int64_t pairs) {
+  constexpr int kUnits = 32;
+  constexpr double kTileCost = 4.3;
+  const int64_t cap = kGramSplitTokens;
+  const int64_t s_min = (N + cap - 1) / cap;
+  const int64_t per_xcd = (pairs + 7) / 8;
+  int64_t best_k = N < cap ? ((N + 63) / 64) * 64 : cap;
+  double best = -1.0;
+  for (int64_t sp = s_min; sp <= s_min + 6; ++sp) {
+    for (const int sixths : {6, 4, 3, 2}) {
+      if (sp == 1 && sixths != 6) continue;
+      int64_t k = (6 * N + 6 * (sp - 1) + sixths - 1) / (6 * (sp - 1) + sixths);
+      k = ((k + 63) / 64) * 64;
+      if (k > cap) k = cap;
+      const int64_t splits = (N + k - 1) / k;
+      const int64_t last = N - (splits - 1) * k;
+      // the units' busy times as a min-heap: each block goes to the first unit free
+      std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> busy;
+      for (int v = 0; v < kUnits; ++v) busy.push(0);
+      int64_t span = 0;
+      for (int64_t jj = 0; jj < splits; ++jj) {
+        const int64_t len = jj + 1 == splits ? last : k;
+        for (int64_t b = 0; b < per_xcd; ++b) {
+          const int64_t t = busy.top() + len;
+          busy.pop();
+          busy.push(t);
+          span = t > span ? t : span;
+        }
+      }
+      const double cost = (double)span + kTileCost * (double)(splits * pairs);
+      if (best < 0.0 || cost < best) {
+        best = cost;
+        best_k = k;
+      }
+    }
+  }
+  return best_k;
+}
+
+int64_t gram_split_tokens(int64_t N, int64_t pairs) {
+  struct Entry {
+    int64_t n, pairs, k;
+  };
+  static std::mutex mu;
+  static Entry cache[8] = {};
+  static int next = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& e : cache)
+      if (e.k > 0 && e.n == N && e.pairs == pairs) return e.k;
+  }
+  const int64_t k = gram_split_tokens_uncached(N, pairs);
+  std::lock_guard<std::mutex> lock(mu);
+  cache[next] = Entry{N, pairs, k};
+  next = (next + 1) % 8;
+  return k;
+}
+
 GramPlan gram_plan(int64_t N, int64_t K) {
   GramPlan g;
   g.ld = (N + 7) / 8 * 8;
-  g.splits = (N + kGramSplitTokens - 1) / kGramSplitTokens;
   const int64_t T = loss_tiles_m(K);
   g.pairs = T * (T + 1) / 2;
-  g.tmax = g.splits > 1 ? 4 * g.pairs : g.pairs;
+  g.kchunk = N > 0 ? gram_split_tokens(N, g.pairs) : 64;
+  g.splits = N > 0 ? (N + g.kchunk - 1) / g.kchunk : 1;
+  g.tmax = g.splits * g.pairs;
   return g;
 }
 
 hipError_t launch_gram_full(const uint16_t* X, int N, int K, uint16_t* Xt, float* part,
-                            float* G, float* tmax, uint16_t* Gh, float* gdiag, int32_t* gexp,
+                            float* tmax, uint16_t* Gh, float* gdiag, int32_t* gexp,
                             hipStream_t stream) {
   if (K <= 0) return hipSuccess;
   if (K % 8 != 0 || N <= 0) return hipErrorInvalidValue;
@@ -213,20 +286,11 @@ hipError_t launch_gram_full(const uint16_t* X, int N, int K, uint16_t* Xt, float
                      dim3(256), 0, stream, X, N, K, (int)g.ld, Xt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_gram_build(Xt, N, (int)g.ld, K, kGramSplitTokens, (int)g.splits, g.splits > 1 ? part : G,
-                        tmax, stream);
+  e = launch_gram_build(Xt, N, (int)g.ld, K, (int)g.kchunk, (int)g.splits, part, tmax, stream);
   if (e != hipSuccess) return e;
-  if (g.splits > 1) {
-    const int T = (int)loss_tiles_m(K);
-    hipLaunchKernelGGL(k_gram_combine, dim3((unsigned)(4 * g.pairs)), dim3(256), 0, stream, part,
-                       (int)g.splits, (int)g.pairs, T, K, G, tmax);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int64_t KK = (int64_t)K * K;
-  const int64_t blocks = (KK + kGfSplitChunk - 1) / kGfSplitChunk;
-  hipLaunchKernelGGL(k_gram_full_split, dim3((unsigned)blocks), dim3(256), 0, stream, G, K, KK,
-                     tmax, (int)g.tmax, Gh, gdiag, gexp);
+  const int T = (int)loss_tiles_m(K);
+  hipLaunchKernelGGL(k_gram_split, dim3((unsigned)(4 * g.pairs)), dim3(256), 0, stream, part,
+                     (int)g.splits, (int)g.pairs, T, K, tmax, Gh, gdiag, gexp);
   return hipGetLastError();
 }
 
