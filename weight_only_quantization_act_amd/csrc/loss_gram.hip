@@ -20,7 +20,8 @@
 //                      2^-15 of the sum of |products|), written as that split's partial
 //                      tile with its largest |entry|.  The split length is planned so
 //                      that the blocks fill the compute units (gram_split_tokens).
-//   k_gram_split       each entry of G the fp64 sum of its split partials in split order,
+//   k_gram_combine_split
+//                      each entry of G the fp64 sum of its split partials in split order,
 //                      rounded to fp32; one power of two 2^-ex for the whole matrix (a
 //                      bound on its largest magnitude into [2^13, 2^14)) and the operand
 //                      of the per-grid-point product:
@@ -116,12 +117,10 @@ __device__ __forceinline__ void pair_tiles(int p, int T, int& tm, int& tn) {
 // NaN, and then ex = 0 and the NaN reaches the losses).  Then G' 2^-ex goes to Gh (fp16,
 // row-major [K][K]) and diag(G) 2^-ex to gdiag (fp32); block 0 publishes ex.  Blocks
 // below the diagonal are not formed: the product never reads them.
-__global__ __launch_bounds__(256) void k_gram_split(const float* __restrict__ part, int splits,
-                                                    int npairs, int T, int K,
-                                                    const float* __restrict__ tmax,
-                                                    uint16_t* __restrict__ Gh,
-                                                    float* __restrict__ gdiag,
-                                                    int32_t* __restrict__ gexp) {
+__global__ __launch_bounds__(256) void k_gram_combine_split(
+    const float* __restrict__ part, int splits, int npairs, int T, int K,
+    const float* __restrict__ tmax, uint16_t* __restrict__ Gh, float* __restrict__ gdiag,
+    int32_t* __restrict__ gexp) {
   __shared__ double red[4];
   const int tid = threadIdx.x;
   double m = 0.0;
@@ -289,8 +288,8 @@ hipError_t launch_gram_full(const uint16_t* X, int N, int K, uint16_t* Xt, float
   e = launch_gram_build(Xt, N, (int)g.ld, K, (int)g.kchunk, (int)g.splits, part, tmax, stream);
   if (e != hipSuccess) return e;
   const int T = (int)loss_tiles_m(K);
-  hipLaunchKernelGGL(k_gram_split, dim3((unsigned)(4 * g.pairs)), dim3(256), 0, stream, part,
-                     (int)g.splits, (int)g.pairs, T, K, tmax, Gh, gdiag, gexp);
+  hipLaunchKernelGGL(k_gram_combine_split, dim3((unsigned)(4 * g.pairs)), dim3(256), 0, stream,
+                     part, (int)g.splits, (int)g.pairs, T, K, tmax, Gh, gdiag, gexp);
   return hipGetLastError();
 }
 
