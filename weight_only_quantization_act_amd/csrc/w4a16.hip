@@ -102,13 +102,14 @@ __device__ __forceinline__ float chunk_dot(const h2 d[16], const h2 xt[16]) {
   return acc;
 }
 
-// Codes, step and zero of RB consecutive rows for this thread's chunk.  Rows at or past
-// m_end are not loaded (their registers keep stale values and are never read).
+// Codes, step and zero (raw fp16) of RB consecutive rows for this thread's chunk.  Rows at
+// or past m_end are not loaded (their registers keep stale values and are never read).
+// Nothing here uses a loaded value (the step and zero are converted when the batch is
+// multiplied), so no wait for a row's loads is needed before the next row's are issued.
 template <int RB>
 struct RowBatch {
   u32x4 cw[RB];
-  float st[RB];
-  h2 zz[RB];
+  uint16_t st[RB], zh[RB];
 };
 
 template <int RB>
@@ -122,9 +123,8 @@ __device__ __forceinline__ void load_rows(RowBatch<RB>& b, const uint8_t* __rest
     if (has && m < m_end) {
       b.cw[r] = *(const u32x4*)(codes + (size_t)m * (K >> 1) + (size_t)tid * 16);
       const size_t gi = (size_t)m * gpr + gcol;
-      b.st[r] = h2f(scales[gi]);
-      const uint16_t zh = f2h(h2f(zeros[gi]) + 1024.0f);
-      b.zz[r] = as_h2((uint32_t)zh | ((uint32_t)zh << 16));
+      b.st[r] = scales[gi];
+      b.zh[r] = zeros[gi];
     }
   }
 }
@@ -182,11 +182,14 @@ __global__ __launch_bounds__(MAXT) void k_w4a16_gemv(const uint8_t* __restrict__
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       if (m0 + r < m_end) {
+        const uint16_t zh = f2h(h2f(b.zh[r]) + 1024.0f);
+        const h2 zz = as_h2((uint32_t)zh | ((uint32_t)zh << 16));
+        const float st = h2f(b.st[r]);
         h2 d[16];
-        chunk_delta(b.cw[r], b.zz[r], nib, one024_v, d);
+        chunk_delta(b.cw[r], zz, nib, one024_v, d);
 #pragma unroll
         for (int t = 0; t < T; ++t)
-          red[tid * rs + ((m0 - m_begin) + r) * T + t] = chunk_dot(d, xt[t]) * b.st[r];
+          red[tid * rs + ((m0 - m_begin) + r) * T + t] = chunk_dot(d, xt[t]) * st;
       }
     }
   };
