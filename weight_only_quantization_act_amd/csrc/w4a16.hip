@@ -340,14 +340,16 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void k_w4a16_mfma(
     uint32_t cw[kMfmaTiles][WPL];
     half8 bf[WPL];
   };
+  // Every lane loads (lanes past the last token read token 0 and drop it; rows past
+  // out_features read the last row and drop it), so the loads form one straight-line run
+  // and the wait for the activations before their reordering leaves the code-word loads,
+  // issued after them, in flight.
   auto load_group = [&](int j, GroupBufs& gb) {
 #pragma unroll
     for (int u = 0; u < WPL; ++u) {
-      uint32_t d0 = 0u, d1 = 0u, d2 = 0u, d3 = 0u;
-      if (tok) {
-        const u32x4 r = *(const u32x4*)(xr + (size_t)j * GS + 8 * u);
-        d0 = r[0]; d1 = r[1]; d2 = r[2]; d3 = r[3];
-      }
+      const u32x4 r = *(const u32x4*)(xr + (size_t)j * GS + 8 * u);
+      const uint32_t d0 = tok ? r[0] : 0u, d1 = tok ? r[1] : 0u, d2 = tok ? r[2] : 0u,
+                     d3 = tok ? r[3] : 0u;
       // B in code-word pair order: (c0, c4), (c1, c5), (c2, c6), (c3, c7)
       const uint32_t p0 = (d0 & 0xffffu) | (d2 << 16), p1 = (d0 >> 16) | (d2 & 0xffff0000u);
       const uint32_t p2 = (d1 & 0xffffu) | (d3 << 16), p3 = (d1 >> 16) | (d3 & 0xffff0000u);
@@ -356,21 +358,16 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void k_w4a16_mfma(
     }
 #pragma unroll
     for (int tl = 0; tl < kMfmaTiles; ++tl) {
-      const int row = m0 + 16 * tl + ar;
-      if (row < M) {
-        const uint8_t* cp = codes + (size_t)row * crow + (size_t)j * (GS / 2) + q * (GS / 8);
-        if constexpr (WPL == 4) {
-          const u32x4 r = *(const u32x4*)cp;
-          gb.cw[tl][0] = r[0]; gb.cw[tl][1] = r[1]; gb.cw[tl][2] = r[2]; gb.cw[tl][3] = r[3];
-        } else if constexpr (WPL == 2) {
-          const uint2 r = *(const uint2*)cp;
-          gb.cw[tl][0] = r.x; gb.cw[tl][1] = r.y;
-        } else {
-          gb.cw[tl][0] = *(const uint32_t*)cp;
-        }
+      const int row = min(m0 + 16 * tl + ar, M - 1);  // a row past the end: any codes, dropped
+      const uint8_t* cp = codes + (size_t)row * crow + (size_t)j * (GS / 2) + q * (GS / 8);
+      if constexpr (WPL == 4) {
+        const u32x4 r = *(const u32x4*)cp;
+        gb.cw[tl][0] = r[0]; gb.cw[tl][1] = r[1]; gb.cw[tl][2] = r[2]; gb.cw[tl][3] = r[3];
+      } else if constexpr (WPL == 2) {
+        const uint2 r = *(const uint2*)cp;
+        gb.cw[tl][0] = r.x; gb.cw[tl][1] = r.y;
       } else {
-#pragma unroll
-        for (int u = 0; u < WPL; ++u) gb.cw[tl][u] = 0x88888888u;  // any code; row dropped
+        gb.cw[tl][0] = *(const uint32_t*)cp;
       }
     }
   };
