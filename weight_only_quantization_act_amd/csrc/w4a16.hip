@@ -102,9 +102,10 @@ __device__ __forceinline__ float chunk_dot(const h2 d[16], const h2 xt[16]) {
   return acc;
 }
 
-// Codes, step and zero (raw fp16) of RB consecutive rows for this thread's chunk.  Rows at
-// or past m_end are not loaded (their registers keep stale values and are never read).
-// Nothing here uses a loaded value (the step and zero are converted when the batch is
+// Codes, step and zero (raw fp16) of RB consecutive rows for this thread's chunk.  Every
+// lane loads: rows at or past m_end read row m_end - 1 and lanes without a chunk read
+// chunk 0, values the multiply never uses.  The loads are one straight-line run and
+// nothing here uses a loaded value (the step and zero are converted when the batch is
 // multiplied), so no wait for a row's loads is needed before the next row's are issued.
 template <int RB>
 struct RowBatch {
@@ -117,15 +118,15 @@ __device__ __forceinline__ void load_rows(RowBatch<RB>& b, const uint8_t* __rest
                                           const uint16_t* __restrict__ scales,
                                           const uint16_t* __restrict__ zeros, int m0, int m_end,
                                           bool has, int tid, int K, int gpr, int gcol) {
+  const int tc = has ? tid : 0;
+  const int gc = has ? gcol : 0;
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
-    const int m = m0 + r;
-    if (has && m < m_end) {
-      b.cw[r] = *(const u32x4*)(codes + (size_t)m * (K >> 1) + (size_t)tid * 16);
-      const size_t gi = (size_t)m * gpr + gcol;
-      b.st[r] = scales[gi];
-      b.zh[r] = zeros[gi];
-    }
+    const int m = min(m0 + r, m_end - 1);
+    b.cw[r] = *(const u32x4*)(codes + (size_t)m * (K >> 1) + (size_t)tc * 16);
+    const size_t gi = (size_t)m * gpr + gc;
+    b.st[r] = scales[gi];
+    b.zh[r] = zeros[gi];
   }
 }
 
