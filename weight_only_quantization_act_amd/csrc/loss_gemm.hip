@@ -705,6 +705,14 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
 }
 
 using LossStage = Stage<LOSS_BK, LOSS_NS, LOSS_WM, LOSS_WN>;
+// The direct product and the Gram build run sixteen waves of 128 x 32 (four a SIMD, 64
+// accumulators a wave): their epilogues fit the 128 registers that leaves, and the extra
+// waves hide more of the fragment reads.  The G form's loss epilogue does not fit them
+// and keeps eight waves.
+#ifndef LOSS_WN_WIDE
+#define LOSS_WN_WIDE 8
+#endif
+using LossStageWide = Stage<LOSS_BK, LOSS_NS, LOSS_WM, LOSS_WN_WIDE>;
 
 // Per-alpha loss = fixed-order fp64 sum of its tile partials (wave w handles alphas
 // w, w + 16, ...: lane-strided sums, then a butterfly in a fixed order), then the argmin
@@ -758,8 +766,8 @@ hipError_t launch_loss_gemm(const uint16_t* dW, const uint16_t* X, int M, int N,
   const int tm = (int)loss_tiles_m(M), tn = (int)loss_tiles_n(N);
   const long long blocks = (long long)nb * tm * tn;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_loss_gemm<LossStage, kModeDirect>), dim3((unsigned)blocks),
-                     dim3(LossStage::THREADS), 0, stream, dW, X, nullptr, M, N, K, K, 0, tm, tn,
+  hipLaunchKernelGGL((k_loss_gemm<LossStageWide, kModeDirect>), dim3((unsigned)blocks),
+                     dim3(LossStageWide::THREADS), 0, stream, dW, X, nullptr, M, N, K, K, 0, tm, tn,
                      nb, nullptr, partials, nullptr, nullptr);
   return hipGetLastError();
 }
@@ -787,8 +795,8 @@ hipError_t launch_gram_build(const uint16_t* Xt, int N, int ld, int K, int kchun
   const int T = (int)loss_tiles_m(K);
   const long long blocks = (long long)splits * T * (T + 1) / 2;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_loss_gemm<LossStage, kModeGramBuild>), dim3((unsigned)blocks),
-                     dim3(LossStage::THREADS), 0, stream, nullptr, Xt, nullptr, 0, N, K, ld,
+  hipLaunchKernelGGL((k_loss_gemm<LossStageWide, kModeGramBuild>), dim3((unsigned)blocks),
+                     dim3(LossStageWide::THREADS), 0, stream, nullptr, Xt, nullptr, 0, N, K, ld,
                      kchunk, T, T, splits, nullptr, nullptr, out, tmax);
   return hipGetLastError();
 }
