@@ -186,7 +186,8 @@ int awq_search_scale_table(const void* W, const void* X, const float* s_table, i
  * a, else 1 [AWQ-tut 显著识别 (indicator of channels above a high percentile, 70-90),
  * 缩放保护 (protect by a factor > 1), Python 演示 (70th percentile, factor 2)].  The
  * threshold interpolates linearly between order statistics at position
- * (percentile/100)(K-1), in fp64; the comparison is made in fp64.  Non-finite a sort last.
+ * (percentile/100)(K-1), in fp64; the comparison is made in fp64.  NaN sorts last (as
+ * +inf); +-inf sort at the ends.  s_out may be a itself.
  *   a fp32 [in], s_out fp32 [in] (device); 1 <= in <= 32768; percentile in [0, 100];
  *   factor finite and > 0. */
 int awq_threshold_scales(const float* a, int64_t in_features, double percentile, float factor,
