@@ -266,16 +266,11 @@ def main():
     gram_flops = gram_build_flops(N, K) if gram else 0.0
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
     g = spec.group_size
-    stats_bytes = 2.0 * N * K + 4.0 * K
-    fq_bytes = 2.0 * M * K + 4.0 * K * nA + 2.0 * M * K * nA
-    pack_bytes = 2.0 * M * K + 4.0 * K + M * K / 2 + 4.0 * M * K / g
-    ceilings = measure_ceilings(torch, sptr)
-    copy_gbs = ceilings["copy_GB/s"]
-
-    def hbm(nbytes, ms, what):
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        return {"ms": ms, "bytes": nbytes, "GB/s": gbs, "frac_hbm_8TBps": gbs / HBM_PEAK_GBS,
-                "frac_copy_ceiling": gbs / copy_gbs, "timed": what}
+    # algorithmic bytes read and written by the streaming kernels
+    stats_rw = (2.0 * N * K, 4.0 * K)
+    fq_rw = (2.0 * M * K + 4.0 * K * nA, 2.0 * M * K * nA)
+    pack_rw = (2.0 * M * K + 4.0 * K, M * K / 2 + 4.0 * M * K / g)
+    ceilings = measure_ceilings(awq, torch, sptr)
 
     # HBM bytes per launch from the committed counter summary, valid only for the kernel
     # source and workload it was measured on (null otherwise).
@@ -321,15 +316,21 @@ def main():
                      "kernel": "k_loss_gemm" + ("<G form>" if gram else ""),
                      "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms,
                      "mfma_counters": counters,
+                     # the same rate against this box's matrix-core-only probe (same run)
+                     "measured_ceiling": {
+                         "TFLOP/s": ceilings["mfma_probe"]["TFLOP/s"],
+                         "shader_clock_GHz": ceilings["mfma_probe"]["shader_clock_GHz"],
+                         "frac": gemm_tflops / ceilings["mfma_probe"]["TFLOP/s"],
+                         "source": "awq_probe_mfma"},
                      "form": "gram" if gram else "direct",
                      # the G form executes M K^2 (1 + 128/K) per alpha where the direct product
                      # would take 2 M K N: the ratio of the two is work saved, not a rate
                      "direct_over_executed_flops": direct_flops / (gemm_flops + gram_flops)},
         "kernels": {
-            "act_stats": {**hbm(stats_bytes, stats_pass_ms, "streaming pass (first of the two "
-                                                             "launches), library events"),
-                          "call_ms": stats_ms},
-            "fake_quant": hbm(fq_bytes, fq_ms, "one launch, library events"),
+            "act_stats": hbm_entry(*stats_rw, stats_pass_ms, ceilings, call_ms=stats_ms,
+                                   timed="streaming pass (first of the two launches), library "
+                                         "events"),
+            "fake_quant": hbm_entry(*fq_rw, fq_ms, ceilings, timed="one launch, library events"),
             "loss_gemm": {"ms": gemm_ms, "TFLOP/s": gemm_tflops,
                           "frac_mfma": gemm_tflops / MFMA_F16_PEAK_TFLOPS,
                           "form": "gram" if gram else "direct"},
@@ -338,17 +339,18 @@ def main():
                          "frac_mfma": gram_flops / (gram_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
                          "timed": "the whole Gram pass (transpose, build, combine, split) "
                                   "against the build's executed flops"}} if gram else {}),
-            "quant_pack": hbm(pack_bytes, pack_ms, "one launch, events around the call"),
+            "quant_pack": hbm_entry(*pack_rw, pack_ms, ceilings,
+                                    timed="one launch, events around the call"),
         },
         "search_status": status,
     }
     if not args.no_variants:
-        line["variants"] = time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, copy_gbs)
-        line["w4a16"] = time_w4a16(awq, torch, out, res["s"], Xd, cfg, sptr, M, K, copy_gbs)
-        line["large_layers"] = time_large_layers(awq, torch, alphas, sptr, copy_gbs)
+        line["variants"] = time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, ceilings)
+        line["w4a16"] = time_w4a16(awq, torch, out, res["s"], Xd, cfg, sptr, M, K, ceilings)
+        line["large_layers"] = time_large_layers(awq, torch, alphas, sptr, ceilings)
         line["small_layer"] = time_small_layer(awq, torch, sptr)
     line["ceilings"] = ceilings
-    line["size_floor"] = measure_size_floor(torch, Xd, Wd, sptr, copy_gbs)
+    line["size_floor"] = measure_size_floor(torch, Xd, Wd, sptr)
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib * (1 << 20) // 2, dtype=torch.float16, device="cuda")
         dst = torch.empty_like(src)
@@ -380,10 +382,11 @@ def gram_build_flops(N, K):
     return T * (T + 1) / 2 * 2.0 * 256 * 256 * N
 
 
-def measure_size_floor(torch, Xd, Wd, sptr, copy_gbs, reps=20):
+def measure_size_floor(torch, Xd, Wd, sptr, reps=20):
     """Plain device operations on the headline layer's own tensors, for the size floor of the
     short statistics and pack launches: a full read of X (torch.sum over all elements, fp32
-    accumulation) and a copy of W (read + write of the same bytes)."""
+    accumulation) and a copy of W (read + write of the same bytes).  At 32-64 MiB these
+    operands fit the 256 MB last-level cache, so no HBM fraction is given for them."""
 
     def timed(fn):
         fn()
@@ -399,20 +402,25 @@ def measure_size_floor(torch, Xd, Wd, sptr, copy_gbs, reps=20):
     out = {}
     ms = timed(lambda: torch.sum(Xd, dtype=torch.float32))
     b = Xd.numel() * 2.0
-    out["read_X_torch_sum"] = {"ms": ms, "bytes": b, "GB/s": b / (ms * 1e-3) / 1e9,
-                               "frac_copy_ceiling": b / (ms * 1e-3) / 1e9 / copy_gbs}
+    out["read_X_torch_sum"] = {"ms": ms, "bytes": b, "GB/s": b / (ms * 1e-3) / 1e9}
     dst = torch.empty_like(Wd)
     ms = timed(lambda: dst.copy_(Wd))
     b = Wd.numel() * 4.0
-    out["copy_W"] = {"ms": ms, "bytes": b, "GB/s": b / (ms * 1e-3) / 1e9,
-                     "frac_copy_ceiling": b / (ms * 1e-3) / 1e9 / copy_gbs}
+    out["copy_W"] = {"ms": ms, "bytes": b, "GB/s": b / (ms * 1e-3) / 1e9}
     return out
 
 
-def measure_ceilings(torch, sptr, reps=20):
-    """This box's practical ceilings, measured after the timed region: a 512 MiB
-    device-to-device copy (read + write bytes over time) and a plain fp16 4096^3 product
-    through torch.matmul (hipBLASLt), both on contiguous operands."""
+def measure_ceilings(awq, torch, sptr, reps=5):
+    """This box's practical ceilings, measured after the timed region with the library's
+    probes and torch:
+      - matrix cores: awq_probe_mfma, blocks of eight waves issuing back-to-back fp16
+        32x32x16 MFMAs on registers; the shader clock from the shader-clock and real-time
+        counters;
+      - LDS: awq_probe_lds, conflict-free 16-byte reads, bytes per shader clock per unit;
+      - HBM: a streaming read (awq_probe_read) and write (awq_probe_write) of 1 GiB and a
+        copy (awq_probe_copy, and torch's copy) of 512 MiB (read + write bytes over time),
+        all larger than the 256 MB last-level cache;
+      - a plain fp16 4096^3 product through torch.matmul (hipBLASLt)."""
 
     def timed(fn):
         fn()
@@ -425,11 +433,47 @@ def measure_ceilings(torch, sptr, reps=20):
         torch.cuda.synchronize()
         return e0.elapsed_ms(e1) / reps
 
-    src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
+    out = {}
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    wall_ghz = awq.awq_probe_wall_clock_khz(0) * 1e-6
+
+    def clock_ghz(ticks):
+        # shader-clock ticks over real-time ticks of each block's first wave (its own loop)
+        t = ticks.cpu().double()
+        return float((t[:, 0] / t[:, 1]).median()) * wall_ghz
+
+    # matrix cores: four rounds of blocks (one block of eight waves fits a compute unit);
+    # the rate comes from the kernel's events, not from the blocks' ticks, because the
+    # older wave of a SIMD finishes its loop well before the younger one
+    iters, blocks = 8000, 4 * n_cu
+    ms = timed(lambda: awq.awq_probe_mfma(blocks, iters))
+    ghz = clock_ghz(awq.awq_probe_mfma(blocks, iters))
+    tfs = blocks * 8.0 * iters * 8 * 32768 / (ms * 1e-3) / 1e12
+    out["mfma_probe"] = {"TFLOP/s": tfs, "frac_of_2.5PF": tfs / MFMA_F16_PEAK_TFLOPS,
+                         "shader_clock_GHz": ghz,
+                         "flop_per_clock_per_SIMD": tfs * 1e12 / (n_cu * 4 * ghz * 1e9),
+                         "ms": ms, "blocks": blocks, "compute_units": n_cu}
+    # LDS reads, same geometry
+    iters = 2000
+    ms = timed(lambda: awq.awq_probe_lds(blocks, iters))
+    ghz = clock_ghz(awq.awq_probe_lds(blocks, iters))
+    tbs = blocks * 8.0 * iters * 16 * 1024 / (ms * 1e-3) / 1e12
+    out["lds_probe"] = {"TB/s": tbs, "shader_clock_GHz": ghz,
+                        "bytes_per_clock_per_CU": tbs * 1e12 / (n_cu * ghz * 1e9), "ms": ms}
+    # HBM: 1 GiB read, 1 GiB written, 512 MiB copied (1 GiB moved)
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: awq.awq_probe_read(buf))
+    out["read_GB/s"] = buf.numel() / (ms * 1e-3) / 1e9
+    ms = timed(lambda: awq.awq_probe_write(buf))
+    out["write_GB/s"] = buf.numel() / (ms * 1e-3) / 1e9
+    src, dst = buf[: 512 << 20], buf[512 << 20:]
+    ms = timed(lambda: awq.awq_probe_copy(src, dst))
+    out["copy_GB/s"] = 2.0 * src.numel() / (ms * 1e-3) / 1e9
     ms = timed(lambda: dst.copy_(src))
-    copy_gbs = 2.0 * src.numel() / (ms * 1e-3) / 1e9
-    del src, dst
+    out["torch_copy_GB/s"] = 2.0 * src.numel() / (ms * 1e-3) / 1e9
+    del buf, src, dst
+    for k in ("read", "write", "copy", "torch_copy"):
+        out[f"{k}_frac_of_8TBps"] = out[f"{k}_GB/s"] / HBM_PEAK_GBS
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7)
     a = torch.randn((4096, 4096), device="cuda", generator=gen).half()
@@ -439,9 +483,26 @@ def measure_ceilings(torch, sptr, reps=20):
     gemm_tf = 2.0 * 4096 ** 3 / (ms * 1e-3) / 1e12
     del a, b, c
     torch.cuda.empty_cache()
-    return {"copy_GB/s": copy_gbs, "copy_frac_of_8TBps": copy_gbs / HBM_PEAK_GBS,
-            "torch_matmul_fp16_4096^3_TFLOP/s": gemm_tf,
-            "torch_matmul_frac_of_2.5PF": gemm_tf / MFMA_F16_PEAK_TFLOPS}
+    out["torch_matmul_fp16_4096^3_TFLOP/s"] = gemm_tf
+    out["torch_matmul_frac_of_2.5PF"] = gemm_tf / MFMA_F16_PEAK_TFLOPS
+    return out
+
+
+def hbm_entry(rd, wr, ms, ceil, **extra):
+    """A streaming kernel's rate: algorithmic bytes read (rd) and written (wr) over its time,
+    as a fraction of 8 TB/s and of this box's measured ceiling for that mix of reads and
+    writes.  The ceiling's time adds the read and write streams at the probes' rates and a
+    turnaround cost for interleaving them, fitted so that an equal mix (a copy) takes the
+    copy probe's time:  t = rd / read + wr / write + c min(rd, wr),
+    c = 2 / copy - 1 / read - 1 / write (at least 0)."""
+    b = rd + wr
+    gbs = b / (ms * 1e-3) / 1e9
+    r, w, cp = (ceil[k] * 1e9 for k in ("read_GB/s", "write_GB/s", "copy_GB/s"))
+    turn = max(0.0, 2.0 / cp - 1.0 / r - 1.0 / w)
+    t_ceil = rd / r + wr / w + turn * min(rd, wr)
+    return {"ms": ms, "bytes": b, "GB/s": gbs, "frac_hbm_8TBps": gbs / HBM_PEAK_GBS,
+            "ceiling_GB/s": b / t_ceil / 1e9, "frac_measured_ceiling": t_ceil / (ms * 1e-3),
+            **extra}
 
 
 def graph_and_eager_ms(torch, fn, sptr, reps):
@@ -484,7 +545,7 @@ def graph_and_eager_ms(torch, fn, sptr, reps):
     return best, eager
 
 
-def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, copy_gbs, reps=20):
+def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, ceil, reps=20):
     """Average time per call of the widened entry points on the same layer, measured
     after the timed region: the streaming calls as graph replays (with the eager per-call
     time beside them), the two searches as `reps` back-to-back calls (milliseconds each,
@@ -502,16 +563,13 @@ def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, copy_gbs, reps=20):
         return e0.elapsed_ms(e1) / reps
 
     out = {}
-    x_bytes = 2.0 * N * K + 4.0 * K
     for name, mode, extra in [("stat_max_abs", awq.AWQ_STAT_MAX_ABS, ()),
                               ("stat_rms_ratio", awq.AWQ_STAT_RMS_RATIO, ()),
                               ("stat_ema_mean_b512", awq.AWQ_STAT_EMA_MEAN, (512, 0.9))]:
         ms, eager = graph_and_eager_ms(torch, lambda: awq.awq_act_stats_ex(Xd, mode, *extra),
                                        sptr, reps)
-        gbs = x_bytes / (ms * 1e-3) / 1e9
-        out[name] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
-                     "frac_copy_ceiling": gbs / copy_gbs, "eager_call_ms": eager,
-                     "timed": "whole call (two launches), graph replay"}
+        out[name] = hbm_entry(2.0 * N * K, 4.0 * K, ms, ceil, eager_call_ms=eager,
+                              timed="whole call (two launches), graph replay")
     a = awq.awq_act_stats(Xd)
     ms, eager = graph_and_eager_ms(torch, lambda: awq.awq_threshold_scales(a, 70.0, 2.0), sptr,
                                    reps)
@@ -520,10 +578,8 @@ def time_variants(awq, torch, Wd, Xd, cfg, sptr, M, K, N, copy_gbs, reps=20):
     Xr = torch.empty_like(Xd)
     ms, eager = graph_and_eager_ms(torch, lambda: awq.awq_hadamard_rotate(Xd, 128, out=Xr), sptr,
                                    reps)
-    gbs = 4.0 * N * K / (ms * 1e-3) / 1e9
-    out["hadamard_rotate_X_b128"] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
-                                     "frac_copy_ceiling": gbs / copy_gbs, "eager_call_ms": eager,
-                                     "timed": "graph replay"}
+    out["hadamard_rotate_X_b128"] = hbm_entry(2.0 * N * K, 2.0 * N * K, ms, ceil,
+                                              eager_call_ms=eager, timed="graph replay")
     table = torch.stack([awq.awq_threshold_scales(a, p, f) for p in (50.0, 70.0, 85.0, 95.0, 99.0)
                          for f in (1.5, 2.0, 3.0, 4.0)]).contiguous()
     ws = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, table.shape[0], 0), dtype=torch.uint8,
@@ -616,7 +672,7 @@ def w4a16_bytes(M, K, g, T, with_s):
     return M * K / 2 + 4.0 * M * K / g + 2.0 * T * K + (4.0 * K if with_s else 0.0) + 2.0 * T * M
 
 
-def time_large_layers(awq, torch, alphas, sptr, copy_gbs, reps=2):
+def time_large_layers(awq, torch, alphas, sptr, ceil, reps=2):
     """The whole 20-alpha search on the four large layer shapes, with seeded device-side
     weights and activations (1% of the channels scaled by 20).  The library's event hook
     times the Gram pass and the loss product of each search separately; their rates are
@@ -670,14 +726,14 @@ def time_large_layers(awq, torch, alphas, sptr, copy_gbs, reps=2):
             entry["gram_pass"] = {"ms": gram_ms, "build_flops": bflops, **tf(bflops, gram_ms)}
         entry["direct_over_executed_flops"] = 2.0 * M * K * N * nA / (gflops + bflops)
         if name == "c4":
-            entry["act_stats"] = time_stats_and_pack(awq, torch, W, X, cfg, sptr, copy_gbs)
+            entry["act_stats"] = time_stats_and_pack(awq, torch, W, X, cfg, sptr, ceil)
         out[name] = entry
         del W, X, a, ws
         torch.cuda.empty_cache()
     return out
 
 
-def time_stats_and_pack(awq, torch, W, X, cfg, sptr, copy_gbs, reps=5):
+def time_stats_and_pack(awq, torch, W, X, cfg, sptr, ceil, reps=5):
     """Statistics over a 1 GiB activation tensor and the pack of a 448 MiB weight: sizes at
     which the HBM fraction of these streaming kernels is not set by launch overhead."""
     N, K = X.shape
@@ -699,17 +755,12 @@ def time_stats_and_pack(awq, torch, W, X, cfg, sptr, copy_gbs, reps=5):
     torch.cuda.synchronize()
     ms_s = float(sum(e[0].elapsed_ms(e[1]) for e in st) / reps)
     ms_p = float(sum(e[2].elapsed_ms(e[3]) for e in st) / reps)
-    sb = 2.0 * N * K + 4.0 * K
-    pb = 2.0 * M * K + 4.0 * K + M * K / 2 + 4.0 * M * K / cfg.group_size
-    return {"stats_pass": {"ms": ms_s, "bytes": sb, "GB/s": sb / (ms_s * 1e-3) / 1e9,
-                           "frac_hbm_8TBps": sb / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                           "frac_copy_ceiling": sb / (ms_s * 1e-3) / 1e9 / copy_gbs},
-            "quant_pack": {"ms": ms_p, "bytes": pb, "GB/s": pb / (ms_p * 1e-3) / 1e9,
-                           "frac_hbm_8TBps": pb / (ms_p * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                           "frac_copy_ceiling": pb / (ms_p * 1e-3) / 1e9 / copy_gbs}}
+    return {"stats_pass": hbm_entry(2.0 * N * K, 4.0 * K, ms_s, ceil),
+            "quant_pack": hbm_entry(2.0 * M * K + 4.0 * K,
+                                    M * K / 2 + 4.0 * M * K / cfg.group_size, ms_p, ceil)}
 
 
-def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, copy_gbs, reps=50):
+def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, ceil, reps=50):
     """The packed layer's W4A16 product at decode batches 1 and 4: on the layer just packed,
     and on a 28672 x 8192 packed layer (the 70B-class MLP shape) of seeded random codes.
     Kernel time from graph replays; the eager per-call time (host marshalling and launch
@@ -721,18 +772,18 @@ def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, copy_gbs, reps=50):
     ws = torch.empty(max(256, awq.awq_w4a16_workspace_bytes(16, max(K, 8192))),
                      dtype=torch.uint8, device="cuda")
 
-    def entry(fn, b):
+    def entry(fn, b, out_bytes):
         ms, eager = graph_and_eager_ms(torch, fn, sptr, reps)
-        gbs = b / (ms * 1e-3) / 1e9
-        return {"us": ms * 1e3, "GB/s": gbs, "bytes": b, "frac_hbm": gbs / HBM_PEAK_GBS,
-                "frac_copy_ceiling": gbs / copy_gbs, "eager_call_us": eager * 1e3}
+        e = hbm_entry(b - out_bytes, out_bytes, ms, ceil, eager_call_us=eager * 1e3)
+        e["us"] = ms * 1e3
+        return e
 
     for T in (1, 4):
         x = Xd[:T].contiguous()
         y = torch.empty((T, M), dtype=torch.float16, device="cuda")
         out[f"{M}x{K}_T{T}"] = entry(
             lambda: awq.awq_w4a16_matmul(x, codes, scales, zeros, cfg, s=s, out=y, workspace=ws),
-            w4a16_bytes(M, K, g, T, True))
+            w4a16_bytes(M, K, g, T, True), 2.0 * T * M)
     M2, K2 = 28672, 8192
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20250)
@@ -747,11 +798,11 @@ def time_w4a16(awq, torch, packed, s, Xd, cfg, sptr, M, K, copy_gbs, reps=50):
         if T <= 4:
             out[f"{M2}x{K2}_T{T}"] = entry(
                 lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg, s=s2, out=y, workspace=ws),
-                w4a16_bytes(M2, K2, g, T, True))
+                w4a16_bytes(M2, K2, g, T, True), 2.0 * T * M2)
         # S^-1 already folded into the activations (the deployed form): no division
         out[f"{M2}x{K2}_T{T}_folded"] = entry(
             lambda: awq.awq_w4a16_matmul(x, c2, sc2, z2, cfg, out=y),
-            w4a16_bytes(M2, K2, g, T, False))
+            w4a16_bytes(M2, K2, g, T, False), 2.0 * T * M2)
     return out
 
 

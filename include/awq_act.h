@@ -330,6 +330,34 @@ int awq_set_profile_events(void* gemm_start, void* gemm_stop, void* fq_start,
  * streaming pass over X, the first of its two launches.  Returns AWQ_OK. */
 int awq_set_stats_profile_events(void* pass_start, void* pass_stop);
 
+/* ------------------------------------------------------------------------------------
+ * Measurement probes: this device's practical ceilings, for reporting the kernels above
+ * beside the published peaks.  They are not part of the search, compute nothing useful,
+ * and are enqueued on `stream` like every other call.
+ *
+ * awq_probe_mfma: `blocks` blocks of eight waves (two a SIMD), each wave issuing
+ *   iters x 8 back-to-back v_mfma_f32_32x32x16_f16 (32768 flop each) on register operands.
+ *   clocks_out, device uint64 [blocks][2] (written): per block, the shader-clock ticks and
+ *   the 100 MHz real-time ticks of its loop, so clock = ticks[0] / ticks[1] x 100 MHz.
+ * awq_probe_lds: the same geometry, each wave issuing iters x 16 conflict-free 16-byte LDS
+ *   reads per lane (1 KiB a wave-read); same clocks_out.
+ * awq_probe_read: one streaming read of `bytes` (a multiple of 16) at src (16-byte
+ *   aligned device memory), 16-byte loads, each block over its own contiguous range.
+ * awq_probe_write: one streaming write of `bytes` (a multiple of 16) to dst, 16-byte stores
+ *   (the contents become fp16 ones).
+ * awq_probe_copy: one streaming copy of `bytes` from src to dst (distinct buffers).
+ * awq_probe_wall_clock_khz: host-side query of the frequency of the real-time counter
+ *   (hipDeviceAttributeWallClockRate of `device`) into *khz_out (host int32).
+ * blocks and iters in [1, 2^20] and [1, 2^24].  Errors: AWQ_E_NULL, AWQ_E_SHAPE,
+ * AWQ_E_ALIGN, AWQ_E_DEVICE, AWQ_E_HIP, as for the other calls.
+ * ---------------------------------------------------------------------------------- */
+int awq_probe_mfma(int32_t blocks, int32_t iters, uint64_t* clocks_out, void* stream);
+int awq_probe_lds(int32_t blocks, int32_t iters, uint64_t* clocks_out, void* stream);
+int awq_probe_read(const void* src, int64_t bytes, void* stream);
+int awq_probe_write(void* dst, int64_t bytes, void* stream);
+int awq_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+int awq_probe_wall_clock_khz(int32_t device, int32_t* khz_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,7 +39,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 28, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in awq_act.h but not exported"
     assert set(names) == set(_lib._SIGNATURES)
@@ -310,3 +310,24 @@ def test_clip_validation(L):
     assert g(P, P, None, 8, 128, _cfg(), P, P, P, None) == E["NULL"]
     assert g(P, P, ctypes.c_void_p(0x10002), 8, 128, _cfg(), P, P, P, None) == E["ALIGN"]
     assert g(P, P, P, 0, 128, _cfg(), P, P, P, None) == E["OK"]
+
+
+def test_probe_validation(L):
+    """The measurement probes check their arguments on the host like the other calls."""
+    for probe in (L.awq_probe_mfma, L.awq_probe_lds):
+        assert probe(4, 4, None, None) == E["NULL"]
+        assert probe(0, 4, P, None) == E["SHAPE"]
+        assert probe(4, 0, P, None) == E["SHAPE"]
+        assert probe((1 << 20) + 1, 4, P, None) == E["SHAPE"]
+        assert probe(4, (1 << 24) + 1, P, None) == E["SHAPE"]
+        assert probe(4, 4, ctypes.c_void_p(0x10004), None) == E["ALIGN"]
+    for probe in (L.awq_probe_read, L.awq_probe_write):
+        assert probe(None, 1024, None) == E["NULL"]
+        assert probe(P, 0, None) == E["SHAPE"]
+        assert probe(P, 1000, None) == E["SHAPE"]          # not a multiple of 16
+        assert probe(ctypes.c_void_p(0x10008), 1024, None) == E["ALIGN"]
+    c = L.awq_probe_copy
+    assert c(None, P, 1024, None) == E["NULL"] and c(P, None, 1024, None) == E["NULL"]
+    assert c(P, P, 8, None) == E["SHAPE"]
+    assert c(P, ctypes.c_void_p(0x10008), 1024, None) == E["ALIGN"]
+    assert L.awq_probe_wall_clock_khz(0, None) == E["NULL"]

@@ -74,6 +74,12 @@ _SIGNATURES = {
                                                  _vp]),
     "awq_quantize_pack_checked": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _cfgp, _vp, _vp, _vp,
                                                  _vp, _vp]),
+    "awq_probe_mfma": (ctypes.c_int, [_i32, _i32, _vp, _vp]),
+    "awq_probe_lds": (ctypes.c_int, [_i32, _i32, _vp, _vp]),
+    "awq_probe_read": (ctypes.c_int, [_vp, _i64, _vp]),
+    "awq_probe_write": (ctypes.c_int, [_vp, _i64, _vp]),
+    "awq_probe_copy": (ctypes.c_int, [_vp, _vp, _i64, _vp]),
+    "awq_probe_wall_clock_khz": (ctypes.c_int, [_i32, ctypes.POINTER(_i32)]),
 }
 
 AWQ_STAT_MEAN_ABS, AWQ_STAT_MAX_ABS, AWQ_STAT_RMS_RATIO, AWQ_STAT_EMA_MEAN = 0, 1, 2, 3
@@ -335,6 +341,59 @@ def awq_set_stats_profile_events(pass_start=None, pass_stop=None):
         return int(e) if isinstance(e, int) else int(e.handle)
     _check(lib().awq_set_stats_profile_events(h(pass_start), h(pass_stop)),
            "awq_set_stats_profile_events")
+
+
+@_on_stream
+def awq_probe_mfma(blocks: int, iters: int, stream=None) -> torch.Tensor:
+    """Enqueue the matrix-core probe; returns its per-block clock ticks (device int64
+    [blocks][2]: shader clock, 100 MHz real time)."""
+    clocks = torch.zeros((int(blocks), 2), dtype=torch.int64, device="cuda")
+    _check(lib().awq_probe_mfma(int(blocks), int(iters), _ptr(clocks), _stream_ptr(stream)),
+           "awq_probe_mfma")
+    return clocks
+
+
+@_on_stream
+def awq_probe_lds(blocks: int, iters: int, stream=None) -> torch.Tensor:
+    """Enqueue the LDS-read probe; per-block clock ticks as for awq_probe_mfma."""
+    clocks = torch.zeros((int(blocks), 2), dtype=torch.int64, device="cuda")
+    _check(lib().awq_probe_lds(int(blocks), int(iters), _ptr(clocks), _stream_ptr(stream)),
+           "awq_probe_lds")
+    return clocks
+
+
+def awq_probe_read(src: torch.Tensor, stream=None):
+    """Enqueue one streaming read of the whole (contiguous, device) tensor."""
+    if not (isinstance(src, torch.Tensor) and src.is_cuda and src.is_contiguous()):
+        raise ValueError("src must be a contiguous device tensor")
+    _check(lib().awq_probe_read(_ptr(src), src.numel() * src.element_size(), _stream_ptr(stream)),
+           "awq_probe_read")
+
+
+def awq_probe_write(dst: torch.Tensor, stream=None):
+    """Enqueue one streaming write over the whole (contiguous, device) tensor."""
+    if not (isinstance(dst, torch.Tensor) and dst.is_cuda and dst.is_contiguous()):
+        raise ValueError("dst must be a contiguous device tensor")
+    _check(lib().awq_probe_write(_ptr(dst), dst.numel() * dst.element_size(),
+                                 _stream_ptr(stream)), "awq_probe_write")
+
+
+def awq_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """Enqueue one streaming copy of src into dst (contiguous device tensors, same size)."""
+    for t in (src, dst):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+            raise ValueError("src and dst must be contiguous device tensors")
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst differ in size")
+    _check(lib().awq_probe_copy(_ptr(src), _ptr(dst), nb, _stream_ptr(stream)), "awq_probe_copy")
+
+
+def awq_probe_wall_clock_khz(device: int = 0) -> int:
+    """Frequency of the device's real-time counter in kHz."""
+    v = ctypes.c_int32(0)
+    _check(lib().awq_probe_wall_clock_khz(int(device), ctypes.byref(v)), "awq_probe_wall_clock_khz")
+    return int(v.value)
 
 
 @_on_stream

@@ -567,6 +567,69 @@ int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_fe
                                             errors_out, (hipStream_t)stream));
 }
 
+int awq_probe_mfma(int32_t blocks, int32_t iters, uint64_t* clocks_out, void* stream) {
+  if (!clocks_out) return AWQ_E_NULL;
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 24)) return AWQ_E_SHAPE;
+  if (!aligned(clocks_out, 8)) return AWQ_E_ALIGN;
+  int st;
+  if ((st = device_ptr(clocks_out))) return st;
+  clear_pending_error();
+  return hip_status(awq::launch_probe_mfma(blocks, iters, (unsigned long long*)clocks_out,
+                                           (hipStream_t)stream));
+}
+
+int awq_probe_lds(int32_t blocks, int32_t iters, uint64_t* clocks_out, void* stream) {
+  if (!clocks_out) return AWQ_E_NULL;
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 24)) return AWQ_E_SHAPE;
+  if (!aligned(clocks_out, 8)) return AWQ_E_ALIGN;
+  int st;
+  if ((st = device_ptr(clocks_out))) return st;
+  clear_pending_error();
+  return hip_status(awq::launch_probe_lds(blocks, iters, (unsigned long long*)clocks_out,
+                                          (hipStream_t)stream));
+}
+
+int awq_probe_read(const void* src, int64_t bytes, void* stream) {
+  if (!src) return AWQ_E_NULL;
+  if (bytes < 16 || bytes % 16 != 0) return AWQ_E_SHAPE;
+  if (!aligned(src, 16)) return AWQ_E_ALIGN;
+  int st;
+  if ((st = device_ptr(src))) return st;
+  clear_pending_error();
+  return hip_status(awq::launch_probe_read(src, (long long)bytes, (hipStream_t)stream));
+}
+
+int awq_probe_write(void* dst, int64_t bytes, void* stream) {
+  if (!dst) return AWQ_E_NULL;
+  if (bytes < 16 || bytes % 16 != 0) return AWQ_E_SHAPE;
+  if (!aligned(dst, 16)) return AWQ_E_ALIGN;
+  int st;
+  if ((st = device_ptr(dst))) return st;
+  clear_pending_error();
+  return hip_status(awq::launch_probe_write(dst, (long long)bytes, (hipStream_t)stream));
+}
+
+int awq_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (!src || !dst) return AWQ_E_NULL;
+  if (bytes < 16 || bytes % 16 != 0) return AWQ_E_SHAPE;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return AWQ_E_ALIGN;
+  int st;
+  if ((st = device_ptr(src)) || (st = device_ptr(dst))) return st;
+  clear_pending_error();
+  return hip_status(awq::launch_probe_copy(src, dst, (long long)bytes, (hipStream_t)stream));
+}
+
+int awq_probe_wall_clock_khz(int32_t device, int32_t* khz_out) {
+  if (!khz_out) return AWQ_E_NULL;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, device) != hipSuccess) {
+    (void)hipGetLastError();
+    return AWQ_E_HIP;
+  }
+  *khz_out = v;
+  return AWQ_OK;
+}
+
 int awq_set_stats_profile_events(void* pass_start, void* pass_stop) {
   g_stats_ev[0] = pass_start;
   g_stats_ev[1] = pass_stop;

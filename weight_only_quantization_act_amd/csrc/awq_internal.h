@@ -158,4 +158,17 @@ hipError_t launch_reduce_select(const double* partials, int n_alpha, int tiles,
                                 const float* s_table, int K, double* losses, int32_t* best,
                                 int32_t* status, float* s_out, hipStream_t stream);
 
+
+// ---- measurement probes (this device's ceilings; not part of the search) -------------
+// clocks: device [blocks][2] (shader-clock ticks, 100 MHz real-time ticks of each block's
+// loop).  The stream probes use kProbeStreamBlocks blocks of 256 threads.
+constexpr int kProbeStreamBlocks = 4096;
+hipError_t launch_probe_mfma(int blocks, int iters, unsigned long long* clocks,
+                             hipStream_t stream);
+hipError_t launch_probe_lds(int blocks, int iters, unsigned long long* clocks,
+                            hipStream_t stream);
+hipError_t launch_probe_read(const void* src, long long bytes, hipStream_t stream);
+hipError_t launch_probe_write(void* dst, long long bytes, hipStream_t stream);
+hipError_t launch_probe_copy(const void* src, void* dst, long long bytes, hipStream_t stream);
+
 }  // namespace awq
