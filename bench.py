@@ -350,7 +350,14 @@ def main():
         line["large_layers"] = time_large_layers(awq, torch, alphas, sptr, ceilings)
         line["small_layer"] = time_small_layer(awq, torch, sptr)
     line["ceilings"] = ceilings
-    line["size_floor"] = measure_size_floor(torch, Xd, Wd, sptr)
+    line["size_floor"] = measure_size_floor(awq, torch, Xd, Wd, sptr)
+    # the short streaming kernels against the same-size probes
+    sf = line["size_floor"]
+    line["kernels"]["act_stats"]["frac_same_size_read_probe"] = (
+        sf["read_X_probe"]["ms"] / line["kernels"]["act_stats"]["ms"])
+    line["kernels"]["quant_pack"]["frac_same_size_copy_probe"] = (
+        sf["copy_W_probe"]["ms"] * (pack_rw[0] + pack_rw[1]) / (2.0 * M * K * 2.0)
+        / line["kernels"]["quant_pack"]["ms"])
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib * (1 << 20) // 2, dtype=torch.float16, device="cuda")
         dst = torch.empty_like(src)
@@ -382,11 +389,12 @@ def gram_build_flops(N, K):
     return T * (T + 1) / 2 * 2.0 * 256 * 256 * N
 
 
-def measure_size_floor(torch, Xd, Wd, sptr, reps=20):
+def measure_size_floor(awq, torch, Xd, Wd, sptr, reps=20):
     """Plain device operations on the headline layer's own tensors, for the size floor of the
-    short statistics and pack launches: a full read of X (torch.sum over all elements, fp32
-    accumulation) and a copy of W (read + write of the same bytes).  At 32-64 MiB these
-    operands fit the 256 MB last-level cache, so no HBM fraction is given for them."""
+    short statistics and pack launches: a full read of X (the read probe, and torch.sum over
+    all elements with fp32 accumulation) and a copy of W (the copy probe and torch's copy,
+    read + write of the same bytes).  At 32-64 MiB these operands fit the 256 MB last-level
+    cache, so no HBM fraction is given for them."""
 
     def timed(fn):
         fn()
@@ -407,6 +415,12 @@ def measure_size_floor(torch, Xd, Wd, sptr, reps=20):
     ms = timed(lambda: dst.copy_(Wd))
     b = Wd.numel() * 4.0
     out["copy_W"] = {"ms": ms, "bytes": b, "GB/s": b / (ms * 1e-3) / 1e9}
+    ms = timed(lambda: awq.awq_probe_read(Xd))
+    b = Xd.numel() * 2.0
+    out["read_X_probe"] = {"ms": ms, "bytes": b, "GB/s": b / (ms * 1e-3) / 1e9}
+    ms = timed(lambda: awq.awq_probe_copy(Wd, dst))
+    b = Wd.numel() * 4.0
+    out["copy_W_probe"] = {"ms": ms, "bytes": b, "GB/s": b / (ms * 1e-3) / 1e9}
     return out
 
 
