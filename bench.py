@@ -183,7 +183,7 @@ def cpu_oracle_widened(layer, cfg, rows_table=64, rows_clip=8, rows_w4=512):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build measures "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this benchmark measures "
               "one GPU's share of the layer and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
@@ -316,7 +316,7 @@ def main():
                      "kernel": "k_loss_gemm" + ("<G form>" if gram else ""),
                      "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms,
                      "mfma_counters": counters,
-                     # the same rate against this box's matrix-core-only probe (same run)
+                     # the same rate against this device's matrix-core-only probe (same run)
                      "measured_ceiling": {
                          "TFLOP/s": ceilings["mfma_probe"]["TFLOP/s"],
                          "shader_clock_GHz": ceilings["mfma_probe"]["shader_clock_GHz"],
@@ -428,7 +428,7 @@ def measure_size_floor(awq, torch, Xd, Wd, sptr, reps=20):
 
 
 def measure_ceilings(awq, torch, sptr, reps=5):
-    """This box's practical ceilings, measured after the timed region with the library's
+    """This device's practical ceilings, measured after the timed region with the library's
     probes and torch:
       - matrix cores: awq_probe_mfma, blocks of eight waves issuing back-to-back fp16
         32x32x16 MFMAs on registers; the shader clock from the shader-clock and real-time
@@ -507,7 +507,7 @@ def measure_ceilings(awq, torch, sptr, reps=5):
 
 def hbm_entry(rd, wr, ms, ceil, **extra):
     """A streaming kernel's rate: algorithmic bytes read (rd) and written (wr) over its time,
-    as a fraction of 8 TB/s and of this box's measured ceiling for that mix of reads and
+    as a fraction of 8 TB/s and of this device's measured ceiling for that mix of reads and
     writes.  The ceiling's time adds the read and write streams at the probes' rates and a
     turnaround cost for interleaving them, fitted so that an equal mix (a copy) takes the
     copy probe's time:  t = rd / read + wr / write + c min(rd, wr),

@@ -39,7 +39,7 @@ constexpr int kMaxSplits = 128;
 #ifndef AWQ_STATS_LOAD_BATCH
 #define AWQ_STATS_LOAD_BATCH 4
 #endif
-// token rows a lane loads at once (same-box graph replays of the pass over 65536 x 8192
+// token rows a lane loads at once (same-device graph replays of the pass over 65536 x 8192
 // activations: 196.5 us for 1, 175.8 for 4, 186.2 for 8, 191.9 for 16; 12.4 to 14.2 us
 // for all four at 4096 x 4096)
 constexpr int kLoadBatch = AWQ_STATS_LOAD_BATCH;

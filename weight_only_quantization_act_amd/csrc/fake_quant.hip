@@ -26,7 +26,7 @@ constexpr int kThreads = 256;
 constexpr int kRowsFQ = 8;    // rows per block, fake quantisation
 constexpr long long kFqSliceBelow = 256;    // fewer blocks than this: slice the grid points
 constexpr long long kFqSmallTarget = 1024;  // blocks to aim for when slicing
-// rows per block, packing (same-box sweep at 4096 x 4096: 14.4 us for 2 rows against 15.8
+// rows per block, packing (same-device sweep at 4096 x 4096: 14.4 us for 2 rows against 15.8
 // for 8, 18.7 for 16; 1 and 4 rows in between; the same bytes out)
 constexpr int kRowsPack = 2;
 

@@ -43,7 +43,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define AWQ_GEMV_MAX_ROWS 64
 #endif
 #ifndef AWQ_GEMV_MIN_ROWS
-// rows per block at least (a multiple of the row batch).  Same-box graph replays, one
+// rows per block at least (a multiple of the row batch).  Same-device graph replays, one
 // token, S^-1 folded / s given: 4096 x 4096 6.3 / 8.3 us against 6.7 / 8.7 for 8 rows and
 // batches of 4; 28672 x 8192 28.1 / 32.9 against 30.3 / 35.4; 11008 x 4096 9.1 / 15.1
 // against 9.4 / 13.5
