@@ -348,8 +348,8 @@ int awq_set_stats_profile_events(void* pass_start, void* pass_stop);
  * awq_probe_copy: one streaming copy of `bytes` from src to dst (distinct buffers).
  * awq_probe_wall_clock_khz: host-side query of the frequency of the real-time counter
  *   (hipDeviceAttributeWallClockRate of `device`) into *khz_out (host int32).
- * blocks and iters in [1, 2^16] and [1, 2^20] (a launch of at most a few seconds).  Errors:
- * AWQ_E_NULL, AWQ_E_SHAPE,
+ * blocks and iters in [1, 2^16] and [1, 2^20] with blocks x iters at most 2^28 (about a quarter
+ * of a second of matrix-core work at the device's clock).  Errors: AWQ_E_NULL, AWQ_E_SHAPE,
  * AWQ_E_ALIGN, AWQ_E_DEVICE, AWQ_E_HIP, as for the other calls.
  * ---------------------------------------------------------------------------------- */
 int awq_probe_mfma(int32_t blocks, int32_t iters, uint64_t* clocks_out, void* stream);

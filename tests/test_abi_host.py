@@ -320,6 +320,7 @@ def test_probe_validation(L):
         assert probe(4, 0, P, None) == E["SHAPE"]
         assert probe((1 << 16) + 1, 4, P, None) == E["SHAPE"]
         assert probe(4, (1 << 20) + 1, P, None) == E["SHAPE"]
+        assert probe(1 << 16, 1 << 13, P, None) == E["SHAPE"]      # product above 2^28
         assert probe(4, 4, ctypes.c_void_p(0x10004), None) == E["ALIGN"]
     for probe in (L.awq_probe_read, L.awq_probe_write):
         assert probe(None, 1024, None) == E["NULL"]

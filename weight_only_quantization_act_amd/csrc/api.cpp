@@ -569,7 +569,9 @@ int awq_clip_search(const void* W, const void* X, const float* s, int64_t out_fe
 
 int awq_probe_mfma(int32_t blocks, int32_t iters, uint64_t* clocks_out, void* stream) {
   if (!clocks_out) return AWQ_E_NULL;
-  if (blocks < 1 || blocks > (1 << 16) || iters < 1 || iters > (1 << 20)) return AWQ_E_SHAPE;
+  if (blocks < 1 || blocks > (1 << 16) || iters < 1 || iters > (1 << 20) ||
+      (int64_t)blocks * iters > ((int64_t)1 << 28))
+    return AWQ_E_SHAPE;
   if (!aligned(clocks_out, 8)) return AWQ_E_ALIGN;
   int st;
   if ((st = device_ptr(clocks_out))) return st;
@@ -580,7 +582,9 @@ int awq_probe_mfma(int32_t blocks, int32_t iters, uint64_t* clocks_out, void* st
 
 int awq_probe_lds(int32_t blocks, int32_t iters, uint64_t* clocks_out, void* stream) {
   if (!clocks_out) return AWQ_E_NULL;
-  if (blocks < 1 || blocks > (1 << 16) || iters < 1 || iters > (1 << 20)) return AWQ_E_SHAPE;
+  if (blocks < 1 || blocks > (1 << 16) || iters < 1 || iters > (1 << 20) ||
+      (int64_t)blocks * iters > ((int64_t)1 << 28))
+    return AWQ_E_SHAPE;
   if (!aligned(clocks_out, 8)) return AWQ_E_ALIGN;
   int st;
   if ((st = device_ptr(clocks_out))) return st;
