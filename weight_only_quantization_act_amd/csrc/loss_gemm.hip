@@ -79,7 +79,7 @@ namespace {
 
 constexpr int BM = kLossBM, BN = kLossBN;
 constexpr int kBandM = 4;  // tile-rows per raster band (direct form)
-constexpr int kBandG = 8;  // tile-row pairs per raster band (G form; same-box sweep: 8 over 4 and 2)
+constexpr int kBandG = 8;  // tile-row pairs per raster band (G form; same-device sweep: 8 over 4 and 2)
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
   };
   // The two waves of a SIMD alternate between fragment reads and MFMAs; a wave issuing
   // its reads runs at raised priority, so the next step's operands are requested before
-  // the other wave's MFMAs take the issue slots (same-box A/B of the 20-alpha search,
+  // the other wave's MFMAs take the issue slots (same-device A/B of the 20-alpha search,
   // three rounds: 1.696 against 1.727 ms; priority around the MFMAs instead: 1.698).
   auto load_frag = [&](auto st, int ks, Frag& f) {
     if constexpr (LOSS_PRIO) __builtin_amdgcn_s_setprio(1);
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(S::THREADS) void k_loss_gemm(
     // stage kt+1 has landed (own DMAs) and this wave's reads of stage kt are done
     __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(S::NS - 2) * S::PER_STAGE>::value);
     __builtin_amdgcn_s_barrier();
-    // the refill DMAs, too, go out at raised priority (same-box A/B, three rounds: loss
+    // the refill DMAs, too, go out at raised priority (same-device A/B, three rounds: loss
     // product 1.339 against 1.370 ms)
     if constexpr (LOSS_PRIO) __builtin_amdgcn_s_setprio(1);
     dma_stage(st, kt + S::NS);
