@@ -69,7 +69,7 @@ def _spec(name, c, layer, M, K, N, w_sigma, x_dist, frac_or_count, factor, w_bit
                      1000 * c + 10 * layer)
 
 
-# The five workloads.  Index 1 is the headline case (4096 x 4096, 4096 tokens).
+# The five workloads; the headline case is "c2", a 4096 x 4096 layer with 4096 tokens.
 CONFIGS = {
     "c1": [_spec("c1", 1, 0, 512, 512, 256, 0.02, "normal", 5, 20.0, 4, 128, 0)],
     "c2": [_spec("c2", 2, 0, 4096, 4096, 4096, 0.02, "normal", 0.01,
