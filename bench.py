@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="c2", help="workload name (c1 .. c5)")
     p.add_argument("--layer", type=int, default=0, help="layer index within the workload")
+    p.add_argument("--alpha-batch", type=int, default=0,
+                   help="grid points per pass of the search (0: the library's choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-variants", action="store_true",
                    help="skip timing the statistic / threshold / rotation / table variants")
@@ -67,6 +69,7 @@ class HipEvent:
             hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                 ctypes.c_void_p]
             hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            hip.hipGetLastError.argtypes = []
             HipEvent._hip = hip
         self._ct = ctypes
         self.h = ctypes.c_void_p()
@@ -85,6 +88,9 @@ class HipEvent:
         f = self._ct.c_float()
         rc = HipEvent._hip.hipEventElapsedTime(self._ct.byref(f), self.h, end.h)
         if rc != 0:
+            # a failed query (an event never recorded) leaves its error pending in the
+            # runtime, where the next unrelated call would report it: clear it here
+            HipEvent._hip.hipGetLastError()
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return float(f.value)
 
@@ -180,6 +186,24 @@ def cpu_oracle_widened(layer, cfg, rows_table=64, rows_clip=8, rows_w4=512):
     return out
 
 
+def pass_event_times(evs):
+    """Sum the per-pass fake-quantisation and loss-product times of one search from the
+    4 n events armed with awq_set_profile_pass_events; passes the search did not run were
+    never recorded (their elapsed-time query fails).  Returns (fq_ms, loss_ms, passes)."""
+    fq = loss = 0.0
+    n = 0
+    for p in range(len(evs) // 4):
+        try:
+            f = evs[4 * p].elapsed_ms(evs[4 * p + 1])
+            g = evs[4 * p + 2].elapsed_ms(evs[4 * p + 3])
+        except RuntimeError:
+            break
+        fq += f
+        loss += g
+        n += 1
+    return fq, loss, n
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -205,22 +229,24 @@ def main():
 
     Wd = torch.from_numpy(layer.W).cuda()
     Xd = torch.from_numpy(layer.X).cuda()
-    ws_search = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, nA, 0), dtype=torch.uint8,
+    ws_search = torch.empty(awq.awq_workspace_bytes(M, K, N, cfg, nA, args.alpha_batch), dtype=torch.uint8,
                             device="cuda")
     ws_stats = torch.empty(awq.awq_act_stats_workspace_bytes(N, K), dtype=torch.uint8,
                            device="cuda")
     stream = torch.cuda.current_stream()
     sptr = int(stream.cuda_stream)
 
-    def step(ev=None):
+    def step(ev=None, pev=None):
         if ev is not None:
             ev["st0"].record(sptr)
             awq.awq_set_stats_profile_events(ev["sk0"], ev["sk1"])
         a = awq.awq_act_stats(Xd, workspace=ws_stats)
         if ev is not None:
             ev["st1"].record(sptr)
-            awq.awq_set_profile_events(ev["g0"], ev["g1"], ev["f0"], ev["f1"], ev["r0"],
-                                       ev["r1"])
+            # the Gram pass from the one-shot hook; the fake quantisation and loss product of
+            # every pass of the grid from the per-pass hook
+            awq.awq_set_profile_events(None, None, None, None, ev["r0"], ev["r1"])
+            awq.awq_set_profile_pass_events(pev)
         res = awq.awq_search_scales(Wd, Xd, a, alphas, cfg, workspace=ws_search)
         if ev is not None:
             ev["p0"].record(sptr)
@@ -245,17 +271,23 @@ def main():
     total_ms = t_start.elapsed_ms(t_end)
     ms_per_step = total_ms / args.steps
 
-    names = ("st0", "st1", "sk0", "sk1", "g0", "g1", "f0", "f1", "r0", "r1", "p0", "p1")
+    names = ("st0", "st1", "sk0", "sk1", "r0", "r1", "p0", "p1")
     evs = [{n: HipEvent() for n in names} for _ in range(args.steps)]
+    pevs = [[HipEvent() for _ in range(4 * nA)] for _ in range(args.steps)]
     for i in range(args.steps):
-        res, out = step(evs[i])
+        res, out = step(evs[i], pevs[i])
     torch.cuda.synchronize()
 
     def avg(a, b):
         return float(np.mean([e[a].elapsed_ms(e[b]) for e in evs]))
 
     gram = awq.awq_loss_form(M, K, N, nA) == awq.AWQ_LOSS_GRAM
-    gemm_ms, fq_ms = avg("g0", "g1"), avg("f0", "f1")
+    per_step = [pass_event_times(pe) for pe in pevs]
+    passes = per_step[0][2]
+    assert passes >= 1 and all(t[2] == passes for t in per_step), "per-pass events"
+    fq_ms = float(np.mean([t[0] for t in per_step]))          # all passes of a step
+    gemm_total_ms = float(np.mean([t[1] for t in per_step]))
+    gemm_ms = gemm_total_ms / passes                           # average loss-product launch
     stats_ms, pack_ms = avg("st0", "st1"), avg("p0", "p1")
     stats_pass_ms = avg("sk0", "sk1")
     gram_ms = avg("r0", "r1") if gram else 0.0
@@ -264,11 +296,12 @@ def main():
     direct_flops = 2.0 * M * N * K * nA                     # the direct product dW_k X^T
     gemm_flops = loss_product_flops(M, K, N, nA, gram)
     gram_flops = gram_build_flops(N, K) if gram else 0.0
-    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    gemm_tflops = gemm_flops / (gemm_total_ms * 1e-3) / 1e12
     g = spec.group_size
     # algorithmic bytes read and written by the streaming kernels
     stats_rw = (2.0 * N * K, 4.0 * K)
-    fq_rw = (2.0 * M * K + 4.0 * K * nA, 2.0 * M * K * nA)
+    # (W is read once by each pass's fake quantisation)
+    fq_rw = (2.0 * M * K * passes + 4.0 * K * nA, 2.0 * M * K * nA)
     pack_rw = (2.0 * M * K + 4.0 * K, M * K / 2 + 4.0 * M * K / g)
     ceilings = measure_ceilings(awq, torch, sptr)
 
@@ -280,11 +313,12 @@ def main():
         kv = {}
         with open(args.traffic_summary) as f:
             for ln in f:
-                m = re.match(r"^(kernel_source_sha|workload|hbm_bytes_per_launch|mfma_busy_frac|"
-                             r"shader_clock_ghz): (\S+)\s*$", ln)
+                m = re.match(r"^(kernel_source_sha|workload|launches_per_step|hbm_bytes_per_launch|"
+                             r"mfma_busy_frac|shader_clock_ghz): (\S+)\s*$", ln)
                 if m:
                     kv[m.group(1)] = m.group(2)
-        if kv.get("workload") == spec.name and kv.get("kernel_source_sha") == _kernel_sha():
+        if (kv.get("workload") == spec.name and kv.get("kernel_source_sha") == _kernel_sha()
+                and kv.get("launches_per_step") == str(passes)):
             traffic = float(kv["hbm_bytes_per_launch"])
             if "mfma_busy_frac" in kv:
                 counters = {"mfma_busy_frac": float(kv["mfma_busy_frac"]),
@@ -309,12 +343,14 @@ def main():
                                 f"group {g}, {nA} alphas"),
                    "out_features": M, "in_features": K, "n_tokens": N, "w_bit": spec.w_bit,
                    "group_size": g, "zero_point": spec.zero_point, "n_alpha": nA,
+                   "search_passes": passes,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": gemm_tflops / MFMA_F16_PEAK_TFLOPS,
                      "traffic": traffic,
                      "kernel": "k_loss_gemm" + ("<G form>" if gram else ""),
-                     "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms,
+                     "flops_per_launch": gemm_flops / passes, "avg_launch_ms": gemm_ms,
+                     "launches_per_step": passes,
                      "mfma_counters": counters,
                      # the same rate against this device's matrix-core-only probe (same run)
                      "measured_ceiling": {
@@ -330,8 +366,9 @@ def main():
             "act_stats": hbm_entry(*stats_rw, stats_pass_ms, ceilings, call_ms=stats_ms,
                                    timed="streaming pass (first of the two launches), library "
                                          "events"),
-            "fake_quant": hbm_entry(*fq_rw, fq_ms, ceilings, timed="one launch, library events"),
-            "loss_gemm": {"ms": gemm_ms, "TFLOP/s": gemm_tflops,
+            "fake_quant": hbm_entry(*fq_rw, fq_ms, ceilings, launches=passes,
+                                    timed="all launches of a step, library events"),
+            "loss_gemm": {"ms": gemm_total_ms, "launches": passes, "TFLOP/s": gemm_tflops,
                           "frac_mfma": gemm_tflops / MFMA_F16_PEAK_TFLOPS,
                           "form": "gram" if gram else "direct"},
             **({"gram": {"ms": gram_ms, "build_flops": gram_flops,
@@ -721,24 +758,29 @@ def time_large_layers(awq, torch, alphas, sptr, ceil, reps=2):
         runs = []
         for _ in range(reps):
             ev = [HipEvent() for _ in range(8)]
+            pev = [HipEvent() for _ in range(4 * nA)]
             ev[0].record(sptr)
-            awq.awq_set_profile_events(ev[2], ev[3], ev[4], ev[5], ev[6], ev[7])
+            awq.awq_set_profile_events(None, None, None, None, ev[6], ev[7])
+            awq.awq_set_profile_pass_events(pev)
             awq.awq_search_scales(W, X, a, alphas, cfg, workspace=ws)
             ev[1].record(sptr)
-            runs.append(ev)
+            runs.append((ev, pev))
         torch.cuda.synchronize()
-        search_ms = float(sum(e[0].elapsed_ms(e[1]) for e in runs) / reps)
-        gemm_ms = float(sum(e[2].elapsed_ms(e[3]) for e in runs) / reps)
-        fq_ms = float(sum(e[4].elapsed_ms(e[5]) for e in runs) / reps)
+        search_ms = float(sum(e[0].elapsed_ms(e[1]) for e, _ in runs) / reps)
+        pt = [pass_event_times(pe) for _, pe in runs]
+        gemm_ms = float(sum(t[1] for t in pt) / len(pt))
+        fq_ms = float(sum(t[0] for t in pt) / len(pt))
+        passes = pt[0][2]
         gflops = loss_product_flops(M, K, N, nA, gram)
         entry = {"M": M, "K": K, "N": N, "w_bit": b, "group_size": g, "search_ms": search_ms,
                  "form": "gram" if gram else "direct",
+                 "passes": passes,
                  "loss_product": {"ms": gemm_ms, "flops": gflops, **tf(gflops, gemm_ms)},
                  "fake_quant": {"ms": fq_ms,
-                                "GB/s": (2.0 * M * K * (nA + 1)) / (fq_ms * 1e-3) / 1e9}}
+                                "GB/s": (2.0 * M * K * (nA + passes)) / (fq_ms * 1e-3) / 1e9}}
         bflops = 0.0
         if gram:
-            gram_ms = float(sum(e[6].elapsed_ms(e[7]) for e in runs) / reps)
+            gram_ms = float(sum(e[6].elapsed_ms(e[7]) for e, _ in runs) / reps)
             bflops = gram_build_flops(N, K)
             entry["gram_pass"] = {"ms": gram_ms, "build_flops": bflops, **tf(bflops, gram_ms)}
         entry["direct_over_executed_flops"] = 2.0 * M * K * N * nA / (gflops + bflops)

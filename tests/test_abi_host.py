@@ -39,7 +39,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
-    assert len(names) == 28, names
+    assert len(names) == 29, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in awq_act.h but not exported"
     assert set(names) == set(_lib._SIGNATURES)
@@ -99,12 +99,13 @@ def test_workspace_query(L):
     M = K = 4096
     N = 2048                                     # the direct form
     assert awq.awq_loss_form(M, K, N, 20) == awq.AWQ_LOSS_DIRECT
-    full = awq.awq_workspace_bytes(M, K, N, cfg, 20, 0)
+    full = awq.awq_workspace_bytes(M, K, N, cfg, 20, 20)
     one = awq.awq_workspace_bytes(M, K, N, cfg, 20, 1)
     tiles = (M // 256) * (N // 256)
     fixed = 20 * K * 4 + 20 * tiles * 8          # both already multiples of 256
     assert one == fixed + M * K * 2
     assert full == fixed + 20 * M * K * 2
+    assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 99) == full
     assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 7) == fixed + 7 * M * K * 2
     # the G form: tiles over K, then X^T (fp16 [K][N]), the fp32 split partials of the 136
     # tiles of G's upper block triangle, fp16 G', fp32 diagonal, the partials' tile maxima,
@@ -118,7 +119,7 @@ def test_workspace_query(L):
     fixed = (20 * K * 4 + 20 * tiles * 8 + K * N * 2 + splits * 136 * 256 * 256 * 4 + K * K * 2
              + K * 4 + 1280 + 256)
     assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 1) == fixed + M * K * 2
-    assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 0) == fixed + 20 * M * K * 2
+    assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 20) == fixed + 20 * M * K * 2
     # more tokens than one split (8192) holds: at least three splits; the plan takes four
     # (three of 5760 tokens and one of 2720: the busiest compute unit then runs 11520
     # tokens' worth of tiles, against 13440 with three equal splits)
@@ -192,13 +193,58 @@ def test_loss_form_choice():
     # the choice agrees with the workspace: the G form holds X^T, G' (fp16) and at least one
     # fp32 partial of G's upper block triangle (136 tiles of 256 x 256) besides dW
     cfg = awq.qconfig(4, 128, 1)
-    direct = awq.awq_workspace_bytes(4096, 4096, 1024, cfg, 20, 0)
-    gram = awq.awq_workspace_bytes(4096, 4096, 4096, cfg, 20, 0)
+    direct = awq.awq_workspace_bytes(4096, 4096, 1024, cfg, 20, 20)
+    gram = awq.awq_workspace_bytes(4096, 4096, 4096, cfg, 20, 20)
     assert gram - direct >= 4096 * 4096 * 2 * 2 + 136 * 256 * 256 * 4
 
 
 def test_profile_hook_set_and_clear(L):
     assert L.awq_set_profile_events(None, None, None, None, None, None) == E["OK"]
+    ev = (ctypes.c_void_p * 8)()
+    assert L.awq_set_profile_pass_events(ev, 2) == E["OK"]
+    assert L.awq_set_profile_pass_events(None, 0) == E["OK"]   # clears it
+    assert L.awq_set_profile_pass_events(None, 1) == E["NULL"]
+    assert L.awq_set_profile_pass_events(ev, -1) == E["SHAPE"]
+    big = (ctypes.c_void_p * (4 * 65))()
+    assert L.awq_set_profile_pass_events(big, 65) == E["SHAPE"]
+    with pytest.raises(ValueError):
+        awq.awq_set_profile_pass_events([None] * 5)
+    awq.awq_set_profile_pass_events([])
+
+
+# The grid points a pass when the library chooses (alpha_batch <= 0), on the shapes the
+# policy was measured on (20 grid points, 4-bit, g = 128, zero point): (M, K, N) -> points
+# a pass.  Batched where all of these hold: dW of 20 points above 192 MiB, at least 4
+# points within it, in_features >= 2048 (G form) or n_tokens >= 2048 (direct form), and
+# the pass's loss blocks filling at least 9/10 of their last round on 256 compute units.
+DEFAULT_BATCH = {
+    (4096, 4096, 4096): 6,      # G form, 128 blocks a point: 768 = 3 rounds
+    (4096, 4096, 2048): 6,      # direct form, 128 blocks a point
+    (3072, 3072, 3072): 10,     # 72 blocks a point: 720 of 768
+    (4096, 3072, 3072): 8,      # 96 a point: 768
+    (2048, 8192, 8192): 6,
+    (8192, 2048, 2048): 6,
+    (4608, 4096, 4096): 5,      # 144 a point: 720 of 768 (4 points: 576 of 768, not taken)
+    (6144, 2048, 2048): 8,
+    (4096, 5120, 5120): 20,     # 4 points: 640 of 768 blocks
+    (5120, 5120, 5120): 20,     # only 3 points fit
+    (11008, 4096, 16384): 20,   # only 2 fit
+    (11008, 1024, 1024): 20,    # in_features below 2048
+    (4096, 4096, 1024): 20,     # direct form with fewer than 2048 tokens
+    (4096, 4096, 1536): 20,
+    (2048, 2048, 2048): 20,     # all 20 points fit in 192 MiB
+    (28672, 8192, 65536): 20,
+}
+
+
+@pytest.mark.parametrize("shape", sorted(DEFAULT_BATCH))
+def test_default_batch(shape):
+    M, K, N = shape
+    cfg = awq.qconfig(4, 128, 1)
+    b = DEFAULT_BATCH[shape]
+    assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 0) == awq.awq_workspace_bytes(M, K, N, cfg, 20, b)
+    if b < 20:
+        assert awq.awq_workspace_bytes(M, K, N, cfg, 20, 0) < awq.awq_workspace_bytes(M, K, N, cfg, 20, b + 1)
 
 
 def test_stats_ex_validation(L):

@@ -55,6 +55,7 @@ _SIGNATURES = {
     "awq_fake_quant_delta": (ctypes.c_int, [_vp, _vp, _i64, _i64, _cfgp, _vp, _vp]),
     "awq_quantize_pack": (ctypes.c_int, [_vp, _vp, _i64, _i64, _cfgp, _vp, _vp, _vp, _vp]),
     "awq_set_profile_events": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
+    "awq_set_profile_pass_events": (ctypes.c_int, [ctypes.POINTER(_vp), _i32]),
     "awq_set_stats_profile_events": (ctypes.c_int, [_vp, _vp]),
     "awq_act_stats_ex_workspace_bytes": (_sz, [_i64, _i64, _i32, _i64]),
     "awq_act_stats_ex": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i64, ctypes.c_double, _vp, _vp,
@@ -330,6 +331,19 @@ def awq_set_profile_events(gemm_start=None, gemm_stop=None, fq_start=None, fq_st
     _check(lib().awq_set_profile_events(h(gemm_start), h(gemm_stop), h(fq_start), h(fq_stop),
                                         h(gram_start), h(gram_stop)),
            "awq_set_profile_events")
+
+
+def awq_set_profile_pass_events(events) -> None:
+    """Arm the one-shot per-thread per-pass hook of the next search: `events` is a list of
+    4 n_pass hipEvent_t handles (int, None, or objects with `.handle`), for pass p [4p],
+    [4p + 1] around its fake quantisation and [4p + 2], [4p + 3] around its loss product.
+    An empty list clears the hook."""
+    hs = [None if e is None else (int(e) if isinstance(e, int) else int(e.handle))
+          for e in events]
+    if len(hs) % 4:
+        raise ValueError("awq_set_profile_pass_events: 4 events per pass")
+    arr = (_vp * max(1, len(hs)))(*hs)
+    _check(lib().awq_set_profile_pass_events(arr, len(hs) // 4), "awq_set_profile_pass_events")
 
 
 def awq_set_stats_profile_events(pass_start=None, pass_stop=None):

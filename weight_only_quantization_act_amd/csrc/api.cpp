@@ -97,6 +97,39 @@ SearchLayout search_layout(int64_t M, int64_t K, int64_t N, int32_t n_alpha) {
   return L;
 }
 
+// Grid points per pass when the caller leaves the choice to the library (alpha_batch <= 0
+// in awq_workspace_bytes).  A pass's dW is written by the fake quantisation and read back
+// by the loss product; when it fits in three quarters of the device's 256 MB last-level
+// cache, the loss product reads it from there (4-6% faster on the 4096^2 layer), but every
+// extra pass re-reads W in its fake quantisation (about 14 us on that layer).  Batching
+// pays only when the loss product has enough work per byte of dW (in_features >= 2048 in
+// the G form, n_tokens >= 2048 in the direct form), when at least 4 points fit, and when a
+// pass's loss blocks fill at least 9/10 of their last generation on the compute units;
+// otherwise the whole grid goes in one pass, as it does when all of dW fits the budget.
+constexpr size_t kBatchDwBudget = (size_t)192 << 20;
+constexpr int kMinBatch = 4;
+constexpr int64_t kMinBatchWork = 2048;
+constexpr int64_t kComputeUnits = 256;  // MI355X
+
+int default_batch(int64_t M, int64_t K, int64_t N, int32_t n_alpha) {
+  if (M <= 0 || K <= 0) return n_alpha;
+  const size_t dw = (size_t)M * (size_t)K * 2;
+  if ((size_t)n_alpha * dw <= kBatchDwBudget) return n_alpha;
+  const int64_t fit = (int64_t)(kBatchDwBudget / dw);
+  if (fit < kMinBatch) return n_alpha;
+  const bool gram = awq::loss_use_gram(M, K, N, n_alpha);
+  if ((gram ? K : N) < kMinBatchWork) return n_alpha;
+  // loss-product blocks per grid point (the launchers' grids)
+  const int64_t per_point = gram ? (awq::loss_tiles_m(K) + 1) / 2 * awq::loss_tiles_n(M)
+                                 : awq::loss_tiles_m(M) * awq::loss_tiles_n(N);
+  for (int64_t b = fit < n_alpha - 1 ? fit : n_alpha - 1; b >= kMinBatch; --b) {
+    const int64_t blocks = b * per_point;
+    const int64_t gens = (blocks + kComputeUnits - 1) / kComputeUnits;
+    if (blocks * 10 >= gens * kComputeUnits * 9) return (int)b;
+  }
+  return n_alpha;
+}
+
 struct ProfileHook {
   void* gemm_start = nullptr;
   void* gemm_stop = nullptr;
@@ -106,6 +139,11 @@ struct ProfileHook {
   void* gram_stop = nullptr;
 };
 thread_local ProfileHook g_hook;
+// one-shot events around each pass of the next search (awq_set_profile_pass_events): for
+// pass p, [4p] and [4p + 1] around its fake quantisation, [4p + 2] and [4p + 3] around its
+// loss product
+thread_local void* g_pass_ev[4 * AWQ_MAX_ALPHA];
+thread_local int g_pass_n = 0;
 // one-shot events around the statistics' streaming pass (awq_set_stats_profile_events)
 thread_local void* g_stats_ev[2] = {nullptr, nullptr};
 
@@ -132,6 +170,8 @@ int run_search(const void* W, const void* X, const float* s_table, int64_t M, in
                void* stream) {
   ProfileHook hook = g_hook;
   g_hook = ProfileHook();
+  const int n_pass_ev = g_pass_n;
+  g_pass_n = 0;
   hipStream_t sm = (hipStream_t)stream;
   SearchLayout L = search_layout(M, K, N, nc);
   char* ws = (char*)workspace;
@@ -156,16 +196,20 @@ int run_search(const void* W, const void* X, const float* s_table, int64_t M, in
       if (st) return st;
       if ((st = record(hook.gram_stop, sm))) return st;
     }
-    for (int k0 = 0; k0 < nc; k0 += batch) {
+    for (int k0 = 0, pass = 0; k0 < nc; k0 += batch, ++pass) {
       const int nb = nc - k0 < batch ? nc - k0 : batch;
       const bool first = (k0 == 0);
+      void* const* pev = pass < n_pass_ev ? g_pass_ev + 4 * pass : nullptr;
       if (first && (st = record(hook.fq_start, sm))) return st;
+      if (pev && (st = record(pev[0], sm))) return st;
       st = hip_status(awq::launch_fake_quant_delta((const uint16_t*)W, s_table + (size_t)k0 * K,
                                                    (int)M, (int)K, nb, cfg->w_bit,
                                                    cfg->group_size, cfg->zero_point, dW, sm));
       if (st) return st;
+      if (pev && (st = record(pev[1], sm))) return st;
       if (first && (st = record(hook.fq_stop, sm))) return st;
       if (first && (st = record(hook.gemm_start, sm))) return st;
+      if (pev && (st = record(pev[2], sm))) return st;
       if (L.gram)
         st = hip_status(awq::launch_loss_gemm_gram(dW, Gh, gdiag, gexp, (int)M, (int)K, nb,
                                                    partials + (size_t)k0 * L.tiles, sm));
@@ -173,6 +217,7 @@ int run_search(const void* W, const void* X, const float* s_table, int64_t M, in
         st = hip_status(awq::launch_loss_gemm(dW, (const uint16_t*)X, (int)M, (int)N, (int)K,
                                               nb, partials + (size_t)k0 * L.tiles, sm));
       if (st) return st;
+      if (pev && (st = record(pev[3], sm))) return st;
     }
     if ((st = record(hook.gemm_stop, sm))) return st;
   }
@@ -257,7 +302,8 @@ size_t awq_workspace_bytes(int64_t out_features, int64_t in_features, int64_t n_
   if (token_shape(n_tokens, in_features) != AWQ_OK) return 0;
   if (in_features > kMaxSearchK) return 0;
   if (n_alpha < 1 || n_alpha > AWQ_MAX_ALPHA) return 0;
-  if (alpha_batch <= 0 || alpha_batch > n_alpha) alpha_batch = n_alpha;
+  if (alpha_batch <= 0) alpha_batch = default_batch(out_features, in_features, n_tokens, n_alpha);
+  if (alpha_batch > n_alpha) alpha_batch = n_alpha;
   SearchLayout L = search_layout(out_features, in_features, n_tokens, n_alpha);
   return L.dw_off + (size_t)alpha_batch * L.dw_bytes_per_alpha;
 }
@@ -637,6 +683,14 @@ int awq_probe_wall_clock_khz(int32_t device, int32_t* khz_out) {
 int awq_set_stats_profile_events(void* pass_start, void* pass_stop) {
   g_stats_ev[0] = pass_start;
   g_stats_ev[1] = pass_stop;
+  return AWQ_OK;
+}
+
+int awq_set_profile_pass_events(void* const* events, int32_t n_pass) {
+  if (n_pass < 0 || n_pass > AWQ_MAX_ALPHA) return AWQ_E_SHAPE;
+  if (n_pass > 0 && !events) return AWQ_E_NULL;
+  for (int i = 0; i < 4 * n_pass; ++i) g_pass_ev[i] = events[i];
+  g_pass_n = n_pass;
   return AWQ_OK;
 }
 
