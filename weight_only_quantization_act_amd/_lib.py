@@ -228,7 +228,9 @@ def awq_search_scales(W: torch.Tensor, X: torch.Tensor, a: torch.Tensor,
                       workspace: Optional[torch.Tensor] = None, alpha_batch: int = 0,
                       stream=None):
     """Grid search over alpha.  Returns device tensors (s [K] fp32, losses [n_alpha] fp64,
-    best [1] int32, status [1] int32); nothing is synchronised."""
+    best [1] int32, status [1] int32); nothing is synchronised.  Without a workspace one
+    is allocated for `alpha_batch` grid points a pass (0: the library's choice, sized for
+    the last-level cache); with one, its size sets the points a pass."""
     _dev(W, torch.float16, "W")
     _dev(X, torch.float16, "X")
     M, K = W.shape
