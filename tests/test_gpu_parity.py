@@ -303,6 +303,27 @@ SEARCH_CASES = [
 ]
 
 
+@pytest.mark.parametrize("M,K,N,g", [
+    (2, 1 << 22, 3, 128),   # the largest in_features the search takes: a 256-row operand panel
+                            # spans 2^31 bytes of 32-bit buffer offsets
+    (64, 40960, 64, 64),    # beyond the G form's 32768 channels: the direct form
+])
+def test_search_largest_in_features(M, K, N, g):
+    L = make_layer(small_spec("k", M, K, N, w_bit=4, group_size=g, zero_point=1, seed=3,
+                              outlier_count=max(1, K // 1000), n_alpha=5))
+    cfg = awq.qconfig(4, g, 1)
+    alphas = alpha_grid(5)
+    assert awq.awq_loss_form(M, K, N, 5) == awq.AWQ_LOSS_DIRECT
+    where = f"search M={M} K={K} N={N} g={g} (direct form, 5 alphas)"
+    say(where)
+    res = awq.quantize_layer(dev(L.W), dev(L.X), alphas, cfg)
+    torch.cuda.synchronize()
+    orc = O.run_layer(L.W, L.X, alphas, ocfg(cfg))
+    assert np.array_equal(host(res["a"]), orc["a"]), where
+    check_search(res, orc, where)
+    check_pack(res["codes"], res["scales"], res["zeros"], L.W, host(res["s"]), cfg, where)
+
+
 def test_search_forms_covered():
     """The cases above exercise both forms of the loss."""
     forms = {awq.awq_loss_form(M, K, N, 20) for M, K, N, *_ in SEARCH_CASES}
