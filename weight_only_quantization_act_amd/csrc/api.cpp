@@ -100,8 +100,8 @@ SearchLayout search_layout(int64_t M, int64_t K, int64_t N, int32_t n_alpha) {
 // Grid points per pass when the caller leaves the choice to the library (alpha_batch <= 0
 // in awq_workspace_bytes).  A pass's dW is written by the fake quantisation and read back
 // by the loss product; when it fits in three quarters of the device's 256 MB last-level
-// cache, the loss product reads it from there (4-6% faster on the 4096^2 layer), but every
-// extra pass re-reads W in its fake quantisation (about 14 us on that layer).  Batching
+// cache, the loss product reads it from there (2-6% faster on the 4096^2 layer), but every
+// extra pass re-reads W in its fake quantisation (10-14 us a pass on that layer).  Batching
 // pays only when the loss product has enough work per byte of dW (in_features >= 2048 in
 // the G form, n_tokens >= 2048 in the direct form), when at least 4 points fit, and when a
 // pass's loss blocks fill at least 9/10 of their last generation on the compute units;
