@@ -8,8 +8,9 @@ The default workload is the 4096 x 4096 layer with 4096 calibration tokens (4-bi
 zero-point, group 128, 20 alphas).
 
 Prints one JSON line.  The loss product's live duration comes from HIP events that the
-library records on its own stream around that launch (one launch per step, the whole
-alpha grid in one pass).  On this layer the library takes the loss through G = X^T X
+library records on its own stream around each of a step's loss-product launches (the grid
+runs in the library's default passes, 6, 6, 6 and 2 points on this layer, so that each pass's
+dW stays in the last-level cache).  On this layer the library takes the loss through G = X^T X
 (formed once per step, also bracketed by events): the loss product is then dW_k G'^T
 over the block upper triangle of G, and its flops are counted as executed.  The CPU baseline is the oracle, timed on a bounded row subset
 of the same layer (the loss is a sum over rows) and scaled to the full layer.
@@ -413,7 +414,7 @@ def main():
 
 
 def loss_product_flops(M, K, N, n_alpha, gram):
-    """Matrix-core flops of one loss-product launch over the whole grid, as executed.  G form:
+    """Matrix-core flops of the loss product over the whole grid (all passes), as executed.  G form:
     each half (128 channels) of a 256-channel tile row runs over k from its own first channel
     on, for 256-row tiles of dW (M a multiple of 256 here).  Direct form: 2 M K N per alpha."""
     if not gram:

@@ -1,5 +1,6 @@
 """The four large workloads at full size, in the launch configuration the benchmark uses
-(whole alpha grid in one pass), against the CPU oracle.
+(the library's default, which runs these layers' whole alpha grid in one pass), against the
+CPU oracle.
 
 The oracle cannot evaluate these layers whole in a test (up to 6e14 flop in fp64), so:
   - statistics are compared bit for bit on the full activations;

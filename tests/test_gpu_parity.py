@@ -365,7 +365,8 @@ def test_search_c1_full():
 
 def test_search_headline_layer_full():
     """The 4096 x 4096 layer with 4096 tokens, all 20 alphas, in the launch configuration
-    the benchmark uses (whole grid in one pass), against the full oracle."""
+    the benchmark uses (the library's default passes of 6, 6, 6 and 2 points), against the
+    full oracle."""
     L = make_layer(CONFIGS["c2"][0])
     spec = L.spec
     cfg = awq.qconfig(spec.w_bit, spec.group_size, spec.zero_point)
